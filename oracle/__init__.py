@@ -1,0 +1,48 @@
+"""CPU oracle for the 4-bit routed mixture-of-experts expert layer.
+
+TEST INFRASTRUCTURE ONLY. This package is the plain, slow, obviously correct
+definition of what the layer computes, written with numpy on the host. Only the
+test suite, the smoke check in ``__graft_entry__`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import or run it. The library in ``bit_mixture_experts_amd``
+never imports it, and the two share no code, tables or constants.
+
+Sources (web pages, cited by title and section):
+
+* [MXFP4 page] "How do I train and serve MoE models released in MXFP4
+  (gpt-oss, DeepSeek-V4)?" -- sections "Two fidelity paths", "Why it happens",
+  "Which project solves it", "Supported scope", "Limitations".
+* [Solutions index] "MoE Training & Inference Guides -- Cerin Amroth", the
+  "Solutions -- one page per problem" tables (grouped-nf4-gemm and
+  experts4bit-qlora entries).
+* [experts4bit-qlora page] project page "experts4bit-qlora" -- sections
+  "What it does", "Use this when", "Limitations -- qlora-fused-moe-experts",
+  "Current measured position".
+* [Offload page] "How do I offload MoE experts to host RAM, or serve and train
+  them from an NVMe arena?" -- section "Why it happens".
+
+Precision: the oracle computes in float64 except where the method itself fixes a
+precision (fp32 absmax and the fp32 division that decides an NF4 code; fp32
+router logits; the bf16 value of a row-scaled permutation, which the interface
+defines as an fp32 product rounded to bf16).
+
+Pin status: every public function has a pin in ``tests/test_oracle_*.py`` that
+does not re-use the oracle's own formula (closed forms, exhaustive enumeration,
+brute force on tiny inputs, float64 finite differences, torch CPU autograd, the
+published NF4 construction). No function is "parity unpinned".
+"""
+
+from .numerics import bf16_bits_from_f32, bf16_bits_to_f64, bf16_bits_to_f32
+from .formats import (NF4_LEVELS, nf4_midpoints, quantize_nf4, dequantize_nf4,
+                      E2M1_MAGNITUDES, mxfp4_values, decode_mxfp4_bf16)
+from .routing import route, permute, gather_rows
+from .layer import (ExpertWeights, gate_up, activation, down, combine,
+                    layer_forward, layer_backward, token_forward)
+
+__all__ = [
+    "bf16_bits_from_f32", "bf16_bits_to_f64", "bf16_bits_to_f32",
+    "NF4_LEVELS", "nf4_midpoints", "quantize_nf4", "dequantize_nf4",
+    "E2M1_MAGNITUDES", "mxfp4_values", "decode_mxfp4_bf16",
+    "route", "permute", "gather_rows",
+    "ExpertWeights", "gate_up", "activation", "down", "combine",
+    "layer_forward", "layer_backward", "token_forward",
+]
