@@ -1,0 +1,483 @@
+#!/usr/bin/env python3
+"""Throughput of the routed 4-bit MoE expert layer on one MI355X.
+
+A step is one pass of the layer's hot path over one batch: route -> permute
+(+ gather) -> grouped expert forward (gate_up + activation, down) -> combine.
+The headline workload is the Qwen3-30B-A3B-shaped NF4 layer (E=128, top-8,
+H=2048, I=768) at T=4096 tokens; `value` is routed tokens/s. Weights, tokens
+and router logits are seeded synthetic tensors already resident in HBM.
+
+The dominant kernel (the gate_up grouped GEMM at this size) is timed live with
+HIP events that the library records around its launch on the step's stream,
+and priced against the bf16 MFMA peak. The sweep adds the decode token counts
+(weight GB/s against HBM peak) and the other workloads. The CPU oracle is timed
+on a bounded sample of the same workload on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+HEADLINE_T = 4096
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ HIP events
+
+class Hip:
+    """hipEvent plumbing through the HIP runtime (the library records the
+    events; bench.py only creates and reads them)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            rc = self.lib.hipEventCreate(ctypes.byref(arr, i * ctypes.sizeof(ctypes.c_void_p)))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return arr
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return out.value
+
+    def record(self, ev, stream):
+        rc = self.lib.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+
+# -------------------------------------------------------------- layer set-up
+
+def nf4_layer(moe4, inputs, spec, layer, seed, torch):
+    """NF4 stack quantised on the GPU from seeded fp32 source weights."""
+    E, H, I = spec.E, spec.H, spec.I
+    wg, wd = inputs.device_nf4_source(spec, layer, seed)
+    dev = wg.device
+    gq = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+    gs = torch.empty((E, 2 * I, H // 64), dtype=torch.float32, device=dev)
+    dq = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
+    ds = torch.empty((E, H, I // 64), dtype=torch.float32, device=dev)
+    moe4.moe4_quantize_nf4(wg, gq, gs)
+    moe4.moe4_quantize_nf4(wd, dq, ds)
+    del wg, wd
+    lora = {}
+    if spec.lora_r:
+        lora = dict(lora_A=inputs.device_bf16((E, spec.lora_r, H), 1.0 / H ** 0.5, seed, spec,
+                                              layer, 11),
+                    lora_B=inputs.device_bf16((E, 2 * I, spec.lora_r), 0.01, seed, spec, layer, 12),
+                    lora_scale=spec.lora_scale)
+    return moe4.Experts(moe4.MOE4_FMT_NF4, gq, gs, dq, ds, gu_layout=moe4.MOE4_GU_HALVES,
+                        act=moe4.MOE4_ACT_SWIGLU, E=E, H=H, I=I, **lora)
+
+
+def mxfp4_layer(moe4, inputs, spec, layer, seed, torch):
+    E, H, I = spec.E, spec.H, spec.I
+    gb, gsc, db, dsc = inputs.device_mxfp4_stack(spec, layer, seed)
+    bias = {}
+    if spec.bias:
+        bias = dict(gu_bias=inputs.device_bf16((E, 2 * I), spec.bias_std, seed, spec, layer, 9),
+                    dn_bias=inputs.device_bf16((E, H), spec.bias_std, seed, spec, layer, 10))
+    return moe4.Experts(moe4.MOE4_FMT_MXFP4, gb, gsc, db, dsc,
+                        gu_layout=(moe4.MOE4_GU_INTERLEAVED if spec.layout == "interleaved"
+                                   else moe4.MOE4_GU_HALVES),
+                        act=(moe4.MOE4_ACT_SWIGLU_CLAMPED if spec.act == "swiglu_clamped"
+                             else moe4.MOE4_ACT_SWIGLU),
+                        E=E, H=H, I=I, act_alpha=spec.alpha, act_limit=spec.limit, **bias)
+
+
+def expert_bytes(spec):
+    """Algorithmic weight bytes of one expert: (gate_up, down), packed nibbles
+    plus scales plus bias rows."""
+    H, I = spec.H, spec.I
+    if spec.fmt == "nf4":
+        gu = 2 * I * H // 2 + 2 * I * (H // 64) * 4
+        dn = H * I // 2 + H * (I // 64) * 4
+    else:
+        gu = 2 * I * H // 2 + 2 * I * (H // 32)
+        dn = H * I // 2 + H * (I // 32)
+    if spec.bias:
+        gu += 2 * I * 2
+        dn += H * 2
+    return gu, dn
+
+
+class Step:
+    """Buffers for one (workload, T) and the four calls of one step."""
+
+    def __init__(self, moe4, torch, spec, T, ex, backward=False):
+        self.moe4, self.torch, self.spec, self.T = moe4, torch, spec, T
+        dev = "cuda"
+        k, H, E = spec.k, spec.H, spec.E
+        S = T * k
+        i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+        self.idx = torch.empty((T, k), dtype=i32, device=dev)
+        self.w = torch.empty((T, k), dtype=f32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
+        self.sor = torch.empty(S, dtype=i32, device=dev)
+        self.ros = torch.empty(S, dtype=i32, device=dev)
+        self.x_perm = torch.empty((S, H), dtype=bf, device=dev)
+        self.y_perm = torch.empty((S, H), dtype=f32, device=dev)
+        self.out = torch.empty((T, H), dtype=bf, device=dev)
+        self.ws = torch.empty(moe4.moe4_workspace_size(ex, T, k), dtype=torch.uint8, device=dev)
+        self.backward = backward
+        if backward:
+            r = ex.lora_r
+            self.save_gu = torch.empty((S, 2 * spec.I), dtype=f32, device=dev)
+            self.save_xa = torch.empty((S, r), dtype=f32, device=dev) if r else None
+            self.dy = torch.empty((S, H), dtype=bf, device=dev)
+            self.dx_perm = torch.empty((S, H), dtype=f32, device=dev)
+            self.dx = torch.empty((T, H), dtype=bf, device=dev)
+            self.dA = torch.empty((E, r, H), dtype=f32, device=dev) if r else None
+            self.dB = torch.empty((E, 2 * spec.I, r), dtype=f32, device=dev) if r else None
+            self.scratch_i = torch.empty(S, dtype=i32, device=dev)
+            self.scratch_o = torch.empty(E + 1, dtype=i32, device=dev)
+
+    def forward(self, ex, x, logits):
+        m = self.moe4
+        m.moe4_route(logits, self.spec.k, self.idx, self.w)
+        m.moe4_permute(self.idx, self.spec.E, self.offsets, self.sor, self.ros, x=x,
+                       x_perm=self.x_perm, ws=self.ws)
+        if self.backward:
+            m.moe4_expert_forward(ex, self.x_perm, self.offsets, self.y_perm, save_gu=self.save_gu,
+                                  save_xa=self.save_xa, ws=self.ws)
+        else:
+            m.moe4_expert_forward(ex, self.x_perm, self.offsets, self.y_perm, ws=self.ws)
+        m.moe4_combine(self.y_perm, self.ros, self.w, self.out, self.spec.k)
+
+    def backward_pass(self, ex, dout):
+        m = self.moe4
+        m.moe4_permute(self.idx, self.spec.E, self.scratch_o, self.scratch_i, self.scratch_i,
+                       x=dout, row_scale=self.w.reshape(-1), x_perm=self.dy, ws=self.ws)
+        m.moe4_expert_backward(ex, self.x_perm, self.offsets, self.save_gu, self.save_xa, self.dy,
+                               self.dx_perm, self.dA, self.dB, ws=self.ws)
+        m.moe4_combine(self.dx_perm, self.ros, None, self.dx, self.spec.k)
+
+
+def touched(torch, moe4, step, ex, x, logits):
+    """Distinct experts per step for the given logits (routing is deterministic)."""
+    moe4.moe4_route(logits, step.spec.k, step.idx, step.w)
+    torch.cuda.synchronize()
+    return int(torch.unique(step.idx).numel())
+
+
+# --------------------------------------------------------------------- timing
+
+def time_steps(torch, hip, moe4, steps, warmup, run, nkern=2):
+    """Run `run(i)` warmup + steps times; time the steps with events around the
+    whole timed region and, through the library hook, around each of the
+    (up to two) GEMM launches of every step. Returns (ms_per_step, [avg kernel
+    ms for each GEMM])."""
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    kev = hip.events(4 * steps)
+    region = hip.events(2)
+    per_step = [(ctypes.c_void_p * 4)(*kev[4 * i:4 * i + 4]) for i in range(steps)]
+    hip.record(region[0], stream)
+    for i in range(steps):
+        moe4.moe4_set_timing_events(per_step[i])
+        run(warmup + i)
+    moe4.moe4_set_timing_events(None)
+    hip.record(region[1], stream)
+    torch.cuda.synchronize()
+    total = hip.ms(region[0], region[1])
+    kms = []
+    for j in range(nkern):
+        kms.append(sum(hip.ms(kev[4 * i + 2 * j], kev[4 * i + 2 * j + 1]) for i in range(steps))
+                   / steps)
+    return total / steps, kms
+
+
+# ----------------------------------------------------------------- workloads
+
+def bench_layer(torch, hip, moe4, inputs, spec, T, exs, steps, warmup, seed, nlogits=16):
+    """Forward steps of one workload at T tokens, rotating layer replicas and
+    routing draws so that decode-sized steps read cold weights."""
+    step = Step(moe4, torch, spec, T, exs[0])
+    toks = [inputs.device_tokens(spec, T, layer=li % spec.layers if spec.layers > 1 else 0,
+                                 seed=seed + 1000 + li)
+            for li in range(nlogits)]
+    nrep = len(exs)
+    counts = [touched(torch, moe4, step, exs[0], *toks[i]) for i in range(nlogits)]
+
+    def run(i):
+        x, lg = toks[i % nlogits]
+        step.forward(exs[i % nrep], x, lg)
+
+    ms, (k_gu, k_dn) = time_steps(torch, hip, moe4, steps, warmup, run)
+    gu_b, dn_b = expert_bytes(spec)
+    # steps i = warmup .. warmup+steps-1 used logits set i % nlogits
+    ntouch = sum(counts[(warmup + i) % nlogits] for i in range(steps)) / steps
+    S = T * spec.k
+    flops_gu = 2.0 * S * 2 * spec.I * spec.H
+    flops_dn = 2.0 * S * spec.H * spec.I
+    res = {
+        "workload": spec.name, "T": T, "ms_per_step": round(ms, 5),
+        "routed_tokens_per_s": round(T / (ms / 1e3), 1),
+        "kernel": moe4.moe4_last_variant() == moe4.MOE4_VARIANT_SKINNY and "skinny" or "tiled",
+        "gate_up_us": round(k_gu * 1e3, 2), "down_us": round(k_dn * 1e3, 2),
+        "touched_experts": round(ntouch, 2),
+        "weight_GBps": round(ntouch * (gu_b + dn_b) / ((k_gu + k_dn) * 1e-3) / 1e9, 1),
+        "gate_up_weight_GBps": round(ntouch * gu_b / (k_gu * 1e-3) / 1e9, 1),
+        "tflops": round((flops_gu + flops_dn) / ((k_gu + k_dn) * 1e-3) / 1e12, 2),
+        "gate_up_tflops": round(flops_gu / (k_gu * 1e-3) / 1e12, 2),
+    }
+    res["hbm_frac"] = round(res["weight_GBps"] / HBM_PEAK_GBS, 4)
+    res["mfma_frac"] = round(res["tflops"] / BF16_PEAK_TFLOPS, 4)
+    return res, (k_gu, flops_gu, ntouch * gu_b)
+
+
+def bench_backward(torch, hip, moe4, inputs, spec, T, ex, steps, warmup, seed):
+    step = Step(moe4, torch, spec, T, ex, backward=True)
+    x, lg = inputs.device_tokens(spec, T, seed=seed + 77)
+    dout = inputs.device_bf16((T, spec.H), 1.0, seed, spec, 0, 13)
+
+    def run_f(i):
+        step.forward(ex, x, lg)
+
+    def run_b(i):
+        step.backward_pass(ex, dout)
+
+    f_ms, (f_gu, f_dn) = time_steps(torch, hip, moe4, steps, warmup, run_f)
+    b_ms, (b_dn, b_gu) = time_steps(torch, hip, moe4, steps, warmup, run_b)
+    S = T * spec.k
+    H, I, r = spec.H, spec.I, spec.lora_r
+    f_flops = 2.0 * S * (2 * I * H + H * I)
+    lora_f = 2.0 * S * (r * H + 2 * I * r)
+    b_flops = 2.0 * S * (H * I + 2 * I * H)
+    lora_b = 2.0 * S * (2 * I * r + r * H) + 2.0 * S * (2 * I * r + r * H)
+    tot = f_flops + lora_f + b_flops + lora_b
+    return {
+        "workload": spec.name, "T": T, "forward_ms": round(f_ms, 4), "backward_ms": round(b_ms, 4),
+        "fwd_bwd_ms": round(f_ms + b_ms, 4),
+        "fwd_bwd_tflops_step": round(tot / ((f_ms + b_ms) * 1e-3) / 1e12, 2),
+        "fwd_gemm_tflops": round(f_flops / ((f_gu + f_dn) * 1e-3) / 1e12, 2),
+        "bwd_dgrad_tflops": round(b_flops / ((b_gu + b_dn) * 1e-3) / 1e12, 2),
+        "gemm_us": {"fwd_gate_up": round(f_gu * 1e3, 1), "fwd_down": round(f_dn * 1e3, 1),
+                    "bwd_down_dgrad": round(b_dn * 1e3, 1), "bwd_gate_up_dgrad": round(b_gu * 1e3, 1)},
+        "mfma_frac_step": round(tot / ((f_ms + b_ms) * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+    }
+
+
+def bench_stack(torch, hip, moe4, inputs, spec, T, exs, steps, warmup, seed):
+    """36-layer stack, layers back to back with independent inputs per layer."""
+    L = len(exs)
+    step = Step(moe4, torch, spec, T, exs[0])
+    toks = [inputs.device_tokens(spec, T, layer=l, seed=seed + 500) for l in range(L)]
+    counts = [touched(torch, moe4, step, exs[l], *toks[l]) for l in range(L)]
+
+    def run(i):
+        for l in range(L):
+            x, lg = toks[l]
+            step.forward(exs[l], x, lg)
+
+    # the hook times the last layer's kernels of each pass; the region is the stack
+    ms, _ = time_steps(torch, hip, moe4, steps, warmup, run)
+    gu_b, dn_b = expert_bytes(spec)
+    total_bytes = sum(counts) * (gu_b + dn_b)
+    return {"workload": spec.name, "T": T, "layers": L,
+            "stack_ms": round(ms, 4), "per_layer_us": round(ms * 1e3 / L, 2),
+            "touched_experts_per_layer": round(sum(counts) / L, 2),
+            "stack_weight_GB": round(total_bytes / 1e9, 4),
+            "stack_weight_GBps_end_to_end": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac_end_to_end": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+# -------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(spec, T_batch, n_tokens, seed=0):
+    """The CPU oracle, untuned, on a bounded sample of the headline workload:
+    n_tokens tokens of a T_batch batch through route -> permute -> expert
+    forward (dequantise + matmul per touched expert) -> combine."""
+    import numpy as np
+
+    import oracle
+    from bit_mixture_experts_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    x, lg = inputs.host_tokens(spec, T_batch, seed=seed)
+    x, lg = x[:n_tokens], lg[:n_tokens]
+    idx, _ = oracle.route(lg, spec.k)
+    need = sorted(set(int(e) for e in idx.reshape(-1)))
+    E, H, I = spec.E, spec.H, spec.I
+    gq = np.zeros((E, 2 * I, H // 2), np.uint8)
+    ga = np.zeros((E, 2 * I, H // 64), np.float32)
+    dq = np.zeros((E, H, I // 2), np.uint8)
+    da = np.zeros((E, H, I // 64), np.float32)
+    for e in need:   # set-up, not timed: quantise the experts the sample touches
+        wg, wd = inputs.host_nf4_source(spec, e, 0, seed)
+        p, a = oracle.quantize_nf4(wg.reshape(-1))
+        gq[e], ga[e] = p.reshape(2 * I, H // 2), a.reshape(2 * I, H // 64)
+        p, a = oracle.quantize_nf4(wd.reshape(-1))
+        dq[e], da[e] = p.reshape(H, I // 2), a.reshape(H, I // 64)
+    W = oracle.ExpertWeights.from_nf4(gq, ga, dq, da, layout=spec.layout, act=spec.act)
+    t0 = time.perf_counter()
+    ri, rw = oracle.route(lg, spec.k)
+    oracle.layer_forward(x, ri, rw, W)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 3), "unit": "routed tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{n_tokens} tokens of the T={T_batch} {spec.name} batch "
+                       f"({len(need)} experts touched): route, permute, per-expert NF4 "
+                       f"dequantise + float64 matmul, combine; {dt:.1f} s")}
+
+
+def traffic_from_profile(kernel_tag):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel_tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("csrc_sha256") != csrc_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def csrc_digest():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "bit_mixture_experts_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()
+
+
+# ----------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--only", default="", help="comma list of sweep parts: qwen,gptoss,lora,stack")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures a single GPU: the layer runs on one device here, with no "
+              "sharding or collectives; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_mixture_experts_amd import inputs, moe4
+    hip = Hip()
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+        f"{props.multi_processor_count} CUs")
+
+    spec = inputs.QWEN3_30B_NF4
+    t0 = time.time()
+    exs = [nf4_layer(moe4, inputs, spec, r, args.seed, torch) for r in range(args.replicas)]
+    torch.cuda.synchronize()
+    log(f"qwen3-shaped NF4 replicas ready ({time.time() - t0:.1f} s)")
+
+    head, (k_gu, flops_gu, _) = bench_layer(torch, hip, moe4, inputs, spec, HEADLINE_T, exs,
+                                            args.steps, args.warmup, args.seed)
+    log("headline:", json.dumps(head))
+    achieved = flops_gu / (k_gu * 1e-3) / 1e12
+    traffic = traffic_from_profile("gate_up_tiled_nf4_qwen3_T4096")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": "gate_up grouped GEMM (tiled, NF4)",
+                "avg_launch_us": round(k_gu * 1e3, 2)}
+
+    sweep = []
+    only = set(filter(None, args.only.split(",")))
+    if not args.no_sweep:
+        reps = max(10, args.steps)
+        if not only or "qwen" in only:
+            for T in (1, 16, 128):
+                r, _ = bench_layer(torch, hip, moe4, inputs, spec, T, exs, reps * 2, args.warmup,
+                                   args.seed)
+                log("sweep:", json.dumps(r))
+                sweep.append(r)
+            sweep.append(head)
+        if not only or "gptoss" in only:
+            g = inputs.GPT_OSS_20B_MXFP4
+            gex = [mxfp4_layer(moe4, inputs, g, r, args.seed, torch) for r in range(args.replicas)]
+            for T in g.tokens:
+                r, _ = bench_layer(torch, hip, moe4, inputs, g, T, gex, reps * 2, args.warmup,
+                                   args.seed)
+                log("sweep:", json.dumps(r))
+                sweep.append(r)
+            del gex
+        if not only or "lora" in only:
+            lspec = inputs.QWEN3_30B_NF4_LORA
+            lex = nf4_layer(moe4, inputs, lspec, 0, args.seed, torch)
+            r = bench_backward(torch, hip, moe4, inputs, lspec, lspec.tokens[0], lex, reps,
+                               args.warmup, args.seed)
+            log("sweep:", json.dumps(r))
+            sweep.append(r)
+            del lex
+        if not only or "stack" in only:
+            s5 = inputs.GPT_OSS_120B_STACK
+            t0 = time.time()
+            sex = [mxfp4_layer(moe4, inputs, s5, l, args.seed, torch) for l in range(s5.layers)]
+            torch.cuda.synchronize()
+            log(f"36-layer MXFP4 stack ready ({time.time() - t0:.1f} s)")
+            for T in s5.tokens:
+                r = bench_stack(torch, hip, moe4, inputs, s5, T, sex, max(5, reps // 2),
+                                2, args.seed)
+                log("sweep:", json.dumps(r))
+                sweep.append(r)
+            del sex
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(spec, HEADLINE_T, args.cpu_tokens, args.seed)
+        log("cpu_baseline:", json.dumps(cpu))
+
+    line = {
+        "metric": "routed tokens/s + effective 4-bit weight GB/s (decode) / TFLOP/s (prefill), 1 GPU",
+        "value": head["routed_tokens_per_s"], "unit": "routed tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name} T={HEADLINE_T}", "T": HEADLINE_T, "E": spec.E,
+                   "top_k": spec.k, "H": spec.H, "I": spec.I, "format": "nf4",
+                   "replicas": args.replicas, "device": props.name},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,59 @@
+// Internal launcher interface between the C ABI (moe4_abi.hip) and the kernel
+// files. Launchers assume validated arguments and return hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe4.h"
+
+namespace moe4 {
+
+// ---- codecs
+hipError_t launch_quantize_nf4(const float* w, int64_t n, uint8_t* packed, float* absmax,
+                               hipStream_t s);
+hipError_t launch_decode_mxfp4(const uint8_t* blocks, const uint8_t* scales, int64_t R,
+                               int64_t K, uint16_t* out, hipStream_t s);
+
+// ---- routing / permutation / combine
+hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, int32_t* idx,
+                        float* w, hipStream_t s);
+size_t permute_ws_bytes(int T, int k, int E);
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
+                          int32_t* slot_of_row, int32_t* row_of_slot, const uint16_t* x,
+                          const float* row_scale, int H, uint16_t* x_perm, void* ws,
+                          hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+hipError_t launch_combine(const float* y, const int32_t* row_of_slot, const float* w, int T,
+                          int k, int H, void* out, bool out_f32, hipStream_t s);
+
+// ---- expert forward / backward
+size_t forward_ws_bytes(const moe4_experts& ex, int rows);
+size_t backward_ws_bytes(const moe4_experts& ex, int rows);
+// Optional events recorded around the two GEMM launches (null = off):
+// ev[0]/ev[1] around the first, ev[2]/ev[3] around the second.
+struct LaunchEvents {
+  hipEvent_t const* ev;
+  void before(int i, hipStream_t s) const {
+    if (ev) hipEventRecord(ev[2 * i], s);
+  }
+  void after(int i, hipStream_t s) const {
+    if (ev) hipEventRecord(ev[2 * i + 1], s);
+  }
+};
+
+// returns the kernel family used through *variant
+hipError_t launch_expert_forward(const moe4_experts& ex, const uint16_t* x_perm,
+                                 const int32_t* offsets, int rows, float* y_perm,
+                                 float* save_gu, float* save_xa, void* ws, int* variant,
+                                 const LaunchEvents& le, hipStream_t s);
+hipError_t launch_expert_backward(const moe4_experts& ex, const uint16_t* x_perm,
+                                  const int32_t* offsets, int rows, const float* save_gu,
+                                  const float* save_xa, const uint16_t* dy_perm,
+                                  float* dx_perm, float* dA, float* dB, void* ws,
+                                  int* variant, const LaunchEvents& le, hipStream_t s);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace moe4

@@ -21,9 +21,14 @@ Sources (web pages, cited by title and section):
   them from an NVMe arena?" -- section "Why it happens".
 
 Precision: the oracle computes in float64 except where the method itself fixes a
-precision (fp32 absmax and the fp32 division that decides an NF4 code; fp32
-router logits; the bf16 value of a row-scaled permutation, which the interface
-defines as an fp32 product rounded to bf16).
+precision: fp32 absmax and the fp32 division that decides an NF4 code; fp32
+router logits; and bf16 wherever the layer hands a value to a bf16 GEMM operand
+(the model dtype is bf16, accumulation fp32): the dequantised weight
+bf16(fp32(level * absmax)), the activation h, the LoRA intermediates xa and
+t = dGU B, dGU, and the row-scaled gradient bf16(fp32(w * dOut)). Sums and
+outputs (gu, y, out, dX, dA, dB) stay float64. ``layer_forward`` and
+``layer_backward`` take exact=True to drop every bf16 step, which the
+finite-difference pins of the backward use.
 
 Pin status: every public function has a pin in ``tests/test_oracle_*.py`` that
 does not re-use the oracle's own formula (closed forms, exhaustive enumeration,
@@ -31,16 +36,16 @@ brute force on tiny inputs, float64 finite differences, torch CPU autograd, the
 published NF4 construction). No function is "parity unpinned".
 """
 
-from .numerics import bf16_bits_from_f32, bf16_bits_to_f64, bf16_bits_to_f32
+from .numerics import bf16_bits_from_f32, bf16_bits_to_f64, bf16_bits_to_f32, bf16_round_f64
 from .formats import (NF4_LEVELS, nf4_midpoints, quantize_nf4, dequantize_nf4,
-                      E2M1_MAGNITUDES, mxfp4_values, decode_mxfp4_bf16)
+                      dequantize_nf4_bf16, E2M1_MAGNITUDES, mxfp4_values, decode_mxfp4_bf16)
 from .routing import route, permute, gather_rows
 from .layer import (ExpertWeights, gate_up, activation, down, combine,
                     layer_forward, layer_backward, token_forward)
 
 __all__ = [
-    "bf16_bits_from_f32", "bf16_bits_to_f64", "bf16_bits_to_f32",
-    "NF4_LEVELS", "nf4_midpoints", "quantize_nf4", "dequantize_nf4",
+    "bf16_bits_from_f32", "bf16_bits_to_f64", "bf16_bits_to_f32", "bf16_round_f64",
+    "NF4_LEVELS", "nf4_midpoints", "quantize_nf4", "dequantize_nf4", "dequantize_nf4_bf16",
     "E2M1_MAGNITUDES", "mxfp4_values", "decode_mxfp4_bf16",
     "route", "permute", "gather_rows",
     "ExpertWeights", "gate_up", "activation", "down", "combine",

@@ -23,7 +23,7 @@ Readings where the pages are silent (each also listed in the design notes):
 
 import numpy as np
 
-from .numerics import bf16_bits_from_f32
+from .numerics import bf16_bits_from_f32, bf16_bits_to_f64
 
 # NormalFloat4 levels, exact float32 numbers (QLoRA paper, appendix E).
 NF4_LEVELS = np.array([
@@ -97,6 +97,22 @@ def dequantize_nf4(packed, absmax):
     if am.size != codes.shape[0]:
         raise ValueError("absmax length does not match the packed data")
     return (NF4_LEVELS.astype(np.float64)[codes] * am[:, None]).reshape(-1)
+
+
+def dequantize_nf4_bf16(packed, absmax):
+    """The bf16 operand value of each NF4 weight: level[code] * absmax formed
+    as one IEEE fp32 product, then rounded once to bf16 (float64 result).
+
+    Reading: the pages fix fp32 accumulation over bf16 operands but not how the
+    decoded weight is rounded; one fp32 product and one rounding is the plain
+    way to form a bf16 operand from an fp32 level and an fp32 absmax.
+    """
+    codes = nf4_codes(packed).reshape(-1, NF4_BLOCK)
+    am = np.asarray(absmax, dtype=np.float32).reshape(-1)
+    if am.size != codes.shape[0]:
+        raise ValueError("absmax length does not match the packed data")
+    prod = (NF4_LEVELS[codes] * am[:, None]).astype(np.float32)   # fp32 product
+    return bf16_bits_to_f64(bf16_bits_from_f32(prod)).reshape(-1)
 
 
 def mxfp4_values(blocks, scales):

@@ -28,7 +28,15 @@ Readings (the pages are silent):
 * Backward covers the expert path only (router logits are given inputs):
   dX, dA, dB; the frozen base and biases get no gradient. Clamp derivatives
   pass where the clamp is inactive, boundaries included.
-* No intermediate rounding: the oracle keeps every intermediate in float64.
+* Precision: bf16 model tensors with fp32 accumulation (solutions index,
+  grouped-nf4-gemm entries; experts4bit-qlora page, the adapter runs in the
+  model dtype, bf16). The oracle rounds to bf16 exactly where a value becomes
+  an operand of a bf16 GEMM -- the dequantised NF4 weight
+  bf16(fp32(level * absmax)) (MXFP4 values are exact in bf16), h, xa before
+  the B product, dGU, and t = dGU B before the A product -- and where the
+  interface defines a bf16 tensor (the row-scaled gradient). Every sum and
+  every output stays float64. exact=True drops all of these roundings (the
+  backward is pinned against finite differences in that mode).
 """
 
 from dataclasses import dataclass, field
@@ -36,8 +44,8 @@ from typing import Callable, Optional
 
 import numpy as np
 
-from .formats import dequantize_nf4, mxfp4_values
-from .numerics import bf16_bits_to_f64
+from .formats import dequantize_nf4, dequantize_nf4_bf16, mxfp4_values
+from .numerics import bf16_bits_from_f32, bf16_bits_to_f64, bf16_round_f64
 from .routing import permute
 
 HALVES = "halves"
@@ -83,16 +91,18 @@ class ExpertWeights:
     @classmethod
     def from_nf4(cls, gu_packed, gu_absmax, dn_packed, dn_absmax, *, layout, act,
                  gu_bias=None, dn_bias=None, lora_A=None, lora_B=None,
-                 lora_scale=0.0, alpha=1.702, limit=7.0):
+                 lora_scale=0.0, alpha=1.702, limit=7.0, bf16_weights=True):
         """Stacks: gu_packed [E,2I,H/2], gu_absmax [E,2I,H/64],
         dn_packed [E,H,I/2], dn_absmax [E,H,I/64]; bf16 bits for biases and
-        adapters (A [E,r,H], B [E,2I,r])."""
+        adapters (A [E,r,H], B [E,2I,r]). bf16_weights=False keeps the exact
+        level * absmax values instead of the bf16 GEMM operands."""
         E, N2, Hh = gu_packed.shape
         H, I = Hh * 2, N2 // 2
+        deq = dequantize_nf4_bf16 if bf16_weights else dequantize_nf4
         return cls(
             E=E, H=H, I=I, layout=layout, act=act,
-            gu=lambda e: dequantize_nf4(gu_packed[e], gu_absmax[e]).reshape(2 * I, H),
-            dn=lambda e: dequantize_nf4(dn_packed[e], dn_absmax[e]).reshape(H, I),
+            gu=lambda e: deq(gu_packed[e], gu_absmax[e]).reshape(2 * I, H),
+            dn=lambda e: deq(dn_packed[e], dn_absmax[e]).reshape(H, I),
             b_gu=cls._bias(gu_bias), b_dn=cls._bias(dn_bias),
             lora_A=cls._bias(lora_A), lora_B=cls._bias(lora_B),
             lora_scale=lora_scale, alpha=alpha, limit=limit)
@@ -152,9 +162,14 @@ def join_gate_up(g, u, layout):
     return out
 
 
-def gate_up(X, W, e):
+def _op(v, exact):
+    """A value handed to a bf16 GEMM operand (unchanged when exact)."""
+    return v if exact else bf16_round_f64(v)
+
+
+def gate_up(X, W, e, exact=False):
     """gu = X W_gu[e]^T + bias + LoRA delta, float64 [n, 2I]; also returns
-    xa = X A_e^T (or None)."""
+    xa = X A_e^T (float64, before its bf16 rounding; or None)."""
     Wgu, _ = W.expert(e)
     gu = X @ Wgu.T
     if W.b_gu is not None:
@@ -162,7 +177,7 @@ def gate_up(X, W, e):
     xa = None
     if W.lora_A is not None:
         xa = X @ W.lora_A(e).T
-        gu = gu + W.lora_scale * (xa @ W.lora_B(e).T)
+        gu = gu + W.lora_scale * (_op(xa, exact) @ W.lora_B(e).T)
     return gu, xa
 
 
@@ -214,10 +229,10 @@ def combine(y, row_of_slot, topk_w, T, k):
     return out
 
 
-def layer_forward(x_bits, topk_idx, topk_w, W, keep=False):
+def layer_forward(x_bits, topk_idx, topk_w, W, keep=False, exact=False):
     """Whole-layer forward (x: bf16 bits or float64 [T,H]). Returns a dict
-    with ``out`` [T,H] and, with
-    keep=True, the per-row intermediates (``gu``, ``h``, ``y``, ``xa``)."""
+    with ``out`` [T,H], ``y`` [T*k,H] and, with keep=True, the per-row
+    intermediates (``gu``, ``h`` as the bf16 operand, ``xa``)."""
     x = _as_f64(x_bits)
     T, k = np.asarray(topk_idx).shape
     offsets, slot_of_row, row_of_slot = permute(topk_idx, W.E)
@@ -234,8 +249,8 @@ def layer_forward(x_bits, topk_idx, topk_w, W, keep=False):
         if a == b:
             continue
         X = x[slot_of_row[a:b] // k]
-        gu, xa = gate_up(X, W, e)
-        h = activation(gu, W)
+        gu, xa = gate_up(X, W, e, exact)
+        h = _op(activation(gu, W), exact)
         y[a:b] = down(h, W, e)
         if keep:
             res["gu"][a:b], res["h"][a:b] = gu, h
@@ -246,22 +261,24 @@ def layer_forward(x_bits, topk_idx, topk_w, W, keep=False):
     return res
 
 
-def token_forward(x_row_bits, experts, weights, W):
+def token_forward(x_row_bits, experts, weights, W, exact=False):
     """out for one token: sum_j w_j * expert_j(x). For sampled checks at sizes
     where the whole layer is too slow on the host."""
     x = _as_f64(x_row_bits).reshape(1, -1)
     out = np.zeros(W.H)
     for e, w in zip(experts, weights):
-        gu, _ = gate_up(x, W, int(e))
-        out += float(w) * down(activation(gu, W), W, int(e))[0]
+        gu, _ = gate_up(x, W, int(e), exact)
+        out += float(w) * down(_op(activation(gu, W), exact), W, int(e))[0]
     return out
 
 
-def layer_backward(x_bits, topk_idx, topk_w, dout_bits, W):
+def layer_backward(x_bits, topk_idx, topk_w, dout_bits, W, exact=False):
     """Gradient of sum_t <dOut[t], out[t]> with respect to x, A and B.
 
     Returns dict with ``dx`` [T,H], ``dA`` [E,r,H], ``dB`` [E,2I,r] (zero for
     experts that receive no rows), plus the per-row ``dgu`` and ``dx_perm``.
+    Unless exact, the routing weights enter as fp32 (the interface's dtype) and
+    the scaled upstream gradient is bf16(fp32(w * dOut)).
     """
     x = _as_f64(x_bits)
     dout = _as_f64(dout_bits)
@@ -281,17 +298,22 @@ def layer_backward(x_bits, topk_idx, topk_w, dout_bits, W):
             continue
         slots = slot_of_row[a:b]
         X = x[slots // k]
-        dY = w[slots][:, None] * dout[slots // k]
-        gu, xa = gate_up(X, W, e)
+        if exact:
+            dY = w[slots][:, None] * dout[slots // k]
+        else:
+            prod = (w[slots].astype(np.float32)[:, None] *
+                    dout[slots // k].astype(np.float32)).astype(np.float32)
+            dY = bf16_bits_to_f64(bf16_bits_from_f32(prod))
+        gu, xa = gate_up(X, W, e, exact)
         Wgu, Wd = W.expert(e)
         dH = dY @ Wd
-        dGU = activation_backward(gu, dH, W)
+        dGU = _op(activation_backward(gu, dH, W), exact)
         dX = dGU @ Wgu
         if lora:
             A, B = W.lora_A(e), W.lora_B(e)
-            t = dGU @ B
+            t = _op(dGU @ B, exact)
             dX = dX + W.lora_scale * (t @ A)
-            dB[e] = W.lora_scale * (dGU.T @ xa)
+            dB[e] = W.lora_scale * (dGU.T @ _op(xa, exact))
             dA[e] = W.lora_scale * (t.T @ X)
         dx_perm[a:b] = dX
         dgu_all[a:b] = dGU

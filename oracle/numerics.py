@@ -34,3 +34,27 @@ def bf16_bits_to_f32(bits):
 def bf16_bits_to_f64(bits):
     """Exact float64 value of bf16 bit patterns."""
     return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def bf16_round_f64(x):
+    """Round float64 values once to the nearest bfloat16 value (ties to even);
+    returns float64. Used where the layer feeds a value to a bf16 GEMM operand.
+
+    Normal range: 8 significant bits. Below 2^-126 the spacing is fixed at
+    2^-133 (bf16 subnormals). Beyond the largest finite bf16 value, rounding
+    goes to +-inf as round-to-nearest-even does.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    fin = np.isfinite(x)
+    out[~fin] = x[~fin]
+    xf = x[fin]
+    m, e = np.frexp(xf)                    # xf = m * 2^e, 0.5 <= |m| < 1
+    normal = e > -125                      # |x| >= 2^-126
+    r = np.empty_like(xf)
+    r[normal] = np.ldexp(np.rint(m[normal] * 256.0), e[normal] - 8)
+    r[~normal] = np.ldexp(np.rint(np.ldexp(xf[~normal], 133)), -133)
+    big = np.abs(r) >= 2.0 ** 128
+    r[big] = np.copysign(np.inf, r[big])
+    out[fin] = r
+    return out

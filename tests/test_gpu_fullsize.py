@@ -1,0 +1,225 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (automatic kernel choice). The whole batch's routing,
+permutation and gathered rows are checked bit-exactly; layer outputs are
+checked on sampled tokens, which the oracle computes one by one from its own
+quantisation of the experts those tokens use (the GPU-quantised codes of those
+experts are compared bit-exactly first)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_mixture_experts_amd import inputs as inp
+from tests.gpu_helpers import DEV, assert_close, bits, run_layer, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+moe4 = pytest.importorskip("bit_mixture_experts_amd.moe4")
+
+
+class BigNF4Layer:
+    """NF4 stack quantised on the GPU from the seeded fp32 source; the oracle
+    re-quantises single experts on demand from the same source."""
+
+    def __init__(self, spec, layer=0, seed=0):
+        self.spec, self.layer, self.seed = spec, layer, seed
+        E, H, I = spec.E, spec.H, spec.I
+        wg = torch.empty((E, 2 * I, H), dtype=torch.float32, device=DEV)
+        wd = torch.empty((E, H, I), dtype=torch.float32, device=DEV)
+        for e in range(E):
+            g, d = inp.host_nf4_source(spec, e, layer, seed)
+            wg[e].copy_(torch.from_numpy(g))
+            wd[e].copy_(torch.from_numpy(d))
+        self.gq = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=DEV)
+        self.gs = torch.empty((E, 2 * I, H // 64), dtype=torch.float32, device=DEV)
+        self.dq = torch.empty((E, H, I // 2), dtype=torch.uint8, device=DEV)
+        self.ds = torch.empty((E, H, I // 64), dtype=torch.float32, device=DEV)
+        moe4.moe4_quantize_nf4(wg, self.gq, self.gs)
+        moe4.moe4_quantize_nf4(wd, self.dq, self.ds)
+        torch.cuda.synchronize()
+        del wg, wd
+        torch.cuda.empty_cache()
+        self.A = self.B = None
+        if spec.lora_r:
+            self.A, self.B = inp.host_stack_lora(spec, layer, seed)
+        self._q = {}
+
+    def oracle_expert(self, e):
+        if e not in self._q:
+            g, d = inp.host_nf4_source(self.spec, e, self.layer, self.seed)
+            q = oracle.quantize_nf4(g.reshape(-1)) + oracle.quantize_nf4(d.reshape(-1))
+            # the GPU quantiser's output for this expert is bit-exact
+            assert np.array_equal(self.gq[e].cpu().numpy().reshape(-1), q[0])
+            assert np.array_equal(self.gs[e].cpu().numpy().reshape(-1), q[1])
+            assert np.array_equal(self.dq[e].cpu().numpy().reshape(-1), q[2])
+            assert np.array_equal(self.ds[e].cpu().numpy().reshape(-1), q[3])
+            if len(self._q) > 16:
+                self._q.clear()
+            self._q[e] = q
+        return self._q[e]
+
+    def W(self):
+        s = self.spec
+        I, H = s.I, s.H
+        return oracle.ExpertWeights(
+            E=s.E, H=H, I=I, layout=s.layout, act=s.act,
+            gu=lambda e: oracle.dequantize_nf4_bf16(*self.oracle_expert(e)[:2]).reshape(2 * I, H),
+            dn=lambda e: oracle.dequantize_nf4_bf16(*self.oracle_expert(e)[2:]).reshape(H, I),
+            lora_A=None if self.A is None else (lambda e: oracle.bf16_bits_to_f64(self.A[e])),
+            lora_B=None if self.B is None else (lambda e: oracle.bf16_bits_to_f64(self.B[e])),
+            lora_scale=s.lora_scale)
+
+    def device(self):
+        s = self.spec
+        lora = {}
+        if self.A is not None:
+            lora = dict(lora_A=to_dev(self.A), lora_B=to_dev(self.B), lora_scale=s.lora_scale)
+        return moe4.Experts(moe4.MOE4_FMT_NF4, self.gq, self.gs, self.dq, self.ds,
+                            gu_layout=moe4.MOE4_GU_HALVES, act=moe4.MOE4_ACT_SWIGLU,
+                            E=s.E, H=s.H, I=s.I, **lora)
+
+
+class BigMXFP4Layer:
+    def __init__(self, spec, layer=0, seed=0):
+        self.spec = spec
+        self.q = inp.host_stack_mxfp4(spec, layer, seed)
+        self.bias = inp.host_stack_bias(spec, layer, seed) if spec.bias else (None, None)
+        self.W = oracle.ExpertWeights.from_mxfp4(*self.q, layout=spec.layout, act=spec.act,
+                                                 gu_bias=self.bias[0], dn_bias=self.bias[1],
+                                                 alpha=spec.alpha, limit=spec.limit)
+
+    def device(self):
+        s = self.spec
+        t = lambda a: None if a is None else to_dev(a)
+        return moe4.Experts(moe4.MOE4_FMT_MXFP4, *[to_dev(a) for a in self.q],
+                            gu_layout=moe4.MOE4_GU_INTERLEAVED, act=moe4.MOE4_ACT_SWIGLU_CLAMPED,
+                            E=s.E, H=s.H, I=s.I, gu_bias=t(self.bias[0]), dn_bias=t(self.bias[1]),
+                            act_alpha=s.alpha, act_limit=s.limit)
+
+
+def _check_layer(spec, W, ex, T, n_sample, layer=0, seed=0):
+    x, lg = inp.host_tokens(spec, T, layer, seed)
+    say(f"  T={T}: running the layer")
+    res = run_layer(ex, to_dev(x), to_dev(lg), spec.k)
+    say(f"  kernel family {res['variant']}; checking routing and permutation")
+    ri, rw = oracle.route(lg, spec.k)
+    assert np.array_equal(res["idx"].cpu().numpy(), ri)
+    assert np.allclose(res["w"].cpu().numpy(), rw, rtol=1e-5, atol=0)
+    ro, rs, rr = oracle.permute(ri, spec.E)
+    assert np.array_equal(res["offsets"].cpu().numpy(), ro)
+    assert np.array_equal(res["slot_of_row"].cpu().numpy(), rs)
+    assert np.array_equal(res["row_of_slot"].cpu().numpy(), rr)
+    assert np.array_equal(bits(res["x_perm"]), oracle.gather_rows(x, rs, spec.k))
+    rng = np.random.default_rng(T)
+    tokens = np.sort(rng.choice(T, min(T, n_sample), replace=False))
+    say(f"  oracle on {len(tokens)} sampled tokens")
+    ref = np.stack([oracle.token_forward(x[t], ri[t], rw[t], W) for t in tokens])
+    got = res["out32"].cpu().numpy()[tokens]
+    assert_close(got, ref, f"out (T={T}, sampled)")
+    return res
+
+
+@pytest.mark.parametrize("T", [1, 16, 128, 4096])
+def test_qwen3_30b_a3b_nf4_full(T, qwen_layer):
+    say(f"Qwen3-30B-A3B-shaped NF4 layer, T={T}")
+    _check_layer(inp.QWEN3_30B_NF4, qwen_layer.W(), qwen_layer.device(), T, 6)
+
+
+@pytest.fixture(scope="module")
+def qwen_layer():
+    say("building the Qwen3-30B-A3B-shaped NF4 stack (GPU quantisation)")
+    return BigNF4Layer(inp.QWEN3_30B_NF4)
+
+
+@pytest.fixture(scope="module")
+def gptoss_layer():
+    say("building the gpt-oss-20b-shaped MXFP4 stack")
+    return BigMXFP4Layer(inp.GPT_OSS_20B_MXFP4)
+
+
+@pytest.mark.parametrize("T", [1, 64, 2048])
+def test_gpt_oss_20b_mxfp4_full(T, gptoss_layer):
+    say(f"gpt-oss-20b-shaped MXFP4 layer, T={T}")
+    _check_layer(inp.GPT_OSS_20B_MXFP4, gptoss_layer.W, gptoss_layer.device(), T, 8)
+
+
+def test_gpt_oss_20b_decode_stack_bit_exact(gptoss_layer):
+    say("MXFP4 decode of the full gpt-oss-20b-shaped gate_up stack")
+    q, s = gptoss_layer.q[0], gptoss_layer.q[1]
+    out = torch.empty(s.shape[:-1] + (s.shape[-1] * 32,), dtype=torch.bfloat16, device=DEV)
+    moe4.moe4_decode_mxfp4(to_dev(q), to_dev(s), out)
+    torch.cuda.synchronize()
+    for e in (0, 17, 31):   # whole experts
+        assert np.array_equal(bits(out[e]), oracle.decode_mxfp4_bf16(q[e], s[e]))
+    rows = np.random.default_rng(3).choice(s.shape[1], 64, replace=False)
+    for e in range(s.shape[0]):   # sampled rows of every expert
+        assert np.array_equal(bits(out[e][rows]), oracle.decode_mxfp4_bf16(q[e][rows], s[e][rows]))
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_gpt_oss_120b_stack_layer_full(T):
+    spec = inp.GPT_OSS_120B_STACK
+    layer = 7   # one of the 36 independently seeded layers, with its Zipf skew
+    say(f"gpt-oss-120b-shaped MXFP4 stack, layer {layer}, T={T}")
+    L = _stack_layer(spec, layer)
+    _check_layer(spec, L.W, L.device(), T, 8, layer=layer)
+
+
+_STACK = {}
+
+
+def _stack_layer(spec, layer):
+    if layer not in _STACK:
+        _STACK.clear()
+        _STACK[layer] = BigMXFP4Layer(spec, layer)
+    return _STACK[layer]
+
+
+def test_lora_backward_full(qwen_lora_layer):
+    spec = inp.QWEN3_30B_NF4_LORA
+    T = spec.tokens[0]
+    say(f"per-expert LoRA on the Qwen3-shaped NF4 stack, T={T}: forward + backward")
+    L = qwen_lora_layer
+    ex = L.device()
+    x, lg = inp.host_tokens(spec, T)
+    dout = inp.host_upstream_grad(spec, T)
+    res = run_layer(ex, to_dev(x), to_dev(lg), spec.k, save=True)
+    S = T * spec.k
+    dy = torch.empty((S, spec.H), dtype=torch.bfloat16, device=DEV)
+    sc = torch.empty(S, dtype=torch.int32, device=DEV)
+    moe4.moe4_permute(res["idx"], spec.E, torch.empty_like(res["offsets"]), sc,
+                      torch.empty_like(sc), x=to_dev(dout), row_scale=res["w"].reshape(-1),
+                      x_perm=dy, ws=res["ws"])
+    dx_perm = torch.empty((S, spec.H), dtype=torch.float32, device=DEV)
+    dA = torch.empty((spec.E, spec.lora_r, spec.H), dtype=torch.float32, device=DEV)
+    dB = torch.empty((spec.E, 2 * spec.I, spec.lora_r), dtype=torch.float32, device=DEV)
+    moe4.moe4_expert_backward(ex, res["x_perm"], res["offsets"], res["save_gu"], res["save_xa"],
+                              dy, dx_perm, dA, dB, ws=res["ws"])
+    dx = torch.empty((T, spec.H), dtype=torch.float32, device=DEV)
+    moe4.moe4_combine(dx_perm, res["row_of_slot"], None, dx, spec.k)
+    torch.cuda.synchronize()
+    ri, rw = oracle.route(lg, spec.k)
+    assert np.array_equal(res["idx"].cpu().numpy(), ri)
+    W = L.W()
+    # dX of sampled tokens: the oracle backward of those tokens alone
+    tokens = np.sort(np.random.default_rng(5).choice(T, 4, replace=False))
+    say("  oracle dX on sampled tokens")
+    refb = oracle.layer_backward(x[tokens], ri[tokens], rw[tokens], dout[tokens], W)
+    assert_close(dx.cpu().numpy()[tokens], refb["dx"], "dx (sampled)")
+    # dA, dB of one expert: the oracle backward over exactly the tokens routed to it
+    e = int(ri[0, 0])
+    toks = np.nonzero((ri == e).any(axis=1))[0]
+    say(f"  oracle dA/dB of expert {e} ({len(toks)} tokens)")
+    refe = oracle.layer_backward(x[toks], ri[toks], rw[toks], dout[toks], W)
+    assert_close(dA.cpu().numpy()[e], refe["dA"][e], f"dA[{e}]")
+    assert_close(dB.cpu().numpy()[e], refe["dB"][e], f"dB[{e}]")
+    # experts without rows have exact-zero adapter gradients
+    counts = np.bincount(ri.reshape(-1), minlength=spec.E)
+    for ee in np.nonzero(counts == 0)[0]:
+        assert torch.all(dA[ee] == 0) and torch.all(dB[ee] == 0)
+
+
+@pytest.fixture(scope="module")
+def qwen_lora_layer():
+    say("building the LoRA NF4 stack")
+    return BigNF4Layer(inp.QWEN3_30B_NF4_LORA)

@@ -1,0 +1,344 @@
+"""GPU parity against the oracle, element by element, at sizes the oracle
+finishes in seconds that still span several tiles and ragged tails. Every call
+goes through the C ABI (bit_mixture_experts_amd.moe4).
+
+Bars: bit-exact for the MXFP4 decode, NF4 codes/absmax, top-k indices, the
+permutation and x_perm; routing weights to 1e-5 relative; every other float
+output within max|err| <= 2e-2 * RMS(oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_mixture_experts_amd import inputs as inp
+from tests.gpu_helpers import (DEV, HostLayer, assert_close, bits, check_bf16_output, f64,
+                               run_layer, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+moe4 = pytest.importorskip("bit_mixture_experts_amd.moe4")
+
+# scaled-down shapes of the workloads (same formats, layouts, epilogues)
+QWEN_SMALL = inp.QWEN3_30B_NF4.scaled(name="qwen3_shaped_small", seed_id=102, E=16, H=512,
+                                      I=192, tokens=(5, 100))
+GPTOSS_SMALL = inp.GPT_OSS_20B_MXFP4.scaled(name="gpt_oss_shaped_small", seed_id=103, E=8,
+                                            H=352, I=352, tokens=(3, 200))
+LORA_SMALL = inp.QWEN3_30B_NF4_LORA.scaled(name="lora_small", seed_id=104, E=8, k=2, H=256,
+                                           I=128, tokens=(150,))
+MXFP4_LORA_SMALL = inp.GPT_OSS_20B_MXFP4.scaled(name="mxfp4_lora_small", seed_id=105, E=8, k=2,
+                                                H=320, I=192, tokens=(40,), lora_r=4,
+                                                lora_alpha=8.0)
+_LAYERS = {}
+
+
+def layer_of(spec):
+    if spec.name not in _LAYERS:
+        _LAYERS[spec.name] = HostLayer(spec)
+    return _LAYERS[spec.name]
+
+
+# ------------------------------------------------------------------- codecs
+
+def test_decode_mxfp4_exhaustive():
+    say("decode_mxfp4: all 256 bytes x 256 scales")
+    byte = np.repeat(np.arange(256, dtype=np.uint8), 256)
+    scale = np.tile(np.arange(256, dtype=np.uint8), 256)
+    blocks = np.repeat(byte[:, None], 16, axis=1).reshape(-1, 1, 16)
+    scales = scale.reshape(-1, 1)
+    out = torch.empty((blocks.shape[0], 32), dtype=torch.bfloat16, device=DEV)
+    moe4.moe4_decode_mxfp4(to_dev(blocks), to_dev(scales), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), oracle.decode_mxfp4_bf16(blocks, scales).reshape(-1, 32))
+
+
+def test_decode_mxfp4_stack_rows_ragged():
+    say("decode_mxfp4: gpt-oss-shaped small stack")
+    L = layer_of(GPTOSS_SMALL)
+    for q, s in ((L.gu_q, L.gu_s), (L.dn_q[:, :37], L.dn_s[:, :37])):
+        q = np.ascontiguousarray(q)
+        s = np.ascontiguousarray(s)
+        out = torch.empty(s.shape[:-1] + (s.shape[-1] * 32,), dtype=torch.bfloat16, device=DEV)
+        moe4.moe4_decode_mxfp4(to_dev(q), to_dev(s), out)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), oracle.decode_mxfp4_bf16(q, s))
+
+
+def test_quantize_nf4_bit_exact():
+    say("quantize_nf4: random, midpoint ties, zero and constant blocks")
+    rng = np.random.default_rng(20)
+    parts = [(rng.standard_normal(64 * 5000) * 0.02).astype(np.float32),
+             (rng.standard_normal(64 * 100) * 1e3).astype(np.float32),
+             np.zeros(64 * 3, np.float32),
+             np.full(64, -0.5, np.float32)]
+    # blocks whose elements sit exactly on the fp32 midpoints (absmax = 1)
+    mids = oracle.nf4_midpoints()
+    tie = np.zeros(64, np.float32)
+    tie[0] = 1.0
+    tie[1:16] = mids
+    tie[16:31] = -mids
+    parts.append(tie)
+    w = np.concatenate(parts)
+    packed = torch.empty(w.size // 2, dtype=torch.uint8, device=DEV)
+    absmax = torch.empty(w.size // 64, dtype=torch.float32, device=DEV)
+    moe4.moe4_quantize_nf4(to_dev(w), packed, absmax)
+    torch.cuda.synchronize()
+    rp, ra = oracle.quantize_nf4(w)
+    assert np.array_equal(packed.cpu().numpy(), rp)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), ra.view(np.uint32))
+
+
+def test_quantize_nf4_tiny_stack_matches_oracle_stack():
+    spec = inp.TINY_NF4
+    L = layer_of(spec)
+    for e in (0, spec.E - 1):
+        wg, wd = inp.host_nf4_source(spec, e)
+        for src, q, s in ((wg, L.gu_q[e], L.gu_s[e]), (wd, L.dn_q[e], L.dn_s[e])):
+            packed = torch.empty(src.size // 2, dtype=torch.uint8, device=DEV)
+            absmax = torch.empty(src.size // 64, dtype=torch.float32, device=DEV)
+            moe4.moe4_quantize_nf4(to_dev(src.reshape(-1)), packed, absmax)
+            torch.cuda.synchronize()
+            assert np.array_equal(packed.cpu().numpy(), q.reshape(-1))
+            assert np.array_equal(absmax.cpu().numpy(), s.reshape(-1))
+
+
+# ------------------------------------------------------------------ routing
+
+def _route(lg, k, renorm=True):
+    T, E = lg.shape
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    moe4.moe4_route(to_dev(lg), k, idx, w, renormalize=renorm)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,E,k,kind", [(64, 8, 2, "normal"), (300, 128, 8, "normal"),
+                                        (77, 32, 4, "normal"), (50, 128, 4, "zipf"),
+                                        (40, 1024, 16, "normal"), (33, 16, 16, "normal"),
+                                        (129, 64, 6, "ties"), (17, 1, 1, "normal")])
+def test_route_bit_exact(T, E, k, kind):
+    say(f"route T={T} E={E} k={k} {kind}")
+    rng = np.random.default_rng(T * 1000 + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if kind == "ties":
+        lg = rng.integers(-3, 3, (T, E)).astype(np.float32)
+        lg[lg == 0] = np.where(rng.random((lg == 0).sum()) < 0.5, 0.0, -0.0)
+    if kind == "zipf":
+        lg += -1.1 * np.log(1 + rng.permutation(E)).astype(np.float32)
+    for renorm in (True, False):
+        gi, gw = _route(lg, k, renorm)
+        ri, rw = oracle.route(lg, k, renormalize=renorm)
+        assert np.array_equal(gi, ri)
+        assert np.allclose(gw, rw, rtol=1e-5, atol=0)
+
+
+def _permute(idx, E, x=None, scale=None):
+    T, k = idx.shape
+    S = T * k
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    sor = torch.empty(max(S, 1), dtype=torch.int32, device=DEV)
+    ros = torch.empty(max(S, 1), dtype=torch.int32, device=DEV)
+    xd = None if x is None else to_dev(x)
+    x_perm = None if x is None else torch.empty((max(S, 1), x.shape[1]), dtype=torch.bfloat16,
+                                                device=DEV)
+    # a descriptor-free workspace size: the permutation part only needs E, T, k
+    ws = torch.empty(max(256, 4 * ((S + 2047) // 2048) * E + 256), dtype=torch.uint8, device=DEV)
+    moe4.moe4_permute(to_dev(idx), E, offsets, sor, ros, x=xd,
+                      row_scale=None if scale is None else to_dev(scale), x_perm=x_perm, ws=ws)
+    torch.cuda.synchronize()
+    return offsets, sor, ros, x_perm
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (1, 128, 8), (128, 128, 8), (200, 32, 4),
+                                   (3000, 128, 8), (300, 1024, 7), (1500, 4, 4)])
+def test_permute_bit_exact(T, E, k):
+    say(f"permute T={T} E={E} k={k}")
+    rng = np.random.default_rng(T + E + k)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    H = 40
+    x = inp.to_bf16_bits(rng.standard_normal((T, H)))
+    scale = rng.random(T * k).astype(np.float32)
+    for sc in (None, scale):
+        off, sor, ros, xp = _permute(idx, E, x, sc)
+        ro, rs, rr = oracle.permute(idx, E)
+        assert np.array_equal(off.cpu().numpy(), ro)
+        assert np.array_equal(sor.cpu().numpy(), rs)
+        assert np.array_equal(ros.cpu().numpy(), rr)
+        assert np.array_equal(bits(xp), oracle.gather_rows(x, rs, k, row_scale=sc))
+
+
+def test_permute_skewed_one_expert():
+    say("permute: every slot on one expert")
+    T, E, k = 2500, 64, 1
+    idx = np.full((T, k), 17, np.int32)
+    off, sor, ros, _ = _permute(idx, E)
+    ro, rs, rr = oracle.permute(idx, E)
+    assert np.array_equal(off.cpu().numpy(), ro) and np.array_equal(sor.cpu().numpy(), rs)
+
+
+def test_combine_against_oracle():
+    say("combine")
+    rng = np.random.default_rng(21)
+    T, k, H = 70, 4, 264
+    y = rng.standard_normal((T * k, H)).astype(np.float32)
+    ros = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    out32 = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    for ww in (w, None):
+        wd = None if ww is None else to_dev(ww)
+        moe4.moe4_combine(to_dev(y), to_dev(ros), wd, out, k)
+        moe4.moe4_combine(to_dev(y), to_dev(ros), wd, out32, k)
+        torch.cuda.synchronize()
+        ref = oracle.combine(y.astype(np.float64), ros, ww, T, k)
+        assert_close(out32.cpu().numpy(), ref, "combine out fp32")
+        # fp32 sum of k terms: relative error of a few fp32 ulps
+        assert np.all(np.abs(out32.cpu().numpy() - ref) <= 1e-6 * (np.abs(ref) + 1))
+        check_bf16_output(out, out32, ref, "combine out")
+
+
+# ------------------------------------------------------------ layer forward
+
+FWD_CASES = [(inp.TINY_NF4, 64), (QWEN_SMALL, 5), (QWEN_SMALL, 100), (GPTOSS_SMALL, 3),
+             (GPTOSS_SMALL, 200), (LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40)]
+
+
+@pytest.mark.parametrize("variant", [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED])
+@pytest.mark.parametrize("spec,T", FWD_CASES, ids=[f"{s.name}-T{t}" for s, t in FWD_CASES])
+def test_layer_forward(spec, T, variant):
+    say(f"forward {spec.name} T={T} variant={variant}")
+    L = layer_of(spec)
+    x, lg = inp.host_tokens(spec, T)
+    res = run_layer(L.device(variant), to_dev(x), to_dev(lg), spec.k, save=True)
+    assert res["variant"] == variant
+    ri, rw = oracle.route(lg, spec.k)
+    assert np.array_equal(res["idx"].cpu().numpy(), ri)
+    ref = oracle.layer_forward(x, ri, rw, L.W, keep=True)
+    assert np.array_equal(res["offsets"].cpu().numpy(), ref["offsets"])
+    assert_close(res["save_gu"].cpu().numpy(), ref["gu"], "gu")
+    assert_close(res["y_perm"].cpu().numpy(), ref["y"], "y_perm")
+    assert_close(res["out32"].cpu().numpy(), ref["out"], "out")
+    check_bf16_output(res["out"], res["out32"], ref["out"], "out")
+    if spec.lora_r:
+        assert_close(res["save_xa"].cpu().numpy(), ref["xa"], "xa")
+        # the adapter's own contribution, isolated: the GPU's gu minus the oracle's
+        # adapter-free gu, against the oracle's delta (relative L2, 5%)
+        base = oracle.layer_forward(x, ri, rw, _without_lora(L), keep=True)
+        got = res["save_gu"].cpu().numpy() - base["gu"]
+        want = ref["gu"] - base["gu"]
+        rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+        say(f"  lora delta relative L2 error {rel:.2e}")
+        assert rel < 0.05
+
+
+def _without_lora(L):
+    import copy
+    W = copy.copy(L.W)
+    W.lora_A = W.lora_B = None
+    W._cache = {}
+    return W
+
+
+def test_auto_variant_choice():
+    # decode-sized rows per expert pick the skinny kernel, prefill-sized the tiled one
+    L = layer_of(QWEN_SMALL)
+    for T, want in ((5, moe4.MOE4_VARIANT_SKINNY), (100, moe4.MOE4_VARIANT_TILED)):
+        x, lg = inp.host_tokens(QWEN_SMALL, T)
+        res = run_layer(L.device(), to_dev(x), to_dev(lg), QWEN_SMALL.k)
+        assert res["variant"] == want
+
+
+def test_forward_single_expert_overflow_rows():
+    """All tokens on one expert: the skinny kernel loops over row chunks and the
+    tiled kernel over several 128-row tiles."""
+    spec = inp.TINY_NF4
+    L = layer_of(spec)
+    T = 300
+    x, _ = inp.host_tokens(spec, T)
+    lg = np.full((T, spec.E), -5.0, np.float32)
+    lg[:, 3] = 5.0
+    lg[:, 6] = 4.0
+    ri, rw = oracle.route(lg, spec.k)
+    ref = oracle.layer_forward(x, ri, rw, L.W)
+    for variant in (moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED):
+        say(f"forward skewed variant={variant}")
+        res = run_layer(L.device(variant), to_dev(x), to_dev(lg), spec.k)
+        assert_close(res["out32"].cpu().numpy(), ref["out"], f"out skewed v{variant}")
+
+
+def test_forward_deterministic():
+    spec = GPTOSS_SMALL
+    L = layer_of(spec)
+    x, lg = inp.host_tokens(spec, 200)
+    ex = L.device()
+    a = run_layer(ex, to_dev(x), to_dev(lg), spec.k)
+    b = run_layer(ex, to_dev(x), to_dev(lg), spec.k)
+    for key in ("idx", "offsets", "slot_of_row", "x_perm", "y_perm", "out"):
+        assert torch.equal(a[key].view(torch.int16) if a[key].dtype == torch.bfloat16 else a[key],
+                           b[key].view(torch.int16) if b[key].dtype == torch.bfloat16 else b[key]), key
+
+
+def test_empty_inputs():
+    say("empty: T = 0")
+    spec = inp.TINY_NF4
+    L = layer_of(spec)
+    ex = L.device()
+    e = torch.empty(0, dtype=torch.int32, device=DEV)
+    lg = torch.empty((0, spec.E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((0, spec.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((0, spec.k), dtype=torch.float32, device=DEV)
+    moe4.moe4_route(lg, spec.k, idx, w)
+    offsets = torch.full((spec.E + 1,), 7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(moe4.moe4_workspace_size(ex, 0, spec.k), dtype=torch.uint8, device=DEV)
+    moe4.moe4_permute(idx, spec.E, offsets, e, e, ws=ws)
+    xp = torch.empty((0, spec.H), dtype=torch.bfloat16, device=DEV)
+    yp = torch.empty((0, spec.H), dtype=torch.float32, device=DEV)
+    moe4.moe4_expert_forward(ex, xp, offsets, yp, ws=ws)
+    out = torch.empty((0, spec.H), dtype=torch.bfloat16, device=DEV)
+    moe4.moe4_combine(yp, e, w, out, spec.k)
+    torch.cuda.synchronize()
+    assert torch.all(offsets == 0)
+
+
+# ----------------------------------------------------------------- backward
+
+BWD_CASES = [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40)]
+
+
+@pytest.mark.parametrize("spec,T", BWD_CASES, ids=[s.name for s, _ in BWD_CASES])
+def test_layer_backward(spec, T):
+    say(f"backward {spec.name} T={T}")
+    L = layer_of(spec)
+    ex = L.device()
+    x, lg = inp.host_tokens(spec, T)
+    dout = inp.host_upstream_grad(spec, T)
+    res = run_layer(ex, to_dev(x), to_dev(lg), spec.k, save=True)
+    S = T * spec.k
+    dy = torch.empty((S, spec.H), dtype=torch.bfloat16, device=DEV)
+    e0 = torch.empty(S, dtype=torch.int32, device=DEV)
+    moe4.moe4_permute(res["idx"], spec.E, torch.empty_like(res["offsets"]), e0,
+                      torch.empty_like(e0), x=to_dev(dout), row_scale=res["w"].reshape(-1),
+                      x_perm=dy, ws=res["ws"])
+    dx_perm = torch.empty((S, spec.H), dtype=torch.float32, device=DEV)
+    dA = torch.full((spec.E, spec.lora_r, spec.H), float("nan"), device=DEV)
+    dB = torch.full((spec.E, 2 * spec.I, spec.lora_r), float("nan"), device=DEV)
+    moe4.moe4_expert_backward(ex, res["x_perm"], res["offsets"], res["save_gu"], res["save_xa"],
+                              dy, dx_perm, dA, dB, ws=res["ws"])
+    dx = torch.empty((T, spec.H), dtype=torch.float32, device=DEV)
+    moe4.moe4_combine(dx_perm, res["row_of_slot"], None, dx, spec.k)
+    torch.cuda.synchronize()
+    ri, rw = oracle.route(lg, spec.k)
+    # the row-scaled gather is bit-exact with the oracle's definition
+    _, rs, _ = oracle.permute(ri, spec.E)
+    assert np.array_equal(bits(dy), oracle.gather_rows(dout, rs, spec.k,
+                                                       row_scale=res["w"].cpu().numpy().reshape(-1)))
+    ref = oracle.layer_backward(x, ri, rw, dout, L.W)
+    assert_close(dx_perm.cpu().numpy(), ref["dx_perm"], "dx_perm")
+    assert_close(dx.cpu().numpy(), ref["dx"], "dx")
+    dA_h, dB_h = dA.cpu().numpy(), dB.cpu().numpy()
+    counts = np.bincount(ri.reshape(-1), minlength=spec.E)
+    for e in range(spec.E):
+        if counts[e] == 0:
+            assert np.all(dA_h[e] == 0) and np.all(dB_h[e] == 0)
+    assert_close(dA_h, ref["dA"], "dA")
+    assert_close(dB_h, ref["dB"], "dB")

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 from oracle import (ExpertWeights, layer_forward, layer_backward, token_forward,
-                    route, quantize_nf4, activation, combine)
+                    route, quantize_nf4, activation, combine, bf16_round_f64)
 from oracle.layer import HALVES, INTERLEAVED, SWIGLU, SWIGLU_CLAMPED
 from tests.conftest import read_golden
 
@@ -39,10 +39,16 @@ def _sig(z):
 
 # ---------------------------------------------------------- brute force loops
 
+def _torch_bf16(v):
+    """fp32 value -> nearest bf16 (torch's CPU cast, an independent library)."""
+    return float(torch.tensor([v], dtype=torch.float32).to(torch.bfloat16).float()[0])
+
+
 def _nf4_w(packed, absmax, e, n, kk):
     byte = int(packed[e, n, kk // 2])
     nib = byte & 15 if kk % 2 == 0 else byte >> 4
-    return NF4_GOLD[nib] * float(absmax[e, n, kk // 64])
+    # the bf16 GEMM operand: one fp32 product, one rounding
+    return _torch_bf16(np.float32(NF4_GOLD[nib]) * np.float32(absmax[e, n, kk // 64]))
 
 
 def _mx_w(blocks, scales, e, n, kk):
@@ -68,6 +74,7 @@ def _brute_layer(x_bits, idx, w, wfun_gu, wfun_dn, H, I, layout, act, b_gu=None,
             if A is not None:
                 r = A.shape[1]
                 xa = [sum(x[c] * _bits_to_float(A[e, q, c]) for c in range(H)) for q in range(r)]
+                xa = [float(bf16_round_f64(v)) for v in xa]
                 for n in range(2 * I):
                     gu[n] += scale * sum(xa[q] * _bits_to_float(B[e, n, q]) for q in range(r))
             h = []
@@ -78,6 +85,7 @@ def _brute_layer(x_bits, idx, w, wfun_gu, wfun_dn, H, I, layout, act, b_gu=None,
                 else:
                     gc, uc = min(g, limit), max(-limit, min(u, limit))
                     h.append((uc + 1.0) * gc * _sig(alpha * gc))
+                h[-1] = float(bf16_round_f64(h[-1]))
             for c in range(H):
                 y = sum(h[i] * wfun_dn(e, c, i) for i in range(I))
                 if b_dn is not None:
@@ -147,11 +155,11 @@ def test_single_expert_reduces_to_library_swiglu_mlp():
     rng = np.random.default_rng(12)
     H, I, T = 128, 64, 5
     gq, ga, dq, da = _tiny_nf4(rng, 1, H, I)
-    W = ExpertWeights.from_nf4(gq, ga, dq, da, layout=HALVES, act=SWIGLU)
+    W = ExpertWeights.from_nf4(gq, ga, dq, da, layout=HALVES, act=SWIGLU, bf16_weights=False)
     x = _bf16(rng.standard_normal((T, H)))
     idx = np.zeros((T, 1), np.int32)
     w = np.ones((T, 1))
-    got = layer_forward(x, idx, w, W)["out"]
+    got = layer_forward(x, idx, w, W, exact=True)["out"]
     Wgu, Wd = (torch.from_numpy(a) for a in W.expert(0))
     xt = torch.from_numpy(x.astype(np.uint32) << 16).view(torch.float32).double()
     ref = (torch.nn.functional.silu(xt @ Wgu[:I].T) * (xt @ Wgu[I:].T)) @ Wd.T
@@ -221,7 +229,7 @@ def test_lora_only_special_case():
                                lora_A=A, lora_B=B, lora_scale=2.0)
     x = _bf16(rng.standard_normal((T, H)))
     idx = np.array([[1], [0], [1]], np.int32)
-    res = layer_forward(x, idx, np.ones((T, 1)), W, keep=True)
+    res = layer_forward(x, idx, np.ones((T, 1)), W, keep=True, exact=True)
     xt = torch.from_numpy(x.astype(np.uint32) << 16).view(torch.float32).double()
     At = torch.from_numpy(A.astype(np.uint32) << 16).view(torch.float32).double()
     Bt = torch.from_numpy(B.astype(np.uint32) << 16).view(torch.float32).double()
@@ -259,14 +267,14 @@ def test_backward_matches_finite_differences(layout, act, limit):
     dout = rng.standard_normal((T, H))
     idx = np.array([[0, 1], [1, 2], [0, 2], [2, 0], [1, 0]], np.int32)   # expert 3 idle
     w = rng.random((T, k)) + 0.2
-    gr = layer_backward(x, idx, w, dout, W)
+    gr = layer_backward(x, idx, w, dout, W, exact=True)
     if act == SWIGLU_CLAMPED:
-        gu = layer_forward(x, idx, w, W, keep=True)["gu"]
+        gu = layer_forward(x, idx, w, W, keep=True, exact=True)["gu"]
         assert (gu[:, 0::2] > limit).any() and (np.abs(gu[:, 1::2]) > limit).any()
 
     def loss():
         W._cache.clear()
-        return float(np.sum(dout * layer_forward(x, idx, w, W)["out"]))
+        return float(np.sum(dout * layer_forward(x, idx, w, W, exact=True)["out"]))
 
     eps = 1e-6
 
@@ -295,7 +303,7 @@ def test_backward_matches_torch_autograd():
     x = rng.standard_normal((T, H))
     dout = rng.standard_normal((T, H))
     idx, w = route(rng.standard_normal((T, E)).astype(np.float32), k)
-    gr = layer_backward(x, idx, w, dout, W)
+    gr = layer_backward(x, idx, w, dout, W, exact=True)
     xt = torch.tensor(x, requires_grad=True)
     At = torch.tensor(A, requires_grad=True)
     Bt = torch.tensor(B, requires_grad=True)
@@ -311,3 +319,44 @@ def test_backward_matches_torch_autograd():
     assert np.allclose(gr["dx"], xt.grad.numpy(), rtol=1e-10, atol=1e-12)
     assert np.allclose(gr["dA"], At.grad.numpy(), rtol=1e-10, atol=1e-12)
     assert np.allclose(gr["dB"], Bt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_rounded_backward_stays_near_exact_backward():
+    """The bf16 operand roundings of the backward (dY, dGU, t) move the result
+    by bf16-sized amounts only; the exact mode is pinned by finite differences."""
+    rng = np.random.default_rng(17)
+    E, H, I, r, T, k = 3, 64, 32, 4, 12, 2
+    W, *_ = _dense_layer(rng, E, H, I, r, HALVES, SWIGLU)
+    x = _bf16(rng.standard_normal((T, H)))
+    dout = _bf16(rng.standard_normal((T, H)))
+    idx, w = route(rng.standard_normal((T, E)).astype(np.float32), k)
+    ex = layer_backward(x, idx, w, dout, W, exact=True)
+    rd = layer_backward(x, idx, w, dout, W)
+    for key in ("dx", "dA", "dB"):
+        rel = np.linalg.norm(rd[key] - ex[key]) / np.linalg.norm(ex[key])
+        assert 0 < rel < 2e-2, (key, rel)
+
+
+def test_bf16_round_f64_is_the_nearest_bf16_value():
+    rng = np.random.default_rng(18)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-40, 38, 20000),
+                        np.ldexp(rng.random(2000), -130),            # subnormal range
+                        np.ldexp(2 * rng.integers(128, 256, 2000) + 1.0, -20)])  # 9-bit odd: exact ties
+    r = bf16_round_f64(x)
+    # r is a bf16 value
+    r32 = r.astype(np.float32)
+    assert np.array_equal(r32.astype(np.float64), r)
+    bits = r32.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0)
+    # no bf16 value is nearer: compare with the neighbours one bf16 ulp away
+    # (stepping the magnitude up and down; zero's neighbours are +-2^-133)
+    sign = np.where(bits >> 31, -1.0, 1.0)
+    mag = (bits & 0x7FFFFFFF).astype(np.int64)
+    up = sign * (mag + 0x10000).astype(np.uint32).view(np.float32).astype(np.float64)
+    dn = np.where(mag == 0, -np.sign(x) * 2.0 ** -133,
+                  sign * np.maximum(mag - 0x10000, 0).astype(np.uint32).view(np.float32))
+    d = np.abs(x - r)
+    assert np.all(d <= np.abs(x - up)) and np.all(d <= np.abs(x - dn))
+    # ties go to the even mantissa
+    tie = (d == np.abs(x - up)) | (d == np.abs(x - dn))
+    assert tie.any() and np.all(((bits[tie] >> 16) & 1) == 0)
