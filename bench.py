@@ -51,9 +51,11 @@ class Hip:
     def events(self, n):
         arr = (ctypes.c_void_p * n)()
         for i in range(n):
-            rc = self.lib.hipEventCreate(ctypes.byref(arr, i * ctypes.sizeof(ctypes.c_void_p)))
+            ev = ctypes.c_void_p()
+            rc = self.lib.hipEventCreate(ctypes.byref(ev))
             if rc != 0:
                 raise RuntimeError(f"hipEventCreate failed ({rc})")
+            arr[i] = ev.value
         return arr
 
     def ms(self, a, b):
@@ -152,7 +154,8 @@ class Step:
             self.dx = torch.empty((T, H), dtype=bf, device=dev)
             self.dA = torch.empty((E, r, H), dtype=f32, device=dev) if r else None
             self.dB = torch.empty((E, 2 * spec.I, r), dtype=f32, device=dev) if r else None
-            self.scratch_i = torch.empty(S, dtype=i32, device=dev)
+            self.scratch_sor = torch.empty(S, dtype=i32, device=dev)
+            self.scratch_ros = torch.empty(S, dtype=i32, device=dev)
             self.scratch_o = torch.empty(E + 1, dtype=i32, device=dev)
 
     def forward(self, ex, x, logits):
@@ -169,7 +172,7 @@ class Step:
 
     def backward_pass(self, ex, dout):
         m = self.moe4
-        m.moe4_permute(self.idx, self.spec.E, self.scratch_o, self.scratch_i, self.scratch_i,
+        m.moe4_permute(self.idx, self.spec.E, self.scratch_o, self.scratch_sor, self.scratch_ros,
                        x=dout, row_scale=self.w.reshape(-1), x_perm=self.dy, ws=self.ws)
         m.moe4_expert_backward(ex, self.x_perm, self.offsets, self.save_gu, self.save_xa, self.dy,
                                self.dx_perm, self.dA, self.dB, ws=self.ws)
