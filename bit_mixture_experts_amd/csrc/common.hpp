@@ -10,8 +10,30 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
+
+// Raw buffer resources: a load whose byte offset is at or past the resource's
+// size returns zeros, which takes the place of per-lane bounds branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kOob = 0x7FFFFFF0;   // offset past the end of any resource used here
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: 32-bit data format, no swizzle (gfx9 family)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load_b128(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_u8(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
@@ -23,8 +45,10 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// two fp32 -> packed bf16 pair (lo in bits 0..15), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
@@ -46,7 +70,10 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// logistic function; v_exp_f32 and v_rcp_f32 (about 1 ulp each)
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Locate work item q when expert e owns units(n_e) consecutive items
 // (n_e = offsets[e+1] - offsets[e]). Every lane of the wave gets the same

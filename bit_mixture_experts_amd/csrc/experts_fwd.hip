@@ -30,11 +30,6 @@
 namespace moe4 {
 namespace {
 
-// Copies of the byte -> level table in LDS. Lanes look up data-dependent
-// entries; with the table stored entry-major and lane l reading copy l % 32,
-// the lookups of a wave fall in distinct banks instead of colliding.
-constexpr int kLutCopies = 1;
-
 // ------------------------------------------------------------ skinny kernel
 
 // 4x4 transpose of dwords across the four 16-lane rows of a wave: on entry
@@ -53,188 +48,172 @@ __device__ __forceinline__ void transpose4x4_rows(u32x4& v) {
   v[3] = d[1];
 }
 
-// K loop of one wave for NRT 16-row tiles of one expert's rows and two
-// 16-column weight tiles. Each k-iteration covers 128 k: lane (n = l%16,
-// g = l/16) loads 16 bytes (32 k) of its weight row with one 128-bit load, so
-// the four lanes of a row read 64 contiguous bytes.
+// Per-wave operands of one 128-k iteration of the skinny kernel.
+template <int FMT, int NRT>
+struct SkinnyBatch {
+  u32x4 wraw[2];
+  float sc[2][FMT == MOE4_FMT_NF4 ? 1 : 4];
+  u32x4 av[NRT][4];
+};
+
+// Buffer resources and lane offsets of one wave of the skinny kernel.
+struct SkinnyLane {
+  rsrc_t rq, rs, ra;    // this expert's nibbles and scales; this row chunk's activations
+  int qoff[2];          // byte offset of the lane's 16-byte column in weight row c, k = 0
+  int srow[2];          // weight row index of column tile c (inside the expert)
+};
+
+// Each k-iteration covers 128 k: lane (n = l%16, g = l/16) loads 16 bytes
+// (32 k) of its weight row with one 128-bit load, so the four lanes of a row
+// read 64 contiguous bytes.
 //  NF4: lane g's 32 k lie in one absmax block; each weight becomes
 //       bf16(level * absmax) and MFMA step s uses k = kb + 32g + 8s.
 //  MXFP4: the 4x4 transpose above makes MFMA step s cover exactly the 32-k
 //       block kb/32 + s (k = kb + 32s + 8g), so the block's power-of-two
 //       scale multiplies the fp32 partial sum of that step.
-template <int FMT, int NRT, int U>
-struct SkinnyBatch {
-  u32x4 wraw[U][2];
-  float sc[U][2][FMT == MOE4_FMT_NF4 ? 1 : 4];
-  u32x4 av[U][NRT][4];
-};
-
-template <int FMT, int NRT, int U>
-__device__ __forceinline__ void skinny_load(SkinnyBatch<FMT, NRT, U>& bt, const GemmArgs& a,
-                                            const uint8_t* __restrict__ q0,
-                                            const uint8_t* __restrict__ q1, int64_t srow0,
-                                            int64_t srow1, const uint16_t* __restrict__ arow0,
-                                            int rows_here, int it, int it1) {
+template <int FMT, int NRT>
+__device__ __forceinline__ void skinny_load(SkinnyBatch<FMT, NRT>& bt, const SkinnyLane& sl,
+                                            int K, int it, int it1) {
   using F = Format<FMT>;
   constexpr bool PRESCALE = FMT == MOE4_FMT_NF4;
   const int l = lane_id(), nl = l & 15, g = l >> 4;
-  const int K = a.K;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  const int kb = it * 128;
+  const bool live = it < it1;
+  const bool ink = live && kb + 32 * g < K;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int kb = (it + u) * 128;
-    const bool live = it + u < it1;
-    const bool ink = live && kb + 32 * g < K;
-    bt.wraw[u][0] = ink ? *reinterpret_cast<const u32x4*>(q0 + kb / 2 + 16 * g) : z4;
-    bt.wraw[u][1] = ink ? *reinterpret_cast<const u32x4*>(q1 + kb / 2 + 16 * g) : z4;
+  for (int c = 0; c < 2; ++c) {
+    bt.wraw[c] = buf_load_b128(sl.rq, ink ? sl.qoff[c] + kb / 2 : kOob);
     if (PRESCALE) {
-      bt.sc[u][0][0] = ink ? F::scale(a.ws, srow0, K, (kb + 32 * g) / 64) : 0.0f;
-      bt.sc[u][1][0] = ink ? F::scale(a.ws, srow1, K, (kb + 32 * g) / 64) : 0.0f;
+      const int so = ink ? (sl.srow[c] * (K / 64) + (kb + 32 * g) / 64) * 4 : kOob;
+      bt.sc[c][0] = __uint_as_float(buf_load_b32(sl.rs, so));
     } else {
 #pragma unroll
-      for (int st = 0; st < (PRESCALE ? 1 : 4); ++st) {
+      for (int st = 0; st < 4; ++st) {
         const bool inb = live && kb + 32 * st < K;
-        bt.sc[u][0][st] = inb ? F::scale(a.ws, srow0, K, kb / 32 + st) : 0.0f;
-        bt.sc[u][1][st] = inb ? F::scale(a.ws, srow1, K, kb / 32 + st) : 0.0f;
+        bt.sc[c][st] = Format<MOE4_FMT_MXFP4>::e8m0(
+            buf_load_u8(sl.rs, inb ? sl.srow[c] * (K / 32) + kb / 32 + st : kOob));
       }
     }
+  }
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int m = rt * 16 + nl;
-      const uint16_t* ar = arow0 + (int64_t)m * K;
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int m = rt * 16 + nl;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int k = PRESCALE ? kb + 32 * g + 8 * st : kb + 32 * st + 8 * g;
-        bt.av[u][rt][st] = (live && m < rows_here && k < K)
-                               ? *reinterpret_cast<const u32x4*>(ar + k) : z4;
-      }
+    for (int st = 0; st < 4; ++st) {
+      const int k = PRESCALE ? kb + 32 * g + 8 * st : kb + 32 * st + 8 * g;
+      bt.av[rt][st] = buf_load_b128(sl.ra, (live && k < K) ? (m * K + k) * 2 : kOob);
     }
   }
 }
 
-template <int FMT, int NRT, int U>
-__device__ __forceinline__ void skinny_compute(const SkinnyBatch<FMT, NRT, U>& bt, int it,
-                                               int it1, const float2* lutf, const uint32_t* lut,
+template <int FMT, int NRT>
+__device__ __forceinline__ void skinny_compute(const SkinnyBatch<FMT, NRT>& bt,
+                                               const float2* lutf, const uint32_t* lut,
                                                f32x4 (&acc)[2][2]) {
   constexpr bool PRESCALE = FMT == MOE4_FMT_NF4;
-  // lutf / lut point at this lane's copy of the replicated table (stride kLutCopies)
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (it + u >= it1) break;
+  for (int c = 0; c < 2; ++c) {
+    if (PRESCALE) {
+      // 32 nibbles -> 32 bf16 operands bf16(level * absmax)
+      u32x4 bq[4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (PRESCALE) {
-        // 32 nibbles -> 32 bf16 operands bf16(level * absmax)
-        u32x4 bq[4];
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi) {
+          const float2 f = lutf[(bt.wraw[c][st] >> (8 * bi)) & 255u];
+          bq[st][bi] = pack_bf16x2(f.x * bt.sc[c][0], f.y * bt.sc[c][0]);
+        }
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
         for (int st = 0; st < 4; ++st)
+          acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, bt.av[rt][st]), __builtin_bit_cast(bf16x8, bq[st]),
+              acc[rt][c], 0, 0, 0);
+    } else {
+      u32x4 v = bt.wraw[c];
+      transpose4x4_rows(v);
 #pragma unroll
-          for (int bi = 0; bi < 4; ++bi) {
-            const float2 f = lutf[((bt.wraw[u][c][st] >> (8 * bi)) & 255u) * kLutCopies];
-            bq[st][bi] = pack_bf16x2(f.x * bt.sc[u][c][0], f.y * bt.sc[u][c][0]);
-          }
+      for (int st = 0; st < 4; ++st) {
+        u32x4 t;
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
+        for (int bi = 0; bi < 4; ++bi) t[bi] = lut[(v[st] >> (8 * bi)) & 255u];
+        const bf16x8 bq = __builtin_bit_cast(bf16x8, t);
 #pragma unroll
-          for (int st = 0; st < 4; ++st)
-            acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, bt.av[u][rt][st]), __builtin_bit_cast(bf16x8, bq[st]),
-                acc[rt][c], 0, 0, 0);
-      } else {
-        u32x4 v = bt.wraw[u][c];
-        transpose4x4_rows(v);
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          u32x4 t;
-          t[0] = lut[(v[st] & 255u) * kLutCopies];
-          t[1] = lut[((v[st] >> 8) & 255u) * kLutCopies];
-          t[2] = lut[((v[st] >> 16) & 255u) * kLutCopies];
-          t[3] = lut[(v[st] >> 24) * kLutCopies];
-          const bf16x8 bq = __builtin_bit_cast(bf16x8, t);
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, bt.av[u][rt][st]), bq, zero4, 0, 0, 0);
-            acc[rt][c] += bt.sc[u][c][st] * p;
-          }
+        for (int rt = 0; rt < NRT; ++rt) {
+          const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, bt.av[rt][st]), bq, zero4, 0, 0, 0);
+          acc[rt][c] += bt.sc[c][st] * p;
         }
       }
     }
   }
 }
 
-// K loop of one wave for NRT 16-row tiles of one expert's rows and two
-// 16-column weight tiles. Each k-iteration covers 128 k: lane (n = l%16,
-// g = l/16) loads 16 bytes (32 k) of its weight row with one 128-bit load, so
-// the four lanes of a row read 64 contiguous bytes. Batches of U iterations
-// are double-buffered: the next batch's loads are in flight while the current
-// one is dequantised and multiplied.
-//  NF4: lane g's 32 k lie in one absmax block; each weight becomes
-//       bf16(level * absmax) and MFMA step s uses k = kb + 32g + 8s.
-//  MXFP4: the 4x4 transpose above makes MFMA step s cover exactly the 32-k
-//       block kb/32 + s (k = kb + 32s + 8g), so the block's power-of-two
-//       scale multiplies the fp32 partial sum of that step.
-template <int FMT, int NRT, int U>
-__device__ __forceinline__ void skinny_kloop(const GemmArgs& a, const uint8_t* __restrict__ q0,
-                                             const uint8_t* __restrict__ q1, int64_t srow0,
-                                             int64_t srow1, const uint16_t* __restrict__ arow0,
-                                             int rows_here, int it0, int it1,
+// K loop of one wave over iterations [it0, it1) for NRT 16-row tiles; the
+// next iteration's loads are in flight while the current one is dequantised
+// and multiplied.
+template <int FMT, int NRT>
+__device__ __forceinline__ void skinny_kloop(const SkinnyLane& sl, int K, int it0, int it1,
                                              const float2* lutf, const uint32_t* lut,
                                              f32x4 (&acc)[2][2]) {
-  SkinnyBatch<FMT, NRT, U> b0, b1;
-  skinny_load(b0, a, q0, q1, srow0, srow1, arow0, rows_here, it0, it1);
-  for (int it = it0; it < it1; it += 2 * U) {
-    if (it + U < it1) skinny_load(b1, a, q0, q1, srow0, srow1, arow0, rows_here, it + U, it1);
-    skinny_compute(b0, it, it1, lutf, lut, acc);
-    if (it + U >= it1) break;
-    if (it + 2 * U < it1)
-      skinny_load(b0, a, q0, q1, srow0, srow1, arow0, rows_here, it + 2 * U, it1);
-    skinny_compute(b1, it + U, it1, lutf, lut, acc);
+  SkinnyBatch<FMT, NRT> b0, b1;
+  skinny_load(b0, sl, K, it0, it1);
+  for (int it = it0; it < it1; it += 2) {
+    if (it + 1 < it1) skinny_load(b1, sl, K, it + 1, it1);
+    skinny_compute(b0, lutf, lut, acc);
+    if (it + 1 >= it1) break;
+    if (it + 2 < it1) skinny_load(b0, sl, K, it + 2, it1);
+    skinny_compute(b1, lutf, lut, acc);
   }
 }
 
-template <int FMT, bool GATEUP, int U>
+// Skinny grouped GEMM: one workgroup = one expert x 32 weight rows (gate_up:
+// 16 (gate, up) pairs; down: 32 output columns); its S waves split K and are
+// reduced through LDS; the expert's rows are taken 32 at a time.
+template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(512) void k_skinny(const GemmArgs a) {
   using F = Format<FMT>;
   constexpr bool PRESCALE = FMT == MOE4_FMT_NF4;
   constexpr int MAXR = 2;
-  // dynamic LDS: the byte table replicated kLutCopies times (entry-major, so
-  // lanes reading random entries hit distinct banks), then the reduction buffer
-  extern __shared__ __attribute__((aligned(16))) float dyn[];
-  float2* lutf_all = reinterpret_cast<float2*>(dyn);
-  uint32_t* lut_all = reinterpret_cast<uint32_t*>(dyn);
-  float* red = dyn + (PRESCALE ? 2 : 1) * 256 * kLutCopies;
+  constexpr int KB = F::kBlock;
+  // byte -> two levels: fp32 pair (NF4, scaled afterwards) or bf16 pair (MXFP4)
+  __shared__ __attribute__((aligned(16))) float2 lutf[PRESCALE ? 256 : 1];
+  __shared__ uint32_t lut[PRESCALE ? 1 : 256];
+  extern __shared__ __attribute__((aligned(16))) float red[];   // [S][MAXR][2][256]
   const int S = blockDim.x >> 6, w = wave_id(), l = lane_id();
-  for (int i = threadIdx.x; i < 256 * kLutCopies; i += blockDim.x) {
-    const int byte = i / kLutCopies;
-    if (PRESCALE) lutf_all[i] = make_float2(F::level(byte & 15), F::level(byte >> 4));
-    else lut_all[i] = lut_bf16x2<FMT>(byte);
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+    if (PRESCALE) lutf[i] = make_float2(F::level(i & 15), F::level(i >> 4));
+    else lut[i] = lut_bf16x2<FMT>(i);
   }
-  const float2* lutf = lutf_all + (l & (kLutCopies - 1));
-  const uint32_t* lut = lut_all + (l & (kLutCopies - 1));
   const int item = blockIdx.x / a.ncg, cg = blockIdx.x - item * a.ncg;
   int e, unused;
   locate_item(a.offsets, a.E, item, [](int n) { return n > 0 ? 1 : 0; }, e, unused);
+  e = __builtin_amdgcn_readfirstlane(e);
   __syncthreads();
   if (e < 0) return;
+  const int K = a.K;
   const int rbeg = min(a.offsets[e], a.rows);
   const int n_e = min(a.offsets[e + 1], a.rows) - rbeg;
-  const int nl = l & 15;
+  const int nl = l & 15, g = l >> 4;
   const int Nw = GATEUP ? 2 * a.I : a.N_out;
-  int wrow[2];
+  SkinnyLane sl;
   if (GATEUP) {
     const int j = cg * 16 + nl;
-    wrow[0] = gate_row(a.layout, a.I, j);
-    wrow[1] = up_row(a.layout, a.I, j);
+    sl.srow[0] = gate_row(a.layout, a.I, j);
+    sl.srow[1] = up_row(a.layout, a.I, j);
   } else {
-    wrow[0] = cg * 32 + nl;
-    wrow[1] = cg * 32 + 16 + nl;
+    sl.srow[0] = cg * 32 + nl;
+    sl.srow[1] = cg * 32 + 16 + nl;
   }
-  const int64_t growbase = (int64_t)e * Nw;
-  const uint8_t* q0 = a.wq + (growbase + wrow[0]) * (int64_t)(a.K / 2);
-  const uint8_t* q1 = a.wq + (growbase + wrow[1]) * (int64_t)(a.K / 2);
-  const int nit = (a.K + 127) / 128;
+  sl.rq = make_rsrc(a.wq + (int64_t)e * Nw * (K / 2), (uint32_t)Nw * (K / 2));
+  const int sbytes = PRESCALE ? 4 : 1;
+  sl.rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Nw * (K / KB) * sbytes,
+                    (uint32_t)Nw * (K / KB) * sbytes);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) sl.qoff[c] = sl.srow[c] * (K / 2) + 16 * g;
+  const int nit = (K + 127) / 128;
   const int it0 = (int)((int64_t)w * nit / S), it1 = (int)((int64_t)(w + 1) * nit / S);
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -242,13 +221,9 @@ __global__ __launch_bounds__(512) void k_skinny(const GemmArgs a) {
     const int nrows = min(16 * MAXR, n_e - rc);
     const int nrt = (nrows + 15) >> 4;
     f32x4 acc[2][2] = {{zero4, zero4}, {zero4, zero4}};
-    const uint16_t* arow0 = a.A + (int64_t)(rbeg + rc) * a.K;
-    if (nrt == 1)
-      skinny_kloop<FMT, 1, U>(a, q0, q1, growbase + wrow[0], growbase + wrow[1], arow0, nrows,
-                              it0, it1, lutf, lut, acc);
-    else
-      skinny_kloop<FMT, 2, U>(a, q0, q1, growbase + wrow[0], growbase + wrow[1], arow0, nrows,
-                              it0, it1, lutf, lut, acc);
+    sl.ra = make_rsrc(a.A + (int64_t)(rbeg + rc) * K, (uint32_t)nrows * K * 2);
+    if (nrt == 1) skinny_kloop<FMT, 1>(sl, K, it0, it1, lutf, lut, acc);
+    else skinny_kloop<FMT, 2>(sl, K, it0, it1, lutf, lut, acc);
     // reduce the S partial sums through LDS: red[w][rt][c][lane*4 + i]
 #pragma unroll
     for (int rt = 0; rt < MAXR; ++rt)
@@ -289,15 +264,8 @@ __global__ __launch_bounds__(512) void k_skinny(const GemmArgs a) {
 
 constexpr int kBM = 128, kBK = 64, kLDA = kBK + 8;
 
-// Per-wave state of the tiled kernel's K loop.
-struct TiledLane {
-  const uint8_t* q[2];   // this lane's 16-byte column of each weight row, at k = 32h
-  int64_t srow[2];       // scale rows
-  bool tact[2];          // weight tile inside the stack
-};
-
-// One k-tile of the tiled kernel: dequantise this lane's weight nibbles (scale
-// folded in) and run the MFMAs against the A tile in LDS buffer `buf`.
+// One k-tile of the tiled kernel: dequantise this lane's 32 weight bytes (two
+// weight rows x 32 k, scale folded in) and run the MFMAs against the A tile.
 template <int FMT>
 __device__ __forceinline__ void tiled_step(const uint16_t* As, const float2* lutf,
                                            const u32x4 (&braw)[2], const float (&bsc)[2],
@@ -310,7 +278,7 @@ __device__ __forceinline__ void tiled_step(const uint16_t* As, const float2* lut
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
-        const float2 v = lutf[((braw[c][s] >> (8 * bi)) & 255u) * kLutCopies];
+        const float2 v = lutf[(braw[c][s] >> (8 * bi)) & 255u];
         bq[c][s][bi] = pack_bf16x2(v.x * bsc[c], v.y * bsc[c]);
       }
 #pragma unroll
@@ -330,125 +298,95 @@ __device__ __forceinline__ void tiled_step(const uint16_t* As, const float2* lut
   }
 }
 
-// K loop for NRT 32-row tiles (NRT = ceil(rows / 32) of this tile). The A tile
-// (activations) is double-buffered in LDS; both the A tile and each lane's
-// weight nibbles are fetched two k-tiles ahead (two register sets, loop
-// unrolled by two), so an HBM round trip overlaps two k-tiles of MFMA work.
-template <int FMT>
-__device__ __forceinline__ void tiled_kloop(const GemmArgs& a, const TiledLane& tl,
-                                            uint16_t (*As)[kBM * kLDA], const float2* lutf,
-                                            int row0, int nrows, f32x16 (&acc)[4][2]) {
-  const int nrt = (nrows + 31) >> 5;
+// Tiled grouped GEMM: one workgroup = one 128-row tile of one expert's
+// permuted rows x 128 output columns (gate_up: 128 (gate, up) pairs, i.e. 256
+// weight rows; down: 256 output columns). The A tile goes through LDS
+// (double-buffered, one k-tile of 64 ahead); each wave owns 64 weight rows and
+// fetches its lanes' nibbles and scales straight into registers one k-tile
+// ahead. All loads are raw buffer loads: rows past the tile, k past K and
+// weight rows past the stack read as zero.
+template <int FMT, bool GATEUP>
+__global__ __launch_bounds__(256, 2) void k_tiled(const GemmArgs a) {
   using F = Format<FMT>;
   constexpr int KB = F::kBlock;
-  const int tid = threadIdx.x, l = lane_id();
-  const int h = l >> 5;
-  const int K = a.K;
-  const int nk = (K + kBK - 1) / kBK;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-  auto loadA = [&](u32x4 (&r)[4], int kt) {
-    const int kb = kt * kBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i, rr = id >> 3, cidx = (id & 7) * 8;
-      r[i] = (kt < nk && rr < nrows && kb + cidx < K)
-                 ? *reinterpret_cast<const u32x4*>(a.A + (int64_t)(row0 + rr) * K + kb + cidx)
-                 : z4;
-    }
-  };
-  auto storeA = [&](const u32x4 (&r)[4], int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i, rr = id >> 3, cidx = (id & 7) * 8;
-      *reinterpret_cast<u32x4*>(&As[buf][rr * kLDA + cidx]) = r[i];
-    }
-  };
-  auto loadB = [&](u32x4 (&br)[2], float (&bs)[2], int kt) {
-    const int kb = kt * kBK;
-    const bool inK = kt < nk && kb + 32 * h < K;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bool on = tl.tact[c] && inK;
-      br[c] = on ? *reinterpret_cast<const u32x4*>(tl.q[c] + kb / 2) : z4;
-      bs[c] = on ? F::scale(a.ws, tl.srow[c], K, (kb + 32 * h) / KB) : 0.0f;
-    }
-  };
-
-  u32x4 r0[4], r1[4], b0[2], b1[2];
-  float s0[2], s1[2];
-  loadA(r0, 0);
-  loadB(b0, s0, 0);
-  loadA(r1, 1);
-  loadB(b1, s1, 1);
-  storeA(r0, 0);
-  __syncthreads();
-  for (int it = 0; it < nk; it += 2) {
-    // k-tile `it` (LDS buffer 0, weights b0); fetch k-tile it+2 into r0/b0
-    {
-      const u32x4 bc[2] = {b0[0], b0[1]};
-      const float sc[2] = {s0[0], s0[1]};
-      loadA(r0, it + 2);
-      loadB(b0, s0, it + 2);
-      tiled_step<FMT>(As[0], lutf, bc, sc, nrt, acc);
-      if (it + 1 < nk) storeA(r1, 1);
-      __syncthreads();
-    }
-    if (it + 1 >= nk) break;
-    // k-tile `it+1` (LDS buffer 1, weights b1); fetch k-tile it+3 into r1/b1
-    {
-      const u32x4 bc[2] = {b1[0], b1[1]};
-      const float sc[2] = {s1[0], s1[1]};
-      loadA(r1, it + 3);
-      loadB(b1, s1, it + 3);
-      tiled_step<FMT>(As[1], lutf, bc, sc, nrt, acc);
-      if (it + 2 < nk) storeA(r0, 0);
-      __syncthreads();
-    }
-  }
-}
-
-template <int FMT, bool GATEUP>
-__global__ __launch_bounds__(256) void k_tiled(const GemmArgs a) {
-  using F = Format<FMT>;
+  __shared__ __attribute__((aligned(16))) float2 lutf[256];
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLDA];
-  extern __shared__ __attribute__((aligned(16))) float2 lutf_all[];   // [256][kLutCopies]
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  for (int i = tid; i < 256 * kLutCopies; i += 256) {
-    const int byte = i / kLutCopies;
-    lutf_all[i] = make_float2(F::level(byte & 15), F::level(byte >> 4));
-  }
-  const float2* lutf = lutf_all + (l & (kLutCopies - 1));
+  lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int q = logical / a.ncg, cg = logical - q * a.ncg;
   int e, ut;
   locate_item(a.offsets, a.E, q, [](int n) { return (n + kBM - 1) / kBM; }, e, ut);
+  // wave-uniform by construction; make it visible to the compiler so that the
+  // buffer resources below live in scalar registers
+  e = __builtin_amdgcn_readfirstlane(e);
+  ut = __builtin_amdgcn_readfirstlane(ut);
   __syncthreads();
   if (e < 0) return;
+  const int K = a.K;
   const int row0 = min(a.offsets[e], a.rows) + ut * kBM;
   const int nrows = min(kBM, min(a.offsets[e + 1], a.rows) - row0);
+  const int nrt = (nrows + 31) >> 5;
   const int n32 = l & 31, h = l >> 5;
   const int Nw = GATEUP ? 2 * a.I : a.N_out;
   int wrow[2];
-  TiledLane tl;
+  bool tact[2];
   if (GATEUP) {
     const int jb = cg * 128 + w * 32;
-    tl.tact[0] = tl.tact[1] = jb < a.I;
-    const int j = tl.tact[0] ? jb + n32 : 0;
+    tact[0] = tact[1] = jb < a.I;
+    const int j = tact[0] ? jb + n32 : 0;
     wrow[0] = gate_row(a.layout, a.I, j);
     wrow[1] = up_row(a.layout, a.I, j);
   } else {
     const int c0 = cg * 256 + w * 64;
-    tl.tact[0] = c0 < a.N_out;
-    tl.tact[1] = c0 + 32 < a.N_out;
-    wrow[0] = tl.tact[0] ? c0 + n32 : 0;
-    wrow[1] = tl.tact[1] ? c0 + 32 + n32 : 0;
+    tact[0] = c0 < a.N_out;
+    tact[1] = c0 + 32 < a.N_out;
+    wrow[0] = tact[0] ? c0 + n32 : 0;
+    wrow[1] = tact[1] ? c0 + 32 + n32 : 0;
   }
-  const int64_t growbase = (int64_t)e * Nw;
+  // buffer resources: this tile's activations, this expert's nibbles and scales
+  const rsrc_t ra = make_rsrc(a.A + (int64_t)row0 * K, (uint32_t)nrows * K * 2);
+  const rsrc_t rq = make_rsrc(a.wq + (int64_t)e * Nw * (K / 2), (uint32_t)Nw * (K / 2));
+  const int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
+  const rsrc_t rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Nw * (K / KB) * sbytes,
+                              (uint32_t)Nw * (K / KB) * sbytes);
+  int aoff[4], acol[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + 256 * i;
+    acol[i] = (id & 7) * 8;
+    aoff[i] = ((id >> 3) * K + acol[i]) * 2;
+  }
+  int qoff[2], soff[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    tl.srow[c] = growbase + wrow[c];
-    tl.q[c] = a.wq + tl.srow[c] * (int64_t)(a.K / 2) + 16 * h;
+    qoff[c] = wrow[c] * (K / 2) + 16 * h;
+    soff[c] = (wrow[c] * (K / KB)) * sbytes;
   }
+  const int nk = (K + kBK - 1) / kBK;
+  auto loadA = [&](u32x4 (&r)[4], int kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = buf_load_b128(ra, kb + acol[i] < K ? aoff[i] + 2 * kb : kOob);
+  };
+  auto storeA = [&](const u32x4 (&r)[4], int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(&As[buf][(id >> 3) * kLDA + acol[i]]) = r[i];
+    }
+  };
+  auto loadB = [&](u32x4 (&br)[2], float (&bs)[2], int kb) {
+    const bool ink = kb + 32 * h < K;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool on = ink && tact[c];
+      br[c] = buf_load_b128(rq, on ? qoff[c] + kb / 2 : kOob);
+      const int so = on ? soff[c] + ((kb + 32 * h) / KB) * sbytes : kOob;
+      if (FMT == MOE4_FMT_NF4) bs[c] = __uint_as_float(buf_load_b32(rs, so));
+      else bs[c] = Format<MOE4_FMT_MXFP4>::e8m0(buf_load_u8(rs, so));
+    }
+  };
+
   f32x16 acc[4][2];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -456,7 +394,28 @@ __global__ __launch_bounds__(256) void k_tiled(const GemmArgs a) {
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[rt][c][i] = 0.0f;
-  tiled_kloop<FMT>(a, tl, As, lutf, row0, nrows, acc);
+
+  u32x4 ra_regs[4], bcur[2], bnext[2];
+  float scur[2], snext[2];
+  loadA(ra_regs, 0);
+  loadB(bcur, scur, 0);
+  storeA(ra_regs, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) {
+      loadA(ra_regs, (kt + 1) * kBK);
+      loadB(bnext, snext, (kt + 1) * kBK);
+    }
+    tiled_step<FMT>(As[kt & 1], lutf, bcur, scur, nrt, acc);
+    if (more) storeA(ra_regs, (kt + 1) & 1);
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bcur[c] = bnext[c];
+      scur[c] = snext[c];
+    }
+  }
 
   // epilogue: lane holds column n32 of each 32x32 tile, rows 8*(i/4) + 4*h + i%4
 #pragma unroll
@@ -467,11 +426,11 @@ __global__ __launch_bounds__(256) void k_tiled(const GemmArgs a) {
       if (rt_row < nrows) {
         const int row = row0 + rt_row;
         if (GATEUP) {
-          if (tl.tact[0])
+          if (tact[0])
             gate_up_epilogue(a, e, row, cg * 128 + w * 32 + n32, acc[rt][0][i], acc[rt][1][i]);
         } else {
-          if (tl.tact[0]) down_epilogue(a, e, row, wrow[0], acc[rt][0][i]);
-          if (tl.tact[1]) down_epilogue(a, e, row, wrow[1], acc[rt][1][i]);
+          if (tact[0]) down_epilogue(a, e, row, wrow[0], acc[rt][0][i]);
+          if (tact[1]) down_epilogue(a, e, row, wrow[1], acc[rt][1][i]);
         }
       }
     }
@@ -512,13 +471,12 @@ hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
   int S = (6144 + nwg - 1) / nwg;
   S = max(1, min(S, min(8, nit / 2)));
   constexpr int MAXR = 2;
-  const size_t lut_bytes = (FMT == MOE4_FMT_NF4 ? 8 : 4) * 256 * kLutCopies;
-  const size_t lds = lut_bytes + (size_t)S * MAXR * 2 * 256 * sizeof(float);
+  const size_t lds = (size_t)S * MAXR * 2 * 256 * sizeof(float);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_skinny<FMT, GATEUP, 1>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(lut_bytes + 8 * MAXR * 2 * 256 * 4));
+      reinterpret_cast<const void*>(&k_skinny<FMT, GATEUP>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(8 * MAXR * 2 * 256 * sizeof(float)));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_skinny<FMT, GATEUP, 1>), dim3(nwg), dim3(64 * S), lds, s, a);
+  hipLaunchKernelGGL((k_skinny<FMT, GATEUP>), dim3(nwg), dim3(64 * S), lds, s, a);
   return hipGetLastError();
 }
 
@@ -526,12 +484,7 @@ template <int FMT, bool GATEUP>
 hipError_t run_tiled(const GemmArgs& a, int ntiles, hipStream_t s) {
   const int nwg = ntiles * a.ncg;
   if (nwg == 0) return hipSuccess;
-  constexpr size_t lds = (size_t)256 * kLutCopies * sizeof(float2);
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tiled<FMT, GATEUP>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_tiled<FMT, GATEUP>), dim3(nwg), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((k_tiled<FMT, GATEUP>), dim3(nwg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -72,6 +72,10 @@ int check_experts(const moe4_experts* ex) {
   if ((int64_t)ex->E * 2 * ex->I * ex->H > ((int64_t)1 << 40))
     return fail(MOE4_ESHAPE, "moe4_experts: stack of %lld weights is beyond the supported 2^40",
                 (long long)ex->E * 2 * ex->I * ex->H);
+  // the GEMM kernels address one expert's matrix with 32-bit byte offsets
+  if ((int64_t)ex->I * ex->H >= ((int64_t)1 << 31) - ((int64_t)1 << 24))
+    return fail(MOE4_ESHAPE, "moe4_experts: I*H = %lld; one expert's packed matrix must stay "
+                "under 2 GiB", (long long)ex->I * ex->H);
   REQUIRE_PTR(ex->gu_q, "moe4_experts.gu_q");
   REQUIRE_PTR(ex->gu_s, "moe4_experts.gu_s");
   REQUIRE_PTR(ex->dn_q, "moe4_experts.dn_q");

@@ -97,6 +97,9 @@ enum { MOE4_VARIANT_AUTO = 0, MOE4_VARIANT_SKINNY = 1, MOE4_VARIANT_TILED = 2 };
  *   gu += lora_scale * (x A_e^T) B_e^T before the activation; 1 <= r <= 64.
  * variant: MOE4_VARIANT_*; AUTO unless a test needs one kernel family.
  * All stack pointers are device pointers; gu_q/dn_q 16-byte aligned.
+ * Bounds (else MOE4_ESHAPE): 1 <= E <= 1024; H and I positive multiples of
+ * the block (64 NF4, 32 MXFP4); E*2I*H <= 2^40; I*H < 2^31 - 2^24 (one
+ * expert's packed matrix is addressed with 32-bit byte offsets).
  */
 typedef struct moe4_experts {
   int32_t format;

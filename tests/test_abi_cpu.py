@@ -86,6 +86,7 @@ def test_permute_refusals():
     ("E", 1025, moe4.MOE4_ESHAPE, "E = 1025"),
     ("H", 96, moe4.MOE4_ESHAPE, "not a multiple of 64"),
     ("I", 32, moe4.MOE4_ESHAPE, "not a multiple of 64"),
+    ("I", 1 << 23, moe4.MOE4_ESHAPE, "under 2 GiB"),
     ("gu_q", None, moe4.MOE4_EINVAL, "gu_q is NULL"),
     ("dn_q", FAKE + 8, moe4.MOE4_EALIGN, "dn_q is not 16-byte aligned"),
     ("lora_A", FAKE, moe4.MOE4_EINVAL, "given together"),
