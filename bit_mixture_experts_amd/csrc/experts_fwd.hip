@@ -22,6 +22,8 @@
 //    activations is staged in LDS (double-buffered); each wave owns 64 weight
 //    rows, loads their nibbles straight into registers with 128-bit loads,
 //    dequantises with the scale folded in, and runs 32x32x16 bf16 MFMA.
+#include <type_traits>
+
 #include "common.hpp"
 #include "formats.hpp"
 #include "internal.hpp"
@@ -30,29 +32,45 @@
 namespace moe4 {
 namespace {
 
-// ------------------------------------------------------------ skinny kernel
+// ------------------------------------------------------------ dequantisation
 
-// 4x4 transpose of dwords across the four 16-lane rows of a wave: on entry
-// row g holds D[g][0..3] in v[0..3]; on exit row g holds D[0..3][g].
-// permlane32_swap exchanges the upper half of its first operand with the
-// lower half of its second; permlane16_swap exchanges the odd 16-lane rows of
-// its first operand with the even rows of its second.
-__device__ __forceinline__ void transpose4x4_rows(u32x4& v) {
-  auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
-  auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
-  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  v[0] = c[0];
-  v[1] = c[1];
-  v[2] = d[0];
-  v[3] = d[1];
+// bf16 operands of 8 weights (one dword of nibbles, even element in the low
+// nibble). NF4: fp32 levels of each byte from the LDS table, the absmax
+// applied in fp32 and the product rounded once to bf16. MXFP4: the hardware
+// e2m1 -> bf16 conversion scaled by the block's power of two (exact; the scale
+// operand is the e8m0 byte placed in an fp32 exponent field).
+template <int FMT>
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, float sc, const float2* lutf) {
+  u32x4 r;
+  if constexpr (FMT == MOE4_FMT_NF4) {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      const float2 v = lutf[(w >> (8 * bi)) & 255u];
+      r[bi] = pack_bf16x2(v.x * sc, v.y * sc);
+    }
+  } else {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+  }
+  return r;
 }
 
+// scale operand of dequant8 from a raw scale word: NF4 fp32 absmax bits, or an
+// e8m0 byte
+template <int FMT>
+__device__ __forceinline__ float scale_operand(uint32_t raw) {
+  return FMT == MOE4_FMT_NF4 ? __uint_as_float(raw) : __uint_as_float((raw & 255u) << 23);
+}
+
+// ------------------------------------------------------------ skinny kernel
+
 // Per-wave operands of one 128-k iteration of the skinny kernel.
-template <int FMT, int NRT>
+template <int NRT>
 struct SkinnyBatch {
   u32x4 wraw[2];
-  float sc[2][FMT == MOE4_FMT_NF4 ? 1 : 4];
+  uint32_t sraw[2];
   u32x4 av[NRT][4];
 };
 
@@ -65,17 +83,13 @@ struct SkinnyLane {
 
 // Each k-iteration covers 128 k: lane (n = l%16, g = l/16) loads 16 bytes
 // (32 k) of its weight row with one 128-bit load, so the four lanes of a row
-// read 64 contiguous bytes.
-//  NF4: lane g's 32 k lie in one absmax block; each weight becomes
-//       bf16(level * absmax) and MFMA step s uses k = kb + 32g + 8s.
-//  MXFP4: the 4x4 transpose above makes MFMA step s cover exactly the 32-k
-//       block kb/32 + s (k = kb + 32s + 8g), so the block's power-of-two
-//       scale multiplies the fp32 partial sum of that step.
+// read 64 contiguous bytes. Lane g's 32 k lie in one scale block (64 for NF4,
+// 32 for MXFP4); MFMA step s uses k = kb + 32g + 8s.
 template <int FMT, int NRT>
-__device__ __forceinline__ void skinny_load(SkinnyBatch<FMT, NRT>& bt, const SkinnyLane& sl,
-                                            int K, int it, int it1) {
-  using F = Format<FMT>;
-  constexpr bool PRESCALE = FMT == MOE4_FMT_NF4;
+__device__ __forceinline__ void skinny_load(SkinnyBatch<NRT>& bt, const SkinnyLane& sl, int K,
+                                            int it, int it1) {
+  constexpr int KB = Format<FMT>::kBlock;
+  constexpr int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
   const int l = lane_id(), nl = l & 15, g = l >> 4;
   const int kb = it * 128;
   const bool live = it < it1;
@@ -83,71 +97,36 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<FMT, NRT>& bt, const Ski
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     bt.wraw[c] = buf_load_b128(sl.rq, ink ? sl.qoff[c] + kb / 2 : kOob);
-    if (PRESCALE) {
-      const int so = ink ? (sl.srow[c] * (K / 64) + (kb + 32 * g) / 64) * 4 : kOob;
-      bt.sc[c][0] = __uint_as_float(buf_load_b32(sl.rs, so));
-    } else {
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bool inb = live && kb + 32 * st < K;
-        bt.sc[c][st] = Format<MOE4_FMT_MXFP4>::e8m0(
-            buf_load_u8(sl.rs, inb ? sl.srow[c] * (K / 32) + kb / 32 + st : kOob));
-      }
-    }
+    const int so = ink ? (sl.srow[c] * (K / KB) + (kb + 32 * g) / KB) * sbytes : kOob;
+    bt.sraw[c] = sbytes == 4 ? buf_load_b32(sl.rs, so) : buf_load_u8(sl.rs, so);
   }
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int m = rt * 16 + nl;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const int k = PRESCALE ? kb + 32 * g + 8 * st : kb + 32 * st + 8 * g;
+      const int k = kb + 32 * g + 8 * st;
       bt.av[rt][st] = buf_load_b128(sl.ra, (live && k < K) ? (m * K + k) * 2 : kOob);
     }
   }
 }
 
 template <int FMT, int NRT>
-__device__ __forceinline__ void skinny_compute(const SkinnyBatch<FMT, NRT>& bt,
-                                               const float2* lutf, const uint32_t* lut,
+__device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const float2* lutf,
                                                f32x4 (&acc)[2][2]) {
-  constexpr bool PRESCALE = FMT == MOE4_FMT_NF4;
-  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    if (PRESCALE) {
-      // 32 nibbles -> 32 bf16 operands bf16(level * absmax)
-      u32x4 bq[4];
+    const float sc = scale_operand<FMT>(bt.sraw[c]);
+    u32x4 bq[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) bq[st] = dequant8<FMT>(bt.wraw[c][st], sc, lutf);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi) {
-          const float2 f = lutf[(bt.wraw[c][st] >> (8 * bi)) & 255u];
-          bq[st][bi] = pack_bf16x2(f.x * bt.sc[c][0], f.y * bt.sc[c][0]);
-        }
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-          acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, bt.av[rt][st]), __builtin_bit_cast(bf16x8, bq[st]),
-              acc[rt][c], 0, 0, 0);
-    } else {
-      u32x4 v = bt.wraw[c];
-      transpose4x4_rows(v);
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        u32x4 t;
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi) t[bi] = lut[(v[st] >> (8 * bi)) & 255u];
-        const bf16x8 bq = __builtin_bit_cast(bf16x8, t);
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-          const f32x4 p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, bt.av[rt][st]), bq, zero4, 0, 0, 0);
-          acc[rt][c] += bt.sc[c][st] * p;
-        }
-      }
-    }
+        acc[rt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, bt.av[rt][st]), __builtin_bit_cast(bf16x8, bq[st]),
+            acc[rt][c], 0, 0, 0);
   }
 }
 
@@ -156,16 +135,15 @@ __device__ __forceinline__ void skinny_compute(const SkinnyBatch<FMT, NRT>& bt,
 // and multiplied.
 template <int FMT, int NRT>
 __device__ __forceinline__ void skinny_kloop(const SkinnyLane& sl, int K, int it0, int it1,
-                                             const float2* lutf, const uint32_t* lut,
-                                             f32x4 (&acc)[2][2]) {
-  SkinnyBatch<FMT, NRT> b0, b1;
-  skinny_load(b0, sl, K, it0, it1);
+                                             const float2* lutf, f32x4 (&acc)[2][2]) {
+  SkinnyBatch<NRT> b0, b1;
+  skinny_load<FMT>(b0, sl, K, it0, it1);
   for (int it = it0; it < it1; it += 2) {
-    if (it + 1 < it1) skinny_load(b1, sl, K, it + 1, it1);
-    skinny_compute(b0, lutf, lut, acc);
+    if (it + 1 < it1) skinny_load<FMT>(b1, sl, K, it + 1, it1);
+    skinny_compute<FMT>(b0, lutf, acc);
     if (it + 1 >= it1) break;
-    if (it + 2 < it1) skinny_load(b0, sl, K, it + 2, it1);
-    skinny_compute(b1, lutf, lut, acc);
+    if (it + 2 < it1) skinny_load<FMT>(b0, sl, K, it + 2, it1);
+    skinny_compute<FMT>(b1, lutf, acc);
   }
 }
 
@@ -175,18 +153,16 @@ __device__ __forceinline__ void skinny_kloop(const SkinnyLane& sl, int K, int it
 template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(512) void k_skinny(const GemmArgs a) {
   using F = Format<FMT>;
-  constexpr bool PRESCALE = FMT == MOE4_FMT_NF4;
+  constexpr bool NF4 = FMT == MOE4_FMT_NF4;
   constexpr int MAXR = 2;
   constexpr int KB = F::kBlock;
-  // byte -> two levels: fp32 pair (NF4, scaled afterwards) or bf16 pair (MXFP4)
-  __shared__ __attribute__((aligned(16))) float2 lutf[PRESCALE ? 256 : 1];
-  __shared__ uint32_t lut[PRESCALE ? 1 : 256];
+  // NF4 byte -> two fp32 levels
+  __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
   extern __shared__ __attribute__((aligned(16))) float red[];   // [S][MAXR][2][256]
   const int S = blockDim.x >> 6, w = wave_id(), l = lane_id();
-  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-    if (PRESCALE) lutf[i] = make_float2(F::level(i & 15), F::level(i >> 4));
-    else lut[i] = lut_bf16x2<FMT>(i);
-  }
+  if (NF4)
+    for (int i = threadIdx.x; i < 256; i += blockDim.x)
+      lutf[i] = make_float2(F::level(i & 15), F::level(i >> 4));
   const int item = blockIdx.x / a.ncg, cg = blockIdx.x - item * a.ncg;
   int e, unused;
   locate_item(a.offsets, a.E, item, [](int n) { return n > 0 ? 1 : 0; }, e, unused);
@@ -208,7 +184,7 @@ __global__ __launch_bounds__(512) void k_skinny(const GemmArgs a) {
     sl.srow[1] = cg * 32 + 16 + nl;
   }
   sl.rq = make_rsrc(a.wq + (int64_t)e * Nw * (K / 2), (uint32_t)Nw * (K / 2));
-  const int sbytes = PRESCALE ? 4 : 1;
+  constexpr int sbytes = NF4 ? 4 : 1;
   sl.rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Nw * (K / KB) * sbytes,
                     (uint32_t)Nw * (K / KB) * sbytes);
 #pragma unroll
@@ -222,8 +198,8 @@ __global__ __launch_bounds__(512) void k_skinny(const GemmArgs a) {
     const int nrt = (nrows + 15) >> 4;
     f32x4 acc[2][2] = {{zero4, zero4}, {zero4, zero4}};
     sl.ra = make_rsrc(a.A + (int64_t)(rbeg + rc) * K, (uint32_t)nrows * K * 2);
-    if (nrt == 1) skinny_kloop<FMT, 1>(sl, K, it0, it1, lutf, lut, acc);
-    else skinny_kloop<FMT, 2>(sl, K, it0, it1, lutf, lut, acc);
+    if (nrt == 1) skinny_kloop<FMT, 1>(sl, K, it0, it1, lutf, acc);
+    else skinny_kloop<FMT, 2>(sl, K, it0, it1, lutf, acc);
     // reduce the S partial sums through LDS: red[w][rt][c][lane*4 + i]
 #pragma unroll
     for (int rt = 0; rt < MAXR; ++rt)
@@ -262,57 +238,51 @@ __global__ __launch_bounds__(512) void k_skinny(const GemmArgs a) {
 
 // ------------------------------------------------------------- tiled kernel
 
-constexpr int kBM = 128, kBK = 64, kLDA = kBK + 8;
+constexpr int kBM = 128, kBK = 64, kStages = 3;
+// One LDS stage holds a k-tile of 64: the A tile [128 rows][128 B] with the
+// 16-byte chunks of row r stored at chunk ^ (r & 7) (conflict-free MFMA
+// operand reads), each wave's packed nibbles [c][32 rows][32 B], and each
+// wave's scales (NF4: [c][32] fp32; MXFP4: [h][c][32] e8m0 bytes, each in
+// the low byte of a 4-byte slot: sub-dword loads to LDS advance 4 bytes a lane).
+constexpr int kStageA = kBM * kBK * 2;
+constexpr int kStageB = 4 * 2 * 32 * 32;
+constexpr int kStageS = 4 * 512;
+constexpr int kStageBytes = kStageA + kStageB + kStageS;
+constexpr int kTiledLds = kStages * kStageBytes;
 
-// One k-tile of the tiled kernel: dequantise this lane's 32 weight bytes (two
-// weight rows x 32 k, scale folded in) and run the MFMAs against the A tile.
-template <int FMT>
-__device__ __forceinline__ void tiled_step(const uint16_t* As, const float2* lutf,
-                                           const u32x4 (&braw)[2], const float (&bsc)[2],
-                                           int nrt, f32x16 (&acc)[4][2]) {
-  const int l = lane_id(), n32 = l & 31, h = l >> 5;
-  u32x4 bq[2][4];
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        const float2 v = lutf[(braw[c][s] >> (8 * bi)) & 255u];
-        bq[c][s][bi] = pack_bf16x2(v.x * bsc[c], v.y * bsc[c]);
-      }
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    if (rt < nrt) {   // uniform: row tiles past the tile's rows are skipped
-      bf16x8 af[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        af[s] = *reinterpret_cast<const bf16x8*>(&As[(rt * 32 + n32) * kLDA + 32 * h + 8 * s]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc[rt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              af[s], __builtin_bit_cast(bf16x8, bq[c][s]), acc[rt][c], 0, 0, 0);
-    }
-  }
+#define MOE4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// wait until at most N vector-memory loads of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding LDS-DMA load); compiler-level ordering only
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Tiled grouped GEMM: one workgroup = one 128-row tile of one expert's
 // permuted rows x 128 output columns (gate_up: 128 (gate, up) pairs, i.e. 256
-// weight rows; down: 256 output columns). The A tile goes through LDS
-// (double-buffered, one k-tile of 64 ahead); each wave owns 64 weight rows and
-// fetches its lanes' nibbles and scales straight into registers one k-tile
-// ahead. All loads are raw buffer loads: rows past the tile, k past K and
-// weight rows past the stack read as zero.
+// weight rows; down: 256 output columns); wave w owns 64 weight rows (two
+// 32-column MFMA tiles) against all 128 rows. The activations, nibbles and
+// scales of k-tile kt+2 stream into LDS by buffer loads straight to LDS while
+// k-tile kt is multiplied (three stages, one barrier per k-tile); rows past
+// the tile, k past K and weight rows past the stack read as zeros.
 template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(256, 2) void k_tiled(const GemmArgs a) {
   using F = Format<FMT>;
+  constexpr bool NF4 = FMT == MOE4_FMT_NF4;
   constexpr int KB = F::kBlock;
-  __shared__ __attribute__((aligned(16))) float2 lutf[256];
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLDA];
+  constexpr int kLoadsPerTile = 4 + 2 + (NF4 ? 1 : 2);
+  __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
+  extern __shared__ __attribute__((aligned(16))) uint8_t stage_mem[];
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
+  if (NF4) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int q = logical / a.ncg, cg = logical - q * a.ncg;
   int e, ut;
@@ -329,6 +299,7 @@ __global__ __launch_bounds__(256, 2) void k_tiled(const GemmArgs a) {
   const int nrt = (nrows + 31) >> 5;
   const int n32 = l & 31, h = l >> 5;
   const int Nw = GATEUP ? 2 * a.I : a.N_out;
+  // weight rows of this wave's two column tiles, as seen by MFMA lane n32
   int wrow[2];
   bool tact[2];
   if (GATEUP) {
@@ -344,46 +315,64 @@ __global__ __launch_bounds__(256, 2) void k_tiled(const GemmArgs a) {
     wrow[0] = tact[0] ? c0 + n32 : 0;
     wrow[1] = tact[1] ? c0 + 32 + n32 : 0;
   }
-  // buffer resources: this tile's activations, this expert's nibbles and scales
   const rsrc_t ra = make_rsrc(a.A + (int64_t)row0 * K, (uint32_t)nrows * K * 2);
   const rsrc_t rq = make_rsrc(a.wq + (int64_t)e * Nw * (K / 2), (uint32_t)Nw * (K / 2));
-  const int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
+  constexpr int sbytes = NF4 ? 4 : 1;
   const rsrc_t rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Nw * (K / KB) * sbytes,
                               (uint32_t)Nw * (K / KB) * sbytes);
-  int aoff[4], acol[4];
+
+  // ---- loader roles (lane-contiguous LDS destinations)
+  // A: load i of lane (w, l) fills LDS bytes i*4096 + w*1024 + 16*l of the A
+  //    tile = row 32i + 8w + l/8, physical chunk l%8 = logical chunk ^ (row & 7)
+  int a_off[4], a_col[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int id = tid + 256 * i;
-    acol[i] = (id & 7) * 8;
-    aoff[i] = ((id >> 3) * K + acol[i]) * 2;
+    const int row = 32 * i + 8 * w + (l >> 3);
+    a_col[i] = 8 * ((l & 7) ^ (row & 7));
+    a_off[i] = (row * K + a_col[i]) * 2;
   }
-  int qoff[2], soff[2];
+  // B: load c of lane l fills [c][l/2][16*(l%2)] of this wave's nibble block
+  //    (weight row of column-tile lane n = l/2, bytes 16*(l%2) of the k-tile)
+  const int bn = l >> 1;
+  int b_off[2];
+  bool b_on[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    qoff[c] = wrow[c] * (K / 2) + 16 * h;
-    soff[c] = (wrow[c] * (K / KB)) * sbytes;
+    const int n = __shfl(wrow[c], bn, kWave);
+    b_on[c] = tact[c];
+    b_off[c] = n * (K / 2) + 16 * (l & 1);
   }
-  const int nk = (K + kBK - 1) / kBK;
-  auto loadA = [&](u32x4 (&r)[4], int kb) {
+  // scales: lane l covers column tile c = l/32, lane n = l%32
+  const int s_row0 = __shfl(wrow[0], l & 31, kWave), s_row1 = __shfl(wrow[1], l & 31, kWave);
+  const int s_row = (l >> 5) ? s_row1 : s_row0;
+  const bool s_on = tact[l >> 5];
+  const int s_off = s_row * (K / KB) * sbytes;
+
+  auto stage = [&](int st) { return stage_mem + st * kStageBytes; };
+  auto issue = [&](int kt) {
+    uint8_t* base = stage(kt % kStages);
+    const int kb = kt * kBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = buf_load_b128(ra, kb + acol[i] < K ? aoff[i] + 2 * kb : kOob);
-  };
-  auto storeA = [&](const u32x4 (&r)[4], int buf) {
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, MOE4_LDS(base + i * 4096 + w * 1024), 16,
+          kb + a_col[i] < K ? a_off[i] + 2 * kb : kOob, 0, 0, 0);
+    uint8_t* bbase = base + kStageA + w * 2048;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(&As[buf][(id >> 3) * kLDA + acol[i]]) = r[i];
-    }
-  };
-  auto loadB = [&](u32x4 (&br)[2], float (&bs)[2], int kb) {
-    const bool ink = kb + 32 * h < K;
+    for (int c = 0; c < 2; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, MOE4_LDS(bbase + c * 1024), 16,
+          (b_on[c] && kb + 32 * (l & 1) < K) ? b_off[c] + kb / 2 : kOob, 0, 0, 0);
+    uint8_t* sbase = base + kStageA + kStageB + w * 512;
+    if (NF4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE4_LDS(sbase), 4,
+                                               s_on ? s_off + (kb / 64) * 4 : kOob, 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bool on = ink && tact[c];
-      br[c] = buf_load_b128(rq, on ? qoff[c] + kb / 2 : kOob);
-      const int so = on ? soff[c] + ((kb + 32 * h) / KB) * sbytes : kOob;
-      if (FMT == MOE4_FMT_NF4) bs[c] = __uint_as_float(buf_load_b32(rs, so));
-      else bs[c] = Format<MOE4_FMT_MXFP4>::e8m0(buf_load_u8(rs, so));
+      for (int hh = 0; hh < 2; ++hh)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, MOE4_LDS(sbase + hh * 256), 1,
+            (s_on && kb + 32 * hh < K) ? s_off + kb / 32 + hh : kOob, 0, 0, 0);
     }
   };
 
@@ -395,26 +384,71 @@ __global__ __launch_bounds__(256, 2) void k_tiled(const GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[rt][c][i] = 0.0f;
 
-  u32x4 ra_regs[4], bcur[2], bnext[2];
-  float scur[2], snext[2];
-  loadA(ra_regs, 0);
-  loadB(bcur, scur, 0);
-  storeA(ra_regs, 0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      loadA(ra_regs, (kt + 1) * kBK);
-      loadB(bnext, snext, (kt + 1) * kBK);
-    }
-    tiled_step<FMT>(As[kt & 1], lutf, bcur, scur, nrt, acc);
-    if (more) storeA(ra_regs, (kt + 1) & 1);
-    __syncthreads();
+  // Per k-tile: wait for its loads, dequantise this wave's weights into
+  // registers, then start the loads of k-tile kt+2 and run the MFMAs. (The
+  // table reads of the dequantisation come before the new loads: the compiler
+  // makes LDS table reads wait for every load still streaming into LDS.) The
+  // loop is instantiated per count of live 32-row tiles so that its body is
+  // straight-line code.
+  const int nk = (K + kBK - 1) / kBK;
+  auto kloop = [&](auto nrt_c) {
+    constexpr int NRT = decltype(nrt_c)::value;
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) wait_vmcnt<kLoadsPerTile>();
+      else wait_vmcnt<0>();
+      lds_barrier();   // k-tile kt is in LDS everywhere; stage (kt+2)%3 is free
+      const uint8_t* base = stage(kt % kStages);
+      const uint16_t* As = reinterpret_cast<const uint16_t*>(base);
+      const uint8_t* Bw = base + kStageA + w * 2048;
+      const uint8_t* Sw = base + kStageA + kStageB + w * 512;
+      // A operands of MFMA step s for every live row tile (chunk 4h + s of
+      // row rt*32 + n32, stored at chunk ^ (row & 7))
+      auto load_af = [&](bf16x8 (&af)[NRT], int s) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bcur[c] = bnext[c];
-      scur[c] = snext[c];
+        for (int rt = 0; rt < NRT; ++rt) {
+          const int row = rt * 32 + n32;
+          af[rt] = *reinterpret_cast<const bf16x8*>(As + row * kBK + (((4 * h + s) ^ (row & 7)) * 8));
+        }
+      };
+      bf16x8 af0[NRT], af1[NRT];
+      load_af(af0, 0);
+      u32x4 bq[2][4];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 braw = *reinterpret_cast<const u32x4*>(Bw + c * 1024 + n32 * 32 + 16 * h);
+        const float sc = NF4 ? reinterpret_cast<const float*>(Sw)[c * 32 + n32]
+                             : __uint_as_float((uint32_t)Sw[h * 256 + (c * 32 + n32) * 4] << 23);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bq[c][s] = dequant8<FMT>(braw[s], sc, lutf);
+        // keep the two column tiles' table reads apart (register pressure)
+        if (NF4 && c == 0) __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kt + 2 < nk) issue(kt + 2);
+      auto mfmas = [&](const bf16x8 (&af)[NRT], int s) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            acc[rt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                af[rt], __builtin_bit_cast(bf16x8, bq[c][s]), acc[rt][c], 0, 0, 0);
+      };
+      // operands of step s+1 are read while step s multiplies
+      load_af(af1, 1);
+      mfmas(af0, 0);
+      load_af(af0, 2);
+      mfmas(af1, 1);
+      load_af(af1, 3);
+      mfmas(af0, 2);
+      mfmas(af1, 3);
     }
+  };
+  switch (nrt) {
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    default: kloop(std::integral_constant<int, 4>{}); break;
   }
 
   // epilogue: lane holds column n32 of each 32x32 tile, rows 8*(i/4) + 4*h + i%4
@@ -484,7 +518,11 @@ template <int FMT, bool GATEUP>
 hipError_t run_tiled(const GemmArgs& a, int ntiles, hipStream_t s) {
   const int nwg = ntiles * a.ncg;
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_tiled<FMT, GATEUP>), dim3(nwg), dim3(256), 0, s, a);
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tiled<FMT, GATEUP>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kTiledLds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((k_tiled<FMT, GATEUP>), dim3(nwg), dim3(256), kTiledLds, s, a);
   return hipGetLastError();
 }
 
