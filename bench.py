@@ -352,7 +352,13 @@ def cpu_baseline(spec, T_batch, n_tokens, seed=0):
                        f"dequantise + float64 matmul, combine; {dt:.1f} s")}
 
 
-def traffic_from_profile(kernel_tag):
+PMC_TAG = "gate_up_tiled_nf4_qwen3_T4096"
+HEADLINE_KERNEL = "k_tiled<1, true>"      # the gate_up grouped GEMM, NF4, tiled
+CALIB_BYTES = 256 << 20                    # the copy kernel reads and writes this much
+CALIB_KERNEL = "neg"                       # torch.neg on float32: one read, one write
+
+
+def traffic_from_profile(kernel_tag=PMC_TAG):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
     taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"pmc_{kernel_tag}.json")
@@ -363,6 +369,59 @@ def traffic_from_profile(kernel_tag):
     if rec.get("csrc_sha256") != csrc_digest():
         return None
     return rec.get("bytes_per_launch")
+
+
+def calibration_copy(torch):
+    """A plain copy of known size for scaling the FETCH_SIZE / WRITE_SIZE
+    counters: torch.neg over CALIB_BYTES of float32 reads and writes each byte
+    once."""
+    a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def pmc_summary(fetch_db, write_db, out_dir):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
+    `bench.py --no-sweep --no-cpu-baseline --calibrate` into the per-launch HBM
+    traffic of the headline kernel, scaled by the calibration copy."""
+    import sqlite3
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select name, dispatch_id, counter_value from pmc_events "
+                           "where counter_name = ?", (counter,)).fetchall()
+        con.close()
+        head = [v for n, _, v in rows if HEADLINE_KERNEL in n]
+        cal = [v for n, _, v in rows if CALIB_KERNEL in n and "moe4" not in n]
+        if not head or not cal:
+            raise SystemExit(f"{db}: no {counter} rows for the headline or calibration kernel")
+        return sum(head) / len(head), sum(cal) / len(cal), len(head), len(cal)
+
+    f_head, f_cal, nf, ncf = per_kernel(fetch_db, "FETCH_SIZE")
+    w_head, w_cal, nw, ncw = per_kernel(write_db, "WRITE_SIZE")
+    f_scale = CALIB_BYTES / (f_cal * 1024.0)
+    w_scale = CALIB_BYTES / (w_cal * 1024.0)
+    fetch_b = f_head * 1024.0 * f_scale
+    write_b = w_head * 1024.0 * w_scale
+    rec = {
+        "kernel": HEADLINE_KERNEL, "workload": "qwen3_30b_a3b_nf4 E=128 k=8 H=2048 I=768 T=4096",
+        "fetch_kib_per_launch_raw": round(f_head, 1), "write_kib_per_launch_raw": round(w_head, 1),
+        "calibration": {"kernel": "torch.neg float32", "bytes_read": CALIB_BYTES,
+                        "bytes_written": CALIB_BYTES, "fetch_kib_raw": round(f_cal, 1),
+                        "write_kib_raw": round(w_cal, 1), "fetch_scale": round(f_scale, 4),
+                        "write_scale": round(w_scale, 4)},
+        "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
+        "bytes_per_launch": round(fetch_b + write_b),
+        "launches": {"fetch": nf, "write": nw, "calibration": [ncf, ncw]},
+        "csrc_sha256": csrc_digest(),
+    }
+    path = os.path.join(out_dir, f"pmc_{PMC_TAG}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def csrc_digest():
@@ -385,9 +444,16 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--only", default="", help="comma list of sweep parts: qwen,gptoss,lora,stack")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run the copy kernel of known size (for PMC scaling)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write profiles/pmc_*.json from two rocprofv3 --pmc result databases")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], os.path.join(ROOT, "profiles"))
+        return
     if args.gpus != 1:
         print("bench.py measures a single GPU: the layer runs on one device here, with no "
               "sharding or collectives; run it with --gpus 1.", file=sys.stderr)
@@ -402,6 +468,8 @@ def main():
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
         f"{props.multi_processor_count} CUs")
 
+    if args.calibrate:
+        calibration_copy(torch)
     spec = inputs.QWEN3_30B_NF4
     t0 = time.time()
     exs = [nf4_layer(moe4, inputs, spec, r, args.seed, torch) for r in range(args.replicas)]
@@ -412,7 +480,7 @@ def main():
                                             args.steps, args.warmup, args.seed)
     log("headline:", json.dumps(head))
     achieved = flops_gu / (k_gu * 1e-3) / 1e12
-    traffic = traffic_from_profile("gate_up_tiled_nf4_qwen3_T4096")
+    traffic = traffic_from_profile()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic, "kernel": "gate_up grouped GEMM (tiled, NF4)",
@@ -474,7 +542,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{spec.name} T={HEADLINE_T}", "T": HEADLINE_T, "E": spec.E,
                    "top_k": spec.k, "H": spec.H, "I": spec.I, "format": "nf4",
-                   "replicas": args.replicas, "device": props.name},
+                   "replicas": args.replicas,
+                   "device": f"{props.name or 'AMD GPU'} {getattr(props, 'gcnArchName', '')}".strip()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sweep": sweep,
