@@ -124,6 +124,55 @@ __device__ __forceinline__ void locate_item(const int32_t* __restrict__ offsets,
   u_out = __shfl(uf, owner, kWave);
 }
 
+// Work item of workgroup b in a grouped GEMM whose experts are cut into BM-row
+// tiles, each tile split into ncg column groups. Items are (tile, column
+// group) pairs, column group fastest. The dispatcher deals workgroup ids
+// round-robin over the 8 XCDs (each with its own L2) and in id order within
+// one: XCD x gets a contiguous 1/8 of the full-tile items, then a contiguous
+// 1/8 of the partial-tile items (each expert's last, short tile). Items that
+// share an activation tile or an expert's weights stay on one XCD, and the
+// cheap partial tiles come last everywhere. The grid needs at least
+// (full + partial tiles) * ncg + 16 workgroups; the rest get e = -1.
+template <int BM>
+__device__ __forceinline__ void locate_tile_xcd(const int32_t* __restrict__ offsets, int E,
+                                                int ncg, int b, int& e_out, int& u_out,
+                                                int& cg_out) {
+  constexpr int kXcd = 8;
+  const int l = lane_id();
+  const int per = (E + kWave - 1) / kWave;
+  const int e0 = l * per;
+  int nf = 0, nr = 0;
+  if (e0 < E) {
+    int prev = offsets[e0];
+    for (int i = 0; i < per && e0 + i < E; ++i) {
+      const int nx = offsets[e0 + i + 1];
+      nf += (nx - prev) / BM;
+      nr += (nx - prev) % BM ? 1 : 0;
+      prev = nx;
+    }
+  }
+  const int NF = __shfl(wave_inclusive_scan(nf), kWave - 1, kWave) * ncg;
+  const int NR = __shfl(wave_inclusive_scan(nr), kWave - 1, kWave) * ncg;
+  const int x = b % kXcd, i = b / kXcd;
+  const int f0 = (int)((int64_t)NF * x / kXcd), f1 = (int)((int64_t)NF * (x + 1) / kXcd);
+  const int r0 = (int)((int64_t)NR * x / kXcd), r1 = (int)((int64_t)NR * (x + 1) / kXcd);
+  int item, e = -1, u = 0;
+  if (i < f1 - f0) {
+    item = f0 + i;
+    locate_item(offsets, E, item / ncg, [](int n) { return n / BM; }, e, u);
+  } else if (i < (f1 - f0) + (r1 - r0)) {
+    item = r0 + (i - (f1 - f0));
+    int unused;
+    locate_item(offsets, E, item / ncg, [](int n) { return n % BM ? 1 : 0; }, e, unused);
+    if (e >= 0) u = (offsets[e + 1] - offsets[e]) / BM;
+  } else {
+    item = 0;
+  }
+  e_out = e;
+  u_out = u;
+  cg_out = item % ncg;
+}
+
 // Remap a linear workgroup id so that consecutive logical ids land on the same
 // XCD (the dispatcher deals workgroups round-robin over the 8 XCDs, each with
 // its own L2). Bijective for any grid size.

@@ -283,10 +283,8 @@ __global__ __launch_bounds__(256, 2) void k_tiled(const GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t stage_mem[];
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   if (NF4) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int q = logical / a.ncg, cg = logical - q * a.ncg;
-  int e, ut;
-  locate_item(a.offsets, a.E, q, [](int n) { return (n + kBM - 1) / kBM; }, e, ut);
+  int e, ut, cg;
+  locate_tile_xcd<kBM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
   // wave-uniform by construction; make it visible to the compiler so that the
   // buffer resources below live in scalar registers
   e = __builtin_amdgcn_readfirstlane(e);
@@ -516,8 +514,10 @@ hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
 
 template <int FMT, bool GATEUP>
 hipError_t run_tiled(const GemmArgs& a, int ntiles, hipStream_t s) {
-  const int nwg = ntiles * a.ncg;
-  if (nwg == 0) return hipSuccess;
+  if (ntiles == 0) return hipSuccess;
+  // ntiles bounds full + partial tiles; 16 spare ids keep every XCD's share
+  // of the items within the ids it is dealt
+  const int nwg = ntiles * a.ncg + 16;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tiled<FMT, GATEUP>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kTiledLds);
