@@ -77,7 +77,8 @@ __device__ __forceinline__ void gate_up_epilogue(const GemmArgs& a, int e, int r
 
 __device__ __forceinline__ void down_epilogue(const GemmArgs& a, int e, int row, int col, float y) {
   if (a.bias) y += bf16_to_f32(a.bias[(int64_t)e * a.N_out + col]);
-  a.yout[(int64_t)row * a.N_out + col] = y;
+  // y rows are read once, by the combine, long after: stream them out
+  __builtin_nontemporal_store(y, a.yout + (int64_t)row * a.N_out + col);
 }
 
 // expert owning permuted row `row` (largest e with offsets[e] <= row)

@@ -173,15 +173,25 @@ __device__ __forceinline__ void copy_row(const uint16_t* __restrict__ x, int src
   const u32x4* s = reinterpret_cast<const u32x4*>(x + (int64_t)src_row * H);
   u32x4* d = reinterpret_cast<u32x4*>(dst);
   const int nv = H / 8;
-  if (row_scale == nullptr) {
-    for (int c = l; c < nv; c += kWave) d[c] = s[c];
-  } else {
-    const float sc = row_scale[slot];
-    for (int c = l; c < nv; c += kWave) {
-      u32x4 v = s[c], o;
+  const float sc = row_scale ? row_scale[slot] : 1.0f;
+  // four 16-byte chunks a lane in flight at once
+  for (int c0 = l; c0 < nv; c0 += 4 * kWave) {
+    u32x4 v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(sc * bf16lo(v[i]), sc * bf16hi(v[i]));
-      d[c] = o;
+    for (int u = 0; u < 4; ++u)
+      if (c0 + u * kWave < nv) v[u] = s[c0 + u * kWave];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (c0 + u * kWave >= nv) break;
+      if (row_scale) {
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = pack_bf16x2(sc * bf16lo(v[u][i]), sc * bf16hi(v[u][i]));
+        __builtin_nontemporal_store(o, d + c0 + u * kWave);
+      } else {
+        __builtin_nontemporal_store(v[u], d + c0 + u * kWave);
+      }
     }
   }
 }
@@ -351,35 +361,42 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
   const int t = (int)((blockIdx.x * (unsigned)blockDim.x + threadIdx.x) >> 6);
   if (t >= T) return;
   const int l = lane_id();
-  const int nv = H / 8;
-  for (int c = l; c < nv; c += kWave) {
-    float acc[8];
+  // lane l takes the 4-float chunks l, l + 64, ... of the row, so that every
+  // load instruction of the wave reads 1 KiB of one y row contiguously; the
+  // first kU rows of the token have all their loads in flight together, any
+  // further rows (k > kU) follow one at a time
+  const int nv = H / 4;
+  constexpr int kU = 8;
+  const int ku = min(k, kU);
+  int rows[kU];
+  float wts[kU];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
+  for (int j = 0; j < kU; ++j) {
+    if (j < ku) {
       const int64_t s = (int64_t)t * k + j;
-      const int r = row_of_slot[s];
+      rows[j] = row_of_slot[s];
+      wts[j] = w ? w[s] : 1.0f;
+    }
+  }
+  for (int c = l; c < nv; c += kWave) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 v[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j)
+      if (j < ku) v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (int64_t)rows[j] * H) + c);
+#pragma unroll
+    for (int j = 0; j < kU; ++j)
+      if (j < ku) acc += wts[j] * v[j];
+    for (int j = kU; j < k; ++j) {
+      const int64_t s = (int64_t)t * k + j;
       const float wj = w ? w[s] : 1.0f;
-      const float4* src = reinterpret_cast<const float4*>(y + (int64_t)r * H) + 2 * c;
-      const float4 v0 = src[0], v1 = src[1];
-      acc[0] += wj * v0.x;
-      acc[1] += wj * v0.y;
-      acc[2] += wj * v0.z;
-      acc[3] += wj * v0.w;
-      acc[4] += wj * v1.x;
-      acc[5] += wj * v1.y;
-      acc[6] += wj * v1.z;
-      acc[7] += wj * v1.w;
+      acc += wj * reinterpret_cast<const f32x4*>(y + (int64_t)row_of_slot[s] * H)[c];
     }
     if (OUT_F32) {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + (int64_t)t * H) + 2 * c;
-      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)t * H)[c] = acc;
     } else {
-      u32x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-      reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + (int64_t)t * H)[c] = o;
+      const uint2 o = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (int64_t)t * H)[c] = o;
     }
   }
 }
