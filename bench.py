@@ -102,6 +102,11 @@ def mxfp4_layer(moe4, inputs, spec, layer, seed, torch):
     if spec.bias:
         bias = dict(gu_bias=inputs.device_bf16((E, 2 * I), spec.bias_std, seed, spec, layer, 9),
                     dn_bias=inputs.device_bf16((E, H), spec.bias_std, seed, spec, layer, 10))
+    if spec.lora_r:
+        bias.update(lora_A=inputs.device_bf16((E, spec.lora_r, H), 1.0 / H ** 0.5, seed, spec,
+                                              layer, 11),
+                    lora_B=inputs.device_bf16((E, 2 * I, spec.lora_r), 0.01, seed, spec, layer, 12),
+                    lora_scale=spec.lora_scale)
     return moe4.Experts(moe4.MOE4_FMT_MXFP4, gb, gsc, db, dsc,
                         gu_layout=(moe4.MOE4_GU_INTERLEAVED if spec.layout == "interleaved"
                                    else moe4.MOE4_GU_HALVES),
@@ -514,6 +519,13 @@ def main():
             log("sweep:", json.dumps(r))
             sweep.append(r)
             del lex
+            mspec = inputs.GPT_OSS_20B_MXFP4_LORA
+            mex = mxfp4_layer(moe4, inputs, mspec, 0, args.seed, torch)
+            r = bench_backward(torch, hip, moe4, inputs, mspec, mspec.tokens[0], mex, reps,
+                               args.warmup, args.seed)
+            log("sweep:", json.dumps(r))
+            sweep.append(r)
+            del mex
         if not only or "stack" in only:
             s5 = inputs.GPT_OSS_120B_STACK
             t0 = time.time()

@@ -64,10 +64,11 @@ __global__ __launch_bounds__(256) void k_dgrad(const DgradArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kDN * kDL];
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int q = logical / a.ncg, cg = logical - q * a.ncg;
-  int e, ut;
-  locate_item(a.offsets, a.E, q, [](int n) { return (n + kDM - 1) / kDM; }, e, ut);
+  int e, ut, cg;
+  locate_tile_xcd<kDM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
+  e = __builtin_amdgcn_readfirstlane(e);
+  ut = __builtin_amdgcn_readfirstlane(ut);
+  cg = __builtin_amdgcn_readfirstlane(cg);
   __syncthreads();
   if (e < 0) return;
   const int row0 = min(a.offsets[e], a.rows) + ut * kDM;
@@ -275,7 +276,8 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   d.ncg = (I + kDN - 1) / kDN;
   le.before(0, s);
   if (ntiles * d.ncg > 0)
-    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_DOWN>), dim3(ntiles * d.ncg), dim3(256), 0, s, d);
+    // 16 spare ids keep every XCD's share of the items within the ids it is dealt
+    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_DOWN>), dim3(ntiles * d.ncg + 16), dim3(256), 0, s, d);
   le.after(0, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -300,7 +302,8 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   g.ncg = (H + kDN - 1) / kDN;
   le.before(1, s);
   if (ntiles * g.ncg > 0)
-    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_GATEUP>), dim3(ntiles * g.ncg), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_GATEUP>), dim3(ntiles * g.ncg + 16), dim3(256), 0, s,
+                       g);
   le.after(1, s);
   err = hipGetLastError();
   if (err != hipSuccess || !lora) return err;

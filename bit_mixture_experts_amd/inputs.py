@@ -81,6 +81,13 @@ GPT_OSS_120B_STACK = LayerSpec("gpt_oss_120b_mxfp4_stack_36L_E128_k4", 5, "mxfp4
 WORKLOADS = (TINY_NF4, QWEN3_30B_NF4, GPT_OSS_20B_MXFP4, QWEN3_30B_NF4_LORA,
              GPT_OSS_120B_STACK)
 
+# Beyond the five: per-expert LoRA over the native MXFP4 gpt-oss-20b-shaped
+# experts, with their biases, interleaved gate/up rows and clamped GLU
+# (forward + backward), the adapter variant of the MXFP4 training path.
+GPT_OSS_20B_MXFP4_LORA = LayerSpec("gpt_oss_20b_mxfp4_lora_r8", 6, "mxfp4", E=32, k=4,
+                                   H=2880, I=2880, tokens=(2048,), layout="interleaved",
+                                   act="swiglu_clamped", bias=True, lora_r=8, lora_alpha=16.0)
+
 
 def _rng(seed, spec, *path):
     return np.random.default_rng(np.random.SeedSequence([int(seed), spec.seed_id,

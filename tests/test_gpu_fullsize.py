@@ -84,17 +84,25 @@ class BigMXFP4Layer:
         self.spec = spec
         self.q = inp.host_stack_mxfp4(spec, layer, seed)
         self.bias = inp.host_stack_bias(spec, layer, seed) if spec.bias else (None, None)
+        self.A = self.B = None
+        if spec.lora_r:
+            self.A, self.B = inp.host_stack_lora(spec, layer, seed)
         self.W = oracle.ExpertWeights.from_mxfp4(*self.q, layout=spec.layout, act=spec.act,
                                                  gu_bias=self.bias[0], dn_bias=self.bias[1],
+                                                 lora_A=self.A, lora_B=self.B,
+                                                 lora_scale=spec.lora_scale,
                                                  alpha=spec.alpha, limit=spec.limit)
 
     def device(self):
         s = self.spec
         t = lambda a: None if a is None else to_dev(a)
+        lora = {}
+        if self.A is not None:
+            lora = dict(lora_A=to_dev(self.A), lora_B=to_dev(self.B), lora_scale=s.lora_scale)
         return moe4.Experts(moe4.MOE4_FMT_MXFP4, *[to_dev(a) for a in self.q],
                             gu_layout=moe4.MOE4_GU_INTERLEAVED, act=moe4.MOE4_ACT_SWIGLU_CLAMPED,
                             E=s.E, H=s.H, I=s.I, gu_bias=t(self.bias[0]), dn_bias=t(self.bias[1]),
-                            act_alpha=s.alpha, act_limit=s.limit)
+                            act_alpha=s.alpha, act_limit=s.limit, **lora)
 
 
 def _check_layer(spec, W, ex, T, n_sample, layer=0, seed=0):
@@ -176,11 +184,21 @@ def _stack_layer(spec, layer):
 
 
 def test_lora_backward_full(qwen_lora_layer):
-    spec = inp.QWEN3_30B_NF4_LORA
-    T = spec.tokens[0]
-    say(f"per-expert LoRA on the Qwen3-shaped NF4 stack, T={T}: forward + backward")
+    say("per-expert LoRA on the Qwen3-shaped NF4 stack: forward + backward")
     L = qwen_lora_layer
-    ex = L.device()
+    _check_lora_backward(inp.QWEN3_30B_NF4_LORA, L.device(), L.W())
+
+
+def test_mxfp4_lora_backward_full():
+    spec = inp.GPT_OSS_20B_MXFP4_LORA
+    say("per-expert LoRA on the gpt-oss-20b-shaped MXFP4 stack (bias, clamped GLU): "
+        "forward + backward")
+    L = BigMXFP4Layer(spec)
+    _check_lora_backward(spec, L.device(), L.W)
+
+
+def _check_lora_backward(spec, ex, W):
+    T = spec.tokens[0]
     x, lg = inp.host_tokens(spec, T)
     dout = inp.host_upstream_grad(spec, T)
     res = run_layer(ex, to_dev(x), to_dev(lg), spec.k, save=True)
@@ -200,7 +218,6 @@ def test_lora_backward_full(qwen_lora_layer):
     torch.cuda.synchronize()
     ri, rw = oracle.route(lg, spec.k)
     assert np.array_equal(res["idx"].cpu().numpy(), ri)
-    W = L.W()
     # dX of sampled tokens: the oracle backward of those tokens alone
     tokens = np.sort(np.random.default_rng(5).choice(T, 4, replace=False))
     say("  oracle dX on sampled tokens")
