@@ -38,7 +38,8 @@ published NF4 construction). No function is "parity unpinned".
 
 from .numerics import bf16_bits_from_f32, bf16_bits_to_f64, bf16_bits_to_f32, bf16_round_f64
 from .formats import (NF4_LEVELS, nf4_midpoints, quantize_nf4, dequantize_nf4,
-                      dequantize_nf4_bf16, E2M1_MAGNITUDES, mxfp4_values, decode_mxfp4_bf16)
+                      dequantize_nf4_bf16, E2M1_MAGNITUDES, mxfp4_values, decode_mxfp4_bf16,
+                      convert_mxfp4_to_nf4)
 from .routing import route, permute, gather_rows
 from .layer import (ExpertWeights, gate_up, activation, down, combine,
                     layer_forward, layer_backward, token_forward)
@@ -46,7 +47,7 @@ from .layer import (ExpertWeights, gate_up, activation, down, combine,
 __all__ = [
     "bf16_bits_from_f32", "bf16_bits_to_f64", "bf16_bits_to_f32", "bf16_round_f64",
     "NF4_LEVELS", "nf4_midpoints", "quantize_nf4", "dequantize_nf4", "dequantize_nf4_bf16",
-    "E2M1_MAGNITUDES", "mxfp4_values", "decode_mxfp4_bf16",
+    "E2M1_MAGNITUDES", "mxfp4_values", "decode_mxfp4_bf16", "convert_mxfp4_to_nf4",
     "route", "permute", "gather_rows",
     "ExpertWeights", "gate_up", "activation", "down", "combine",
     "layer_forward", "layer_backward", "token_forward",

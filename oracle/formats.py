@@ -151,3 +151,33 @@ def decode_mxfp4_bf16(blocks, scales):
     with np.errstate(over="ignore", invalid="ignore"):
         v32 = v.astype(np.float32)
     return bf16_bits_from_f32(v32)
+
+
+def convert_mxfp4_to_nf4(blocks, scales):
+    """Re-quantise an MXFP4 stack to NF4 ([MXFP4 page], "Two fidelity paths",
+    the convenient QLoRA path: an exact decode of the released blocks, then the
+    NF4 quantiser applied to the decoded stack).
+
+    blocks uint8 [R, K/32, 16], scales uint8 [R, K/32], K % 64 == 0. The decode
+    is the bf16 one (``decode_mxfp4_bf16``); its values, read as fp32, go
+    through ``quantize_nf4`` row-major, so each NF4 block of 64 covers two
+    consecutive MXFP4 blocks of one row. Returns (packed uint8 [R, K/2],
+    absmax float32 [R, K/64]). Scale bytes up to 252 always decode to finite
+    values; a block that decodes to inf or NaN is refused, like any non-finite
+    input of the quantiser.
+
+    Reading: the page says the decoded stack is quantised but not in which
+    dtype it is held in between; bf16, the decode's own output, is the plain
+    one (for scale bytes up to 252 it holds every decoded value exactly, so
+    the choice changes nothing there).
+    """
+    b = np.asarray(blocks, dtype=np.uint8)
+    s = np.asarray(scales, dtype=np.uint8)
+    if b.ndim != 3 or b.shape[-1] != 16 or s.shape != b.shape[:2]:
+        raise ValueError("blocks must be [R, K/32, 16] and scales [R, K/32]")
+    R, nb = s.shape
+    if nb % 2:
+        raise ValueError("K must be a multiple of 64")
+    dec = bf16_bits_to_f64(decode_mxfp4_bf16(b, s)).astype(np.float32)
+    packed, absmax = quantize_nf4(dec.reshape(-1))
+    return packed.reshape(R, nb * 16), absmax.reshape(R, nb // 2)

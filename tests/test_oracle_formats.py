@@ -14,7 +14,7 @@ import torch
 from scipy.stats import norm
 
 from oracle import (NF4_LEVELS, nf4_midpoints, quantize_nf4, dequantize_nf4,
-                    mxfp4_values, decode_mxfp4_bf16)
+                    mxfp4_values, decode_mxfp4_bf16, convert_mxfp4_to_nf4)
 from oracle.formats import nf4_codes
 from tests.conftest import read_golden
 
@@ -201,3 +201,98 @@ def test_mxfp4_values_layout():
             byte = int(blocks[r, k // 32, (k % 32) // 2])
             nib = byte & 15 if k % 2 == 0 else byte >> 4
             assert v[r, k] == _ocp_e2m1(nib) * 2.0 ** (int(scales[r, k // 32]) - 127)
+
+
+# -------------------------------------------------------- MXFP4 -> NF4
+
+def _ocp_values(blocks, scales):
+    """Element values of [R, K/32, 16] blocks from the OCP bit fields, one by one
+    (float64; exact)."""
+    R, nb, _ = blocks.shape
+    v = np.empty((R, nb * 32))
+    for r in range(R):
+        for k in range(nb * 32):
+            byte = int(blocks[r, k // 32, (k % 32) // 2])
+            nib = byte & 15 if k % 2 == 0 else byte >> 4
+            v[r, k] = math.ldexp(_ocp_e2m1(nib), int(scales[r, k // 32]) - 127)
+    return v
+
+
+def test_convert_mxfp4_nf4_matches_brute_force():
+    # scale pairs inside one NF4 block range from equal to far apart, down to
+    # the fp32-subnormal decodes of scale bytes 0 and 1
+    rng = np.random.default_rng(11)
+    R, K = 24, 192
+    blocks = rng.integers(0, 256, (R, K // 32, 16), dtype=np.uint8)
+    scales = rng.integers(118, 131, (R, K // 32), dtype=np.uint8)
+    scales[:8] = rng.integers(0, 253, (8, K // 32), dtype=np.uint8)
+    scales[8:12, 1::2] = scales[8:12, 0::2] - rng.integers(0, 9, (4, K // 64), dtype=np.uint8)
+    scales[12, :] = [0, 1, 1, 0, 2, 0]
+    blocks[13, 2:4] = 0x88            # a block of negative zeros
+    blocks[14, 4:6] = 0               # an all-zero block
+    packed, absmax = convert_mxfp4_to_nf4(blocks, scales)
+    assert packed.shape == (R, K // 2) and absmax.shape == (R, K // 64)
+    v = _ocp_values(blocks, scales).astype(np.float32)   # exact: <= 2 significant bits
+    assert np.array_equal(v.astype(np.float64), _ocp_values(blocks, scales))
+    bc, tie, am = _brute_codes(v.reshape(-1))
+    assert not tie.any()
+    assert np.array_equal(absmax.reshape(-1), am)
+    assert np.array_equal(nf4_codes(packed.reshape(-1)), bc)
+    assert absmax[14, 2] == 0 and np.all(packed[14, 64:96] == 0x77)
+    assert np.all(packed[13, 32:64] == 0x77)
+
+
+def test_convert_mxfp4_nf4_no_ratio_on_a_threshold():
+    # every x = v / absmax the conversion can form: e2m1 magnitude ratios times
+    # powers of two; none lies on an NF4 decision threshold, so the
+    # nearest-level rule has no ties to break on this path
+    mags = [0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    xs = set()
+    for a in mags:
+        for m in mags:
+            for d in range(-12, 13):
+                x = np.float32(math.ldexp(a, d)) / np.float32(m)
+                if x <= 1:
+                    xs.update([float(x), -float(x)])
+    mids = set(float(m) for m in nf4_midpoints())
+    assert not (xs & mids)
+
+
+def test_convert_mxfp4_nf4_closed_forms():
+    # uniform blocks: every element equal -> absmax = |value|, codes 15 / 0
+    for nib, code in ((7, 15), (0xF, 0), (3, 15), (0xB, 0), (1, 15)):
+        byte = nib | (nib << 4)
+        blocks = np.full((1, 2, 16), byte, np.uint8)
+        scales = np.array([[125, 125]], np.uint8)
+        packed, absmax = convert_mxfp4_to_nf4(blocks, scales)
+        assert absmax[0, 0] == abs(_ocp_e2m1(nib)) * 2.0 ** -2
+        assert np.all(nf4_codes(packed.reshape(-1)) == code)
+    # hand case: 6 * 2^0 in element 0 (first block), 6 * 2^-2 = 1.5 in element
+    # 32 (second block, scale 125), 0.5 * 2^0 in element 1: x = 1, 0.25, 1/12
+    blocks = np.zeros((1, 2, 16), np.uint8)
+    blocks[0, 0, 0] = 0x17     # element 0 = nibble 7 (6.0), element 1 = nibble 1 (0.5)
+    blocks[0, 1, 0] = 0x07     # element 32 = nibble 7
+    scales = np.array([[127, 125]], np.uint8)
+    packed, absmax = convert_mxfp4_to_nf4(blocks, scales)
+    codes = nf4_codes(packed.reshape(-1))
+    assert absmax[0, 0] == 6.0
+    # 0.25 is nearest to level 10 (0.2461); 1/12 = 0.0833 to level 8 (0.0796)
+    assert codes[0] == 15 and codes[32] == 10 and codes[1] == 8
+    assert np.all(np.delete(codes, [0, 1, 32]) == 7)
+
+
+def test_convert_mxfp4_nf4_round_trip_bound_and_refusals():
+    rng = np.random.default_rng(12)
+    blocks = rng.integers(0, 256, (16, 6, 16), dtype=np.uint8)
+    scales = rng.integers(118, 131, (16, 6), dtype=np.uint8)
+    packed, absmax = convert_mxfp4_to_nf4(blocks, scales)
+    v = _ocp_values(blocks, scales).reshape(-1, 64)
+    deq = dequantize_nf4(packed.reshape(-1), absmax.reshape(-1)).reshape(-1, 64)
+    half_gap = np.max(np.diff(NF4_LEVELS.astype(np.float64))) / 2
+    assert np.all(np.abs(deq - v) <= half_gap * absmax.reshape(-1, 1))
+    with pytest.raises(ValueError):      # K = 32 is not a whole NF4 block
+        convert_mxfp4_to_nf4(blocks[:, :1], scales[:, :1])
+    bad = scales.copy()
+    bad[0, 0] = 255                       # e8m0 NaN
+    with pytest.raises(ValueError):
+        convert_mxfp4_to_nf4(blocks, bad)
