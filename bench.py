@@ -315,6 +315,45 @@ def bench_stack(torch, hip, moe4, inputs, spec, T, exs, steps, warmup, seed):
             "hbm_frac_end_to_end": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def bench_convert(torch, hip, moe4, inputs, spec, steps, warmup, seed, nrep=2):
+    """MXFP4 -> NF4 re-quantisation of whole gate_up and down stacks (two
+    launches per pass), alternating between independently seeded layers so
+    that every pass reads cold bytes. Bytes = MXFP4 in + NF4 out."""
+    stream = torch.cuda.current_stream().cuda_stream
+    layers = []
+    for li in range(nrep):
+        gb, gsc, db, dsc = inputs.device_mxfp4_stack(spec, li, seed)
+        outs = []
+        for b, sc in ((gb, gsc), (db, dsc)):
+            R, K = sc.numel() // sc.shape[-1], sc.shape[-1] * 32
+            outs.append((b, sc, torch.empty((R, K // 2), dtype=torch.uint8, device=b.device),
+                         torch.empty((R, K // 64), dtype=torch.float32, device=b.device)))
+        layers.append(outs)
+
+    def run(i):
+        for b, sc, p, a in layers[i % nrep]:
+            moe4.moe4_convert_mxfp4_nf4(b, sc, p, a)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev = hip.events(2 * steps)
+    for i in range(steps):
+        hip.record(ev[2 * i], stream)
+        run(warmup + i)
+        hip.record(ev[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    ms = sorted(hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(steps))
+    med = ms[len(ms) // 2]
+    nbytes = sum(b.numel() + sc.numel() + p.numel() + 4 * a.numel()
+                 for b, sc, p, a in layers[0])
+    gbps = nbytes / (med * 1e-3) / 1e9
+    return {"workload": f"{spec.name} MXFP4->NF4 conversion", "stacks": "gate_up + down",
+            "weights": int(sum(p.numel() * 2 for _, _, p, _ in layers[0])),
+            "bytes_in_out": int(nbytes), "ms": round(med, 4), "GBps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBS, 4)}
+
+
 # -------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(spec, T_batch, n_tokens, seed=0):
@@ -450,7 +489,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
-    ap.add_argument("--only", default="", help="comma list of sweep parts: qwen,gptoss,lora,stack")
+    ap.add_argument("--only", default="", help="comma list of sweep parts: qwen,gptoss,lora,convert,stack")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run the copy kernel of known size (for PMC scaling)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -526,6 +565,11 @@ def main():
             log("sweep:", json.dumps(r))
             sweep.append(r)
             del mex
+        if not only or "convert" in only:
+            r = bench_convert(torch, hip, moe4, inputs, inputs.GPT_OSS_20B_MXFP4, reps,
+                              args.warmup, args.seed)
+            log("sweep:", json.dumps(r))
+            sweep.append(r)
         if not only or "stack" in only:
             s5 = inputs.GPT_OSS_120B_STACK
             t0 = time.time()

@@ -109,6 +109,119 @@ __global__ __launch_bounds__(256) void k_decode_mxfp4(const uint8_t* __restrict_
   }
 }
 
+// ---------------------------------------------------- MXFP4 -> NF4 re-quantisation
+//
+// The convenient QLoRA path of the MXFP4 page ("Two fidelity paths"): decode
+// the released blocks exactly, then quantise the decoded stack to NF4. Fused
+// here into one pass with no floating-point work per element: every decoded
+// value is m * 2^(s-127) with m an e2m1 magnitude, so the block's absmax is
+// (1 + f/2) * 2^(Emax - 127) (f = 0 or 1) and the quantiser's ratio
+// x = fp32(v / absmax) = fp32(m * 2^(s - Emax) / (1 + f/2)) depends only on
+// v's nibble, f and the exponent gap d = s - Emax. A lane's 32 values share
+// one scale, so one table of 16 codes per (f, d) maps all of them. The
+// tables are built at compile time with the quantiser's own rule (IEEE fp32
+// division, fp32 midpoints), which makes the codes those of quantising the
+// decoded values, subnormal decodes (scale bytes 0 and 1) included.
+
+constexpr float kE2m1Mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+// d = 1, 0, -1, ..., -7 take buckets 0..8; d <= -8 (every |x| < 0.024, code 7)
+// and the all-zero block take bucket 9
+constexpr int kConvBuckets = 10;
+
+// code of nibble n for bucket b and absmax mantissa 1 + f/2
+constexpr uint32_t conv_code(int f, int b, int n) {
+  const float mag = kE2m1Mag[n & 7];
+  if (mag == 0.0f || b >= kConvBuckets - 1) return 7u;
+  float p = mag;   // m * 2^d, exact
+  for (int i = 0; i < 1 - b; ++i) p *= 2.0f;
+  for (int i = 0; i < b - 1; ++i) p *= 0.5f;
+  float x = p / (f ? 1.5f : 1.0f);   // correctly rounded, as in the quantiser
+  if (n & 8) x = -x;
+  uint32_t c = 0;
+  for (int i = 0; i < 15; ++i) c += (x > mid(i)) ? 1u : 0u;
+  return c;
+}
+// four codes as bytes: nibbles 4j .. 4j+3 (j = 0: m 0..3 positive, 1: m 4..7
+// positive, 2 and 3: the same magnitudes negative)
+constexpr uint32_t conv_word(int f, int b, int j) {
+  return conv_code(f, b, 4 * j) | (conv_code(f, b, 4 * j + 1) << 8) |
+         (conv_code(f, b, 4 * j + 2) << 16) | (conv_code(f, b, 4 * j + 3) << 24);
+}
+#define MOE4_CONV_ROW(f, b) \
+  conv_word(f, b, 0), conv_word(f, b, 1), conv_word(f, b, 2), conv_word(f, b, 3)
+#define MOE4_CONV_F(f)                                                                    \
+  MOE4_CONV_ROW(f, 0), MOE4_CONV_ROW(f, 1), MOE4_CONV_ROW(f, 2), MOE4_CONV_ROW(f, 3),     \
+      MOE4_CONV_ROW(f, 4), MOE4_CONV_ROW(f, 5), MOE4_CONV_ROW(f, 6), MOE4_CONV_ROW(f, 7), \
+      MOE4_CONV_ROW(f, 8), MOE4_CONV_ROW(f, 9)
+__constant__ uint32_t kConvLut[2 * kConvBuckets * 4] = {MOE4_CONV_F(0), MOE4_CONV_F(1)};
+#undef MOE4_CONV_F
+#undef MOE4_CONV_ROW
+
+// 8 nibbles (one dword) -> 8 NF4 codes, through the lane's table t: the byte
+// permute looks up four magnitudes at once, the sign picks the table half
+__device__ __forceinline__ uint32_t conv_dword(uint32_t w, const u32x4& t) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t nb = (w >> (4 * h)) & 0x0F0F0F0Fu;   // nibbles h, h+2, h+4, h+6 as bytes
+    const uint32_t m = nb & 0x07070707u;
+    const uint32_t neg = ((nb >> 3) & 0x01010101u) * 0xFFu;
+    const uint32_t cp = __builtin_amdgcn_perm(t[1], t[0], m);
+    const uint32_t cn = __builtin_amdgcn_perm(t[3], t[2], m);
+    out |= ((cn & neg) | (cp & ~neg)) << (4 * h);
+  }
+  return out;
+}
+
+// Two lanes per NF4 block of 64: lane h of block q owns MXFP4 block 2q + h
+// (16 bytes, one scale); codes go to the same 16 bytes of the output.
+__global__ __launch_bounds__(256) void k_convert_mxfp4_nf4(const uint8_t* __restrict__ blocks,
+                                                           const uint8_t* __restrict__ scales,
+                                                           int64_t nmx,
+                                                           uint8_t* __restrict__ packed,
+                                                           float* __restrict__ absmax) {
+  __shared__ u32x4 lut[2 * kConvBuckets];
+  if (threadIdx.x < 2 * kConvBuckets)
+    lut[threadIdx.x] = u32x4{kConvLut[4 * threadIdx.x], kConvLut[4 * threadIdx.x + 1],
+                             kConvLut[4 * threadIdx.x + 2], kConvLut[4 * threadIdx.x + 3]};
+  __syncthreads();
+  const int64_t mb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool valid = mb < nmx;   // nmx is even: both lanes of a pair agree
+  u32x4 q = {0u, 0u, 0u, 0u};
+  uint32_t s = 0;
+  if (valid) {
+    q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blocks) + mb);
+    s = scales[mb];
+  }
+  uint32_t mm = 0;   // largest magnitude index among the lane's 32 nibbles
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mm = max(mm, (q[i] >> (4 * j)) & 7u);
+  // key monotone in |value| = (1 + f/2) 2^(E - 127): 2 (E + 2) + f, with
+  // E = s + (-1, 0, 0, 1, 1, 2, 2) and f = (0, 0, 1, 0, 1, 0, 1) for m = 1..7;
+  // 0 when the lane holds only zeros
+  const uint32_t kl = mm ? 2u * s + mm + 2u - (mm == 1u ? 1u : 0u) : 0u;
+  const uint32_t key = max(kl, (uint32_t)__shfl_xor((int)kl, 1, kWave));
+  const int emax = (int)(key >> 1) - 2, f = (int)(key & 1u);
+  const int d = (int)s - emax;
+  const int b = key == 0u ? kConvBuckets - 1 : min(max(1 - d, 0), kConvBuckets - 1);
+  const u32x4 t = lut[f * kConvBuckets + b];
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = conv_dword(q[i], t);
+  // absmax = (1 + f/2) 2^(emax - 127); emax >= -1; subnormal for emax <= 0
+  uint32_t abits;
+  if (key == 0u) abits = 0u;
+  else if (emax >= 255) abits = 0x7F800000u;   // overflow: the decode itself is not finite
+  else if (emax >= 1) abits = ((uint32_t)emax << 23) | ((uint32_t)f << 22);
+  else abits = (2u + (uint32_t)f) << (emax + 21);
+  if (valid) {
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(packed) + mb);
+    if ((mb & 1) == 0) absmax[mb >> 1] = __uint_as_float(abits);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_nf4(const float* w, int64_t n, uint8_t* packed, float* absmax,
@@ -119,6 +232,16 @@ hipError_t launch_quantize_nf4(const float* w, int64_t n, uint8_t* packed, float
   const int64_t grid = (threads + 255) / 256;
   hipLaunchKernelGGL(k_quantize_nf4, dim3((unsigned)grid), dim3(256), 0, s, w, nblocks, packed,
                      absmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert_mxfp4_nf4(const uint8_t* blocks, const uint8_t* scales, int64_t R,
+                                    int64_t K, uint8_t* packed, float* absmax, hipStream_t s) {
+  const int64_t nmx = R * (K / 32);
+  if (nmx == 0) return hipSuccess;
+  const int64_t grid = (nmx + 255) / 256;
+  hipLaunchKernelGGL(k_convert_mxfp4_nf4, dim3((unsigned)grid), dim3(256), 0, s, blocks, scales,
+                     nmx, packed, absmax);
   return hipGetLastError();
 }
 

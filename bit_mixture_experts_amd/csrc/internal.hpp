@@ -15,6 +15,8 @@ hipError_t launch_quantize_nf4(const float* w, int64_t n, uint8_t* packed, float
                                hipStream_t s);
 hipError_t launch_decode_mxfp4(const uint8_t* blocks, const uint8_t* scales, int64_t R,
                                int64_t K, uint16_t* out, hipStream_t s);
+hipError_t launch_convert_mxfp4_nf4(const uint8_t* blocks, const uint8_t* scales, int64_t R,
+                                    int64_t K, uint8_t* packed, float* absmax, hipStream_t s);
 
 // ---- routing / permutation / combine
 hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, int32_t* idx,

@@ -151,6 +151,24 @@ int moe4_decode_mxfp4(const uint8_t* blocks, const uint8_t* scales, int64_t R, i
                   "moe4_decode_mxfp4");
 }
 
+int moe4_convert_mxfp4_nf4(const uint8_t* blocks, const uint8_t* scales, int64_t R, int64_t K,
+                           uint8_t* packed, float* absmax, void* stream) {
+  if (R < 0 || K < 0 || K % 64)
+    return fail(MOE4_ESHAPE, "R = %lld, K = %lld: need R >= 0 and K a non-negative multiple of 64",
+                (long long)R, (long long)K);
+  if (R == 0 || K == 0) return ok();
+  REQUIRE_PTR(blocks, "blocks");
+  REQUIRE_PTR(scales, "scales");
+  REQUIRE_PTR(packed, "packed");
+  REQUIRE_PTR(absmax, "absmax");
+  REQUIRE_ALIGN(blocks, 16, "blocks");
+  REQUIRE_ALIGN(packed, 16, "packed");
+  REQUIRE_ALIGN(absmax, 4, "absmax");
+  return launched(
+      moe4::launch_convert_mxfp4_nf4(blocks, scales, R, K, packed, absmax, (hipStream_t)stream),
+      "moe4_convert_mxfp4_nf4");
+}
+
 int moe4_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renormalize,
                int32_t* topk_idx, float* topk_w, void* stream) {
   if (E < 1 || E > 1024) return fail(MOE4_ESHAPE, "E = %d outside [1, 1024]", E);

@@ -29,7 +29,8 @@ MOE4_VARIANT_AUTO, MOE4_VARIANT_SKINNY, MOE4_VARIANT_TILED = 0, 1, 2
 MOE4_DTYPE_BF16, MOE4_DTYPE_F32 = 1, 2
 
 # every symbol declared in include/moe4.h
-EXPORTS = ("moe4_quantize_nf4", "moe4_decode_mxfp4", "moe4_route", "moe4_permute",
+EXPORTS = ("moe4_quantize_nf4", "moe4_decode_mxfp4", "moe4_convert_mxfp4_nf4", "moe4_route",
+           "moe4_permute",
            "moe4_expert_forward", "moe4_combine", "moe4_expert_backward",
            "moe4_workspace_size", "moe4_set_timing_events", "moe4_last_error",
            "moe4_last_variant")
@@ -55,6 +56,7 @@ _P = ctypes.POINTER(Moe4Experts)
 _SIGS = {
     "moe4_quantize_nf4": ([_vp, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
     "moe4_decode_mxfp4": ([_vp, _vp, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "moe4_convert_mxfp4_nf4": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "moe4_route": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "moe4_permute": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
                      ctypes.c_int),
@@ -159,6 +161,18 @@ def moe4_decode_mxfp4(blocks, scales, out, stream=None):
     K = scales.shape[-1] * 32
     _check(_lib.moe4_decode_mxfp4(_ptr(blocks, _U8, "blocks"), _ptr(scales, _U8, "scales"),
                                   R, K, _ptr(out, _BF16, "out"), _stream(stream)))
+
+
+def moe4_convert_mxfp4_nf4(blocks, scales, packed, absmax, stream=None):
+    """blocks u8 [..., K/32, 16], scales u8 [..., K/32] -> packed u8 [..., K/2],
+    absmax f32 [..., K/64]."""
+    R = scales.numel() // scales.shape[-1] if scales.dim() else 0
+    K = scales.shape[-1] * 32
+    if packed.numel() != R * K // 2 or absmax.numel() != R * (K // 64):
+        raise ValueError("packed / absmax do not match the MXFP4 stack's size")
+    _check(_lib.moe4_convert_mxfp4_nf4(_ptr(blocks, _U8, "blocks"), _ptr(scales, _U8, "scales"),
+                                       R, K, _ptr(packed, _U8, "packed"),
+                                       _ptr(absmax, _F32, "absmax"), _stream(stream)))
 
 
 def moe4_route(logits, k, topk_idx, topk_w, renormalize=True, stream=None):

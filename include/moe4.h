@@ -149,6 +149,21 @@ int moe4_decode_mxfp4(const uint8_t* blocks, const uint8_t* scales, int64_t R, i
                       uint16_t* out, void* stream);
 
 /*
+ * MXFP4 -> NF4 re-quantisation of a stack in one pass [MXFP4 page, "Two
+ * fidelity paths": the convenient QLoRA path decodes the released blocks
+ * exactly and quantises the decoded stack to NF4]. Computes exactly
+ * moe4_quantize_nf4 applied to the moe4_decode_mxfp4 output read as fp32, row
+ * by row, so NF4 block q of a row covers MXFP4 blocks 2q and 2q + 1. Scale
+ * bytes up to 252 always decode to finite values; for a block that decodes to
+ * inf or NaN (bytes 253..255) the output is unspecified.
+ *   blocks u8 [R, K/32, 16] (16-byte aligned), scales u8 [R, K/32]
+ *   packed u8 [R, K/2] out (16-byte aligned), absmax f32 [R, K/64] out
+ *   K % 64 == 0 (else MOE4_ESHAPE)
+ */
+int moe4_convert_mxfp4_nf4(const uint8_t* blocks, const uint8_t* scales, int64_t R, int64_t K,
+                           uint8_t* packed, float* absmax, void* stream);
+
+/*
  * Top-k routing on given fp32 router logits. Per token: the k largest logits
  * (equal logits -> lower expert index; +0 == -0), output in that order;
  * weights = softmax over all E restricted to the k and, if renormalize != 0,

@@ -56,6 +56,12 @@ def test_quantize_refusals():
 def test_decode_route_combine_refusals():
     assert lib.moe4_decode_mxfp4(FAKE, FAKE, 4, 48, FAKE, None) == moe4.MOE4_ESHAPE
     assert lib.moe4_decode_mxfp4(FAKE, FAKE, 4, 64, FAKE_MIS, None) == moe4.MOE4_EALIGN
+    assert lib.moe4_convert_mxfp4_nf4(FAKE, FAKE, 4, 96, FAKE, FAKE, None) == moe4.MOE4_ESHAPE
+    assert "multiple of 64" in moe4.moe4_last_error()
+    assert lib.moe4_convert_mxfp4_nf4(FAKE, FAKE, -1, 64, FAKE, FAKE, None) == moe4.MOE4_ESHAPE
+    assert lib.moe4_convert_mxfp4_nf4(FAKE, FAKE, 4, 64, FAKE_MIS, FAKE, None) == moe4.MOE4_EALIGN
+    assert lib.moe4_convert_mxfp4_nf4(None, FAKE, 4, 64, FAKE, FAKE, None) == moe4.MOE4_EINVAL
+    assert lib.moe4_convert_mxfp4_nf4(None, None, 0, 64, None, None, None) == moe4.MOE4_OK
     assert lib.moe4_route(FAKE, 4, 8, 9, 1, FAKE, FAKE, None) == moe4.MOE4_ESHAPE
     assert lib.moe4_route(FAKE, 4, 2000, 2, 1, FAKE, FAKE, None) == moe4.MOE4_ESHAPE
     assert lib.moe4_route(FAKE, (1 << 28), 128, 8, 1, FAKE, FAKE, None) == moe4.MOE4_ESHAPE

@@ -164,6 +164,22 @@ def test_gpt_oss_20b_decode_stack_bit_exact(gptoss_layer):
         assert np.array_equal(bits(out[e][rows]), oracle.decode_mxfp4_bf16(q[e][rows], s[e][rows]))
 
 
+def test_gpt_oss_20b_convert_to_nf4_bit_exact(gptoss_layer):
+    say("MXFP4 -> NF4 conversion of the full gpt-oss-20b-shaped gate_up and down stacks")
+    for q, s in ((gptoss_layer.q[0], gptoss_layer.q[1]), (gptoss_layer.q[2], gptoss_layer.q[3])):
+        E, R, nb = s.shape
+        packed = torch.empty((E, R, nb * 16), dtype=torch.uint8, device=DEV)
+        absmax = torch.empty((E, R, nb // 2), dtype=torch.float32, device=DEV)
+        moe4.moe4_convert_mxfp4_nf4(to_dev(q), to_dev(s), packed, absmax)
+        torch.cuda.synchronize()
+        rows = np.random.default_rng(4).choice(R, 96, replace=False)
+        for e in range(E):   # sampled rows of every expert, one whole expert
+            sel = slice(None) if e == 5 else rows
+            rp, ra = oracle.convert_mxfp4_to_nf4(q[e][sel], s[e][sel])
+            assert np.array_equal(packed[e][sel].cpu().numpy(), rp)
+            assert np.array_equal(absmax[e][sel].cpu().numpy().view(np.uint32), ra.view(np.uint32))
+
+
 @pytest.mark.parametrize("T", [1, 8, 32])
 def test_gpt_oss_120b_stack_layer_full(T):
     spec = inp.GPT_OSS_120B_STACK

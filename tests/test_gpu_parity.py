@@ -101,6 +101,46 @@ def test_quantize_nf4_tiny_stack_matches_oracle_stack():
             assert np.array_equal(absmax.cpu().numpy(), s.reshape(-1))
 
 
+def _convert(blocks, scales):
+    R, nb = scales.shape
+    packed = torch.empty((R, nb * 16), dtype=torch.uint8, device=DEV)
+    absmax = torch.empty((R, nb // 2), dtype=torch.float32, device=DEV)
+    moe4.moe4_convert_mxfp4_nf4(to_dev(blocks), to_dev(scales), packed, absmax)
+    torch.cuda.synchronize()
+    return packed.cpu().numpy(), absmax.cpu().numpy()
+
+
+def test_convert_mxfp4_nf4_bit_exact():
+    say("convert_mxfp4_nf4: gpt-oss-shaped small stack, wide scale spreads, zero blocks")
+    L = layer_of(GPTOSS_SMALL)
+    # K = 352 there: take 10 of the 11 blocks per row (K % 64 == 0)
+    cases = [(L.gu_q[:, :, :10], L.gu_s[:, :, :10]), (L.dn_q[:, :37, 3:], L.dn_s[:, :37, 3:]),
+             (L.dn_q[:, :, :2], L.dn_s[:, :, :2])]
+    rng = np.random.default_rng(21)
+    R, nb = 300, 90
+    blocks = rng.integers(0, 256, (R, nb, 16), dtype=np.uint8)
+    blocks[::7] &= rng.choice(np.array([0, 0x0F, 0xF0, 0x88, 0x11], np.uint8), (43, nb, 16))
+    blocks[5, 10:12] = 0
+    blocks[6, 20:22] = 0x88
+    scales = rng.integers(0, 253, (R, nb), dtype=np.uint8)
+    scales[100:200, 1::2] = np.clip(scales[100:200, 0::2].astype(int)
+                                    - rng.integers(0, 12, (100, nb // 2)), 0, 252)
+    scales[200:220] = rng.integers(0, 3, (20, nb), dtype=np.uint8)   # subnormal decodes
+    cases.append((blocks, scales))
+    for q, s in cases:
+        q = np.ascontiguousarray(q).reshape(-1, q.shape[-2], 16)
+        s = np.ascontiguousarray(s).reshape(-1, s.shape[-1])
+        gp, ga = _convert(q, s)
+        rp, ra = oracle.convert_mxfp4_to_nf4(q, s)
+        assert np.array_equal(ga.view(np.uint32), ra.view(np.uint32))
+        assert np.array_equal(gp, rp)
+    # R = 0 is a no-op
+    moe4.moe4_convert_mxfp4_nf4(torch.empty((0, 2, 16), dtype=torch.uint8, device=DEV),
+                                torch.empty((0, 2), dtype=torch.uint8, device=DEV),
+                                torch.empty((0, 32), dtype=torch.uint8, device=DEV),
+                                torch.empty((0, 1), dtype=torch.float32, device=DEV))
+
+
 # ------------------------------------------------------------------ routing
 
 def _route(lg, k, renorm=True):
