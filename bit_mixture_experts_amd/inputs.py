@@ -26,6 +26,7 @@ import numpy as np
 # tensor identifiers inside a seed path
 _X, _LOGITS, _W_GU, _W_DN, _GU_BLK, _GU_SCL, _DN_BLK, _DN_SCL = 1, 2, 3, 4, 5, 6, 7, 8
 _B_GU, _B_DN, _LORA_A, _LORA_B, _DOUT, _ZIPF = 9, 10, 11, 12, 13, 14
+_W_ROUTER, _Y_SLOTS = 15, 16
 
 
 @dataclass(frozen=True)
@@ -164,6 +165,20 @@ def host_tokens(spec, T, layer=0, seed=0):
     return to_bf16_bits(x), lg
 
 
+def host_router(spec, layer=0, seed=0):
+    """Router weights W_r bf16 bits [E,H] ~ N(0, 1/H) (so that x W_r^T ~ N(0,1)
+    for x ~ N(0,1)) and the fp32 router bias [E] (the Zipf skew, else zeros)."""
+    w = _rng(seed, spec, layer, _W_ROUTER, 0).standard_normal((spec.E, spec.H),
+                                                              dtype=np.float32)
+    return to_bf16_bits(w * np.float32(1.0 / np.sqrt(spec.H))), host_zipf_bias(spec, layer, seed)
+
+
+def host_slot_outputs(spec, T, layer=0, seed=0):
+    """fp32 [T*k, H] ~ N(0,1): stand-in expert outputs, one row per routed slot."""
+    return _rng(seed, spec, layer, _Y_SLOTS, T).standard_normal((T * spec.k, spec.H),
+                                                                dtype=np.float32)
+
+
 def host_upstream_grad(spec, T, layer=0, seed=0):
     """bf16 bits [T,H] ~ N(0,1): the gradient arriving at the layer output."""
     d = _rng(seed, spec, layer, _DOUT, T).standard_normal((T, spec.H), dtype=np.float32)
@@ -228,6 +243,14 @@ def device_bf16(shape, std, seed, spec, *path, device="cuda"):
     g = device_generator(seed, spec, *path, device=device)
     return (torch.randn(shape, generator=g, device=device, dtype=torch.float32)
             .mul_(std).to(torch.bfloat16))
+
+
+def device_router(spec, layer=0, seed=0, device="cuda"):
+    """(W_r bf16 [E,H] ~ N(0, 1/H), bias fp32 [E]) on device."""
+    import torch
+    w = device_bf16((spec.E, spec.H), 1.0 / spec.H ** 0.5, seed, spec, layer, _W_ROUTER,
+                    device=device)
+    return w, torch.from_numpy(host_zipf_bias(spec, layer, seed)).to(device)
 
 
 def device_tokens(spec, T, layer=0, seed=0, device="cuda"):

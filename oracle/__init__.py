@@ -41,6 +41,8 @@ from .formats import (NF4_LEVELS, nf4_midpoints, quantize_nf4, dequantize_nf4,
                       dequantize_nf4_bf16, E2M1_MAGNITUDES, mxfp4_values, decode_mxfp4_bf16,
                       convert_mxfp4_to_nf4)
 from .routing import route, permute, gather_rows
+from .router import (router_logits, router_logits_error_bound, routing_weight_grad,
+                     routing_logit_grad)
 from .layer import (ExpertWeights, gate_up, activation, down, combine,
                     layer_forward, layer_backward, token_forward)
 
@@ -49,6 +51,7 @@ __all__ = [
     "NF4_LEVELS", "nf4_midpoints", "quantize_nf4", "dequantize_nf4", "dequantize_nf4_bf16",
     "E2M1_MAGNITUDES", "mxfp4_values", "decode_mxfp4_bf16", "convert_mxfp4_to_nf4",
     "route", "permute", "gather_rows",
+    "router_logits", "router_logits_error_bound", "routing_weight_grad", "routing_logit_grad",
     "ExpertWeights", "gate_up", "activation", "down", "combine",
     "layer_forward", "layer_backward", "token_forward",
 ]
