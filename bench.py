@@ -354,6 +354,54 @@ def bench_convert(torch, hip, moe4, inputs, spec, steps, warmup, seed, nrep=2):
             "hbm_frac": round(gbps / HBM_PEAK_GBS, 4)}
 
 
+def bench_router(torch, hip, moe4, inputs, spec, T, steps, warmup, seed):
+    """Router step at the layer's shape: logits (x W_r^T, fp32) and the routing
+    backward (dw and d logits from dOut and the slots' expert outputs)."""
+    stream = torch.cuda.current_stream().cuda_stream
+    x, _ = inputs.device_tokens(spec, T, seed=seed + 31)
+    wr, rb = inputs.device_router(spec, seed=seed)
+    E, k, H = spec.E, spec.k, spec.H
+    lg = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=x.device)
+    sor = torch.empty(T * k, dtype=torch.int32, device=x.device)
+    ros = torch.empty(T * k, dtype=torch.int32, device=x.device)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=x.device)
+    moe4.moe4_router_logits(x, wr, lg)
+    moe4.moe4_route(lg, k, idx, w)
+    moe4.moe4_permute(idx, E, offsets, sor, ros, ws=ws)
+    y = inputs.device_bf16((T * k, H), 1.0, seed, spec, 0, 16).float()
+    dout = inputs.device_bf16((T, H), 1.0, seed, spec, 0, 13)
+    dw = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    dl = torch.empty((T, E), dtype=torch.float32, device=x.device)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = hip.events(2 * steps)
+        for i in range(steps):
+            hip.record(ev[2 * i], stream)
+            fn()
+            hip.record(ev[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        ms = sorted(hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(steps))
+        return ms[len(ms) // 2]
+
+    f_ms = timed(lambda: moe4.moe4_router_logits(x, wr, lg))
+    b_ms = timed(lambda: moe4.moe4_route_backward(idx, w, dout, y, ros, dw, dl))
+    f_bytes = T * H * 2 + E * H * 2 + T * E * 4
+    b_bytes = T * k * H * 4 + T * H * 2 + T * k * 12 + T * E * 4
+    return {"workload": f"{spec.name} router step", "T": T,
+            "logits_us": round(f_ms * 1e3, 2),
+            "logits_tflops": round(2.0 * T * E * H / (f_ms * 1e-3) / 1e12, 2),
+            "logits_GBps": round(f_bytes / (f_ms * 1e-3) / 1e9, 1),
+            "route_backward_us": round(b_ms * 1e3, 2),
+            "route_backward_GBps": round(b_bytes / (b_ms * 1e-3) / 1e9, 1),
+            "route_backward_hbm_frac": round(b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 # -------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(spec, T_batch, n_tokens, seed=0):
@@ -489,7 +537,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
-    ap.add_argument("--only", default="", help="comma list of sweep parts: qwen,gptoss,lora,convert,stack")
+    ap.add_argument("--only", default="", help="comma list of sweep parts: qwen,gptoss,lora,router,convert,stack")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run the copy kernel of known size (for PMC scaling)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -565,6 +613,11 @@ def main():
             log("sweep:", json.dumps(r))
             sweep.append(r)
             del mex
+        if not only or "router" in only:
+            r = bench_router(torch, hip, moe4, inputs, spec, HEADLINE_T, reps, args.warmup,
+                             args.seed)
+            log("sweep:", json.dumps(r))
+            sweep.append(r)
         if not only or "convert" in only:
             r = bench_convert(torch, hip, moe4, inputs, inputs.GPT_OSS_20B_MXFP4, reps,
                               args.warmup, args.seed)

@@ -18,6 +18,14 @@ hipError_t launch_decode_mxfp4(const uint8_t* blocks, const uint8_t* scales, int
 hipError_t launch_convert_mxfp4_nf4(const uint8_t* blocks, const uint8_t* scales, int64_t R,
                                     int64_t K, uint8_t* packed, float* absmax, hipStream_t s);
 
+// ---- router step
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
+                                int H, int E, float* logits, hipStream_t s);
+hipError_t launch_route_backward(const int32_t* idx, const float* tw, const float* lg,
+                                 int renorm, const uint16_t* dout, const float* y,
+                                 const int32_t* row_of_slot, int T, int k, int E, int H,
+                                 float* dw, float* dlog, hipStream_t s);
+
 // ---- routing / permutation / combine
 hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, int32_t* idx,
                         float* w, hipStream_t s);

@@ -187,6 +187,56 @@ int moe4_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t ren
                   "moe4_route");
 }
 
+int moe4_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int32_t T,
+                       int32_t H, int32_t E, float* logits, void* stream) {
+  if (E < 1 || E > 1024) return fail(MOE4_ESHAPE, "E = %d outside [1, 1024]", E);
+  if (H <= 0 || H % 8 || H >= (1 << 25))
+    return fail(MOE4_ESHAPE, "H = %d must be a positive multiple of 8 below 2^25", H);
+  if (T < 0) return fail(MOE4_ESHAPE, "T = %d is negative", T);
+  if (T == 0) return ok();
+  REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(wr, "wr");
+  REQUIRE_PTR(logits, "logits");
+  REQUIRE_ALIGN(x, 16, "x");
+  REQUIRE_ALIGN(wr, 16, "wr");
+  REQUIRE_ALIGN(bias, 4, "bias");
+  REQUIRE_ALIGN(logits, 4, "logits");
+  return launched(moe4::launch_router_logits(x, wr, bias, T, H, E, logits, (hipStream_t)stream),
+                  "moe4_router_logits");
+}
+
+int moe4_route_backward(const int32_t* topk_idx, const float* topk_w, const float* logits,
+                        int32_t renormalize, const uint16_t* dout, const float* y_perm,
+                        const int32_t* row_of_slot, int32_t T, int32_t k, int32_t E, int32_t H,
+                        float* dw, float* dlogits, void* stream) {
+  if (E < 1 || E > 1024) return fail(MOE4_ESHAPE, "E = %d outside [1, 1024]", E);
+  if (k < 1 || k > E) return fail(MOE4_ESHAPE, "k = %d outside [1, E = %d]", k, E);
+  if (T < 0 || (int64_t)T * k >= ((int64_t)1 << 31))
+    return fail(MOE4_ESHAPE, "T = %d: need T >= 0 and T*k < 2^31", T);
+  if (H <= 0 || H % 8) return fail(MOE4_ESHAPE, "H = %d must be a positive multiple of 8", H);
+  if (!renormalize && T > 0) REQUIRE_PTR(logits, "logits (needed without renormalisation)");
+  if (T == 0) return ok();
+  REQUIRE_PTR(topk_idx, "topk_idx");
+  REQUIRE_PTR(topk_w, "topk_w");
+  REQUIRE_PTR(dout, "dout");
+  REQUIRE_PTR(y_perm, "y_perm");
+  REQUIRE_PTR(row_of_slot, "row_of_slot");
+  REQUIRE_PTR(dw, "dw");
+  REQUIRE_PTR(dlogits, "dlogits");
+  REQUIRE_ALIGN(dout, 16, "dout");
+  REQUIRE_ALIGN(y_perm, 16, "y_perm");
+  REQUIRE_ALIGN(topk_idx, 4, "topk_idx");
+  REQUIRE_ALIGN(topk_w, 4, "topk_w");
+  REQUIRE_ALIGN(logits, 4, "logits");
+  REQUIRE_ALIGN(row_of_slot, 4, "row_of_slot");
+  REQUIRE_ALIGN(dw, 4, "dw");
+  REQUIRE_ALIGN(dlogits, 4, "dlogits");
+  return launched(moe4::launch_route_backward(topk_idx, topk_w, logits, renormalize != 0, dout,
+                                              y_perm, row_of_slot, T, k, E, H, dw, dlogits,
+                                              (hipStream_t)stream),
+                  "moe4_route_backward");
+}
+
 int moe4_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t* offsets,
                  int32_t* slot_of_row, int32_t* row_of_slot, const uint16_t* x,
                  const float* row_scale, int32_t H, uint16_t* x_perm, void* ws, size_t ws_bytes,

@@ -29,8 +29,8 @@ MOE4_VARIANT_AUTO, MOE4_VARIANT_SKINNY, MOE4_VARIANT_TILED = 0, 1, 2
 MOE4_DTYPE_BF16, MOE4_DTYPE_F32 = 1, 2
 
 # every symbol declared in include/moe4.h
-EXPORTS = ("moe4_quantize_nf4", "moe4_decode_mxfp4", "moe4_convert_mxfp4_nf4", "moe4_route",
-           "moe4_permute",
+EXPORTS = ("moe4_quantize_nf4", "moe4_decode_mxfp4", "moe4_convert_mxfp4_nf4",
+           "moe4_router_logits", "moe4_route", "moe4_route_backward", "moe4_permute",
            "moe4_expert_forward", "moe4_combine", "moe4_expert_backward",
            "moe4_workspace_size", "moe4_set_timing_events", "moe4_last_error",
            "moe4_last_variant")
@@ -58,6 +58,9 @@ _SIGS = {
     "moe4_decode_mxfp4": ([_vp, _vp, _i64, _i64, _vp, _vp], ctypes.c_int),
     "moe4_convert_mxfp4_nf4": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "moe4_route": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "moe4_router_logits": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "moe4_route_backward": ([_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp,
+                             _vp, _vp], ctypes.c_int),
     "moe4_permute": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
                      ctypes.c_int),
     "moe4_expert_forward": ([_P, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -180,6 +183,32 @@ def moe4_route(logits, k, topk_idx, topk_w, renormalize=True, stream=None):
     _check(_lib.moe4_route(_ptr(logits, _F32, "logits"), T, E, k, int(bool(renormalize)),
                            _ptr(topk_idx, _I32, "topk_idx"), _ptr(topk_w, _F32, "topk_w"),
                            _stream(stream)))
+
+
+def moe4_router_logits(x, wr, logits, bias=None, stream=None):
+    """x bf16 [T, H], wr bf16 [E, H], bias f32 [E] or None -> logits f32 [T, E]."""
+    T, H = x.shape
+    E = wr.shape[0]
+    if wr.shape[1] != H or tuple(logits.shape) != (T, E):
+        raise ValueError("router_logits: x [T,H], wr [E,H] and logits [T,E] do not agree")
+    _check(_lib.moe4_router_logits(_ptr(x, _BF16, "x"), _ptr(wr, _BF16, "wr"),
+                                   _ptr(bias, _F32, "bias"), T, H, E,
+                                   _ptr(logits, _F32, "logits"), _stream(stream)))
+
+
+def moe4_route_backward(topk_idx, topk_w, dout, y_perm, row_of_slot, dw, dlogits,
+                        logits=None, renormalize=True, stream=None):
+    """dw f32 [T, k] and dlogits f32 [T, E] from the upstream gradient dout
+    bf16 [T, H] and the slots' expert outputs y_perm f32 [T*k, H]."""
+    T, k = topk_idx.shape
+    E = dlogits.shape[1]
+    H = dout.shape[1]
+    _check(_lib.moe4_route_backward(_ptr(topk_idx, _I32, "topk_idx"), _ptr(topk_w, _F32, "topk_w"),
+                                    _ptr(logits, _F32, "logits"), int(bool(renormalize)),
+                                    _ptr(dout, _BF16, "dout"), _ptr(y_perm, _F32, "y_perm"),
+                                    _ptr(row_of_slot, _I32, "row_of_slot"), T, k, E, H,
+                                    _ptr(dw, _F32, "dw"), _ptr(dlogits, _F32, "dlogits"),
+                                    _stream(stream)))
 
 
 def moe4_permute(topk_idx, E, offsets, slot_of_row, row_of_slot, x=None, row_scale=None,

@@ -175,6 +175,41 @@ int moe4_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t ren
                int32_t* topk_idx, float* topk_w, void* stream);
 
 /*
+ * Router logits, the step in front of moe4_route [experts4bit-qlora page,
+ * "Current measured position": rounding flips router top-k choices between
+ * arithmetically equivalent forwards, so routing is compared against a
+ * measured floor]: logits[t, e] = sum_h x[t, h] * wr[e, h] (+ bias[e]),
+ * products of bf16 values summed in fp32 (MFMA, order unspecified; each
+ * logit is within the fp32 dot-product bound gamma_H * sum |x w| of the exact
+ * sum).
+ *   x bf16 [T, H], wr bf16 [E, H] (both 16-byte aligned); bias f32 [E] or NULL
+ *   logits f32 [T, E] out; 1 <= E <= 1024; H a positive multiple of 8 below 2^25
+ */
+int moe4_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int32_t T,
+                       int32_t H, int32_t E, float* logits, void* stream);
+
+/*
+ * Backward of the routing weights [same page and section]. With
+ * out[t] = sum_j w[t, j] * y_perm[row_of_slot[t*k + j]], given the upstream
+ * gradient dOut:
+ *   dw[t, j] = <dOut[t], y_perm[row_of_slot[t*k + j]]>   (fp32 sums)
+ *   dlogits[t, e]: renormalize != 0 (weights = softmax of the k chosen
+ *   logits): w[t, j] * (dw[t, j] - sum_i w[t, i] dw[t, i]) for e = topk_idx[t, j],
+ *   0 for experts not chosen; renormalize == 0 (weights = the full softmax p of
+ *   `logits`): p[t, e] * (g[t, e] - sum_i w[t, i] dw[t, i]), g = dw at the
+ *   chosen experts, 0 elsewhere. The top-k choice itself has no gradient.
+ *   topk_idx i32 [T, k] (distinct experts in [0, E) per token, as moe4_route
+ *   writes them; otherwise the output is unspecified), topk_w f32 [T, k]
+ *   logits f32 [T, E] (read only when renormalize == 0, then required)
+ *   dout bf16 [T, H], y_perm f32 [T*k, H] (16-byte aligned), row_of_slot i32 [T*k]
+ *   dw f32 [T, k] out, dlogits f32 [T, E] out; H % 8 == 0
+ */
+int moe4_route_backward(const int32_t* topk_idx, const float* topk_w, const float* logits,
+                        int32_t renormalize, const uint16_t* dout, const float* y_perm,
+                        const int32_t* row_of_slot, int32_t T, int32_t k, int32_t E, int32_t H,
+                        float* dw, float* dlogits, void* stream);
+
+/*
  * Stable permutation of the T*k routed slots (s = t*k + j) by expert, plus the
  * row gather. Rows of expert e are offsets[e] .. offsets[e+1]-1, in ascending
  * slot order. x_perm[r] = x[slot_of_row[r] / k], or with row_scale,

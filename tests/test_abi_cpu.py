@@ -72,6 +72,25 @@ def test_decode_route_combine_refusals():
     assert "out_dtype unset" in moe4.moe4_last_error()
 
 
+def test_router_refusals():
+    r = lib.moe4_router_logits
+    assert r(FAKE, FAKE, None, 4, 64, 0, FAKE, None) == moe4.MOE4_ESHAPE
+    assert r(FAKE, FAKE, None, 4, 60, 8, FAKE, None) == moe4.MOE4_ESHAPE
+    assert "multiple of 8" in moe4.moe4_last_error()
+    assert r(FAKE_MIS, FAKE, None, 4, 64, 8, FAKE, None) == moe4.MOE4_EALIGN
+    assert r(FAKE, None, None, 4, 64, 8, FAKE, None) == moe4.MOE4_EINVAL
+    assert r(None, None, None, 0, 64, 8, None, None) == moe4.MOE4_OK
+    b = lib.moe4_route_backward
+    args = [FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 4, 2, 8, 64, FAKE, FAKE, None]
+    assert b(*args[:7], 4, 9, 8, 64, *args[11:]) == moe4.MOE4_ESHAPE          # k > E
+    assert b(*args[:7], 4, 2, 8, 36, *args[11:]) == moe4.MOE4_ESHAPE         # H % 8
+    assert b(FAKE, FAKE, None, 0, *args[4:]) == moe4.MOE4_EINVAL              # logits needed
+    assert "renormalisation" in moe4.moe4_last_error()
+    assert b(*args[:4], FAKE_MIS, *args[5:]) == moe4.MOE4_EALIGN              # dout
+    assert b(*args[:11], None, FAKE, None) == moe4.MOE4_EINVAL                # dw
+    assert b(None, None, None, 1, None, None, None, 0, 2, 8, 64, None, None, None) == moe4.MOE4_OK
+
+
 def test_permute_refusals():
     # row_scale without x, undersized workspace for a large permutation
     assert lib.moe4_permute(FAKE, 4, 2, 8, FAKE, FAKE, FAKE, None, FAKE, 0, None, None, 0,

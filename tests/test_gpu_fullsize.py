@@ -180,6 +180,50 @@ def test_gpt_oss_20b_convert_to_nf4_bit_exact(gptoss_layer):
             assert np.array_equal(absmax[e][sel].cpu().numpy().view(np.uint32), ra.view(np.uint32))
 
 
+@pytest.mark.parametrize("spec,T,layer", [(inp.QWEN3_30B_NF4, 4096, 0),
+                                           (inp.GPT_OSS_120B_STACK, 32, 7)],
+                         ids=["qwen3_T4096", "gpt_oss_120b_T32"])
+def test_router_step_full(spec, T, layer):
+    """Router logits at the layer's real shape (with the Zipf router bias of
+    the 120b stack), the routing-flip floor against the exact logits, and the
+    routing backward on the same tokens."""
+    say(f"router step: {spec.name}, T={T}")
+    x, _ = inp.host_tokens(spec, T, layer)
+    wr, rb = inp.host_router(spec, layer)
+    bias = rb if spec.zipf else None
+    lg = torch.empty((T, spec.E), dtype=torch.float32, device=DEV)
+    moe4.moe4_router_logits(to_dev(x), to_dev(wr), lg, bias=None if bias is None else to_dev(bias))
+    torch.cuda.synchronize()
+    got = lg.cpu().numpy()
+    exact = oracle.router_logits(x, wr, bias)
+    bound = oracle.router_logits_error_bound(x, wr, bias)
+    err = np.abs(got.astype(np.float64) - exact)
+    say(f"  logits: max|err| = {err.max():.3e}, max err/bound = {(err / bound).max():.3e}")
+    assert np.all(err <= bound)
+    k = spec.k
+    gi, gw = oracle.route(got, k)
+    ei, _ = oracle.route(exact.astype(np.float32), k)
+    flips = np.array([set(gi[t]) != set(ei[t]) for t in range(T)])
+    srt = -np.sort(-exact, axis=1)
+    gap = srt[:, k - 1] - srt[:, k]
+    say(f"  routing-flip floor (GPU fp32 logits vs exact): {int(flips.sum())} of {T} tokens "
+        f"({flips.mean():.2e}); smallest top-k gap {gap.min():.2e}")
+    assert np.all(gap[flips] <= 2 * bound.max())
+    # backward on stand-in expert outputs, routed by the GPU's own logits
+    _, _, row_of_slot = oracle.permute(gi, spec.E)
+    y = inp.host_slot_outputs(spec, T, layer)
+    dout = inp.host_upstream_grad(spec, T, layer)
+    dw = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    dl = torch.empty((T, spec.E), dtype=torch.float32, device=DEV)
+    moe4.moe4_route_backward(to_dev(gi), to_dev(gw.astype(np.float32)), to_dev(dout), to_dev(y),
+                             to_dev(row_of_slot), dw, dl)
+    torch.cuda.synchronize()
+    dw_ref = oracle.routing_weight_grad(dout, y, row_of_slot, k)
+    dl_ref = oracle.routing_logit_grad(gi, gw, dw_ref, spec.E)
+    assert_close(dw.cpu().numpy(), dw_ref, "dw")
+    assert_close(dl.cpu().numpy(), dl_ref, "dlogits")
+
+
 @pytest.mark.parametrize("T", [1, 8, 32])
 def test_gpt_oss_120b_stack_layer_full(T):
     spec = inp.GPT_OSS_120B_STACK

@@ -141,6 +141,102 @@ def test_convert_mxfp4_nf4_bit_exact():
                                 torch.empty((0, 1), dtype=torch.float32, device=DEV))
 
 
+# --------------------------------------------------------------- router step
+
+def router_case(T, E, H, seed, bias=True):
+    rng = np.random.default_rng(seed)
+    xb = inp.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wb = inp.to_bf16_bits((rng.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32))
+    b = rng.standard_normal(E).astype(np.float32) if bias else None
+    return xb, wb, b
+
+
+def gpu_router_logits(xb, wb, b):
+    T, E = xb.shape[0], wb.shape[0]
+    lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    moe4.moe4_router_logits(to_dev(xb), to_dev(wb), lg, bias=None if b is None else to_dev(b))
+    torch.cuda.synchronize()
+    return lg.cpu().numpy()
+
+
+def check_router_logits(xb, wb, b):
+    """GPU logits within the fp32 dot-product bound of the exact sums; routing
+    on them equal to routing on the rounded exact logits except where the
+    exact gap at the top-k boundary is within the bound. Returns the flip
+    fraction."""
+    got = gpu_router_logits(xb, wb, b)
+    exact = oracle.router_logits(xb, wb, b)
+    bound = oracle.router_logits_error_bound(xb, wb, b)
+    err = np.abs(got.astype(np.float64) - exact)
+    say(f"  logits: max|err| = {err.max():.3e}, max err/bound = {(err / bound).max():.3e}")
+    assert np.all(err <= bound)
+    return got, exact, bound
+
+
+@pytest.mark.parametrize("T,E,H", [(100, 40, 264), (37, 8, 256), (300, 128, 2048), (5, 1024, 64)])
+def test_router_logits_within_fp32_bound(T, E, H):
+    say(f"router_logits T={T} E={E} H={H}")
+    xb, wb, b = router_case(T, E, H, seed=T + E + H)
+    check_router_logits(xb, wb, b)
+    check_router_logits(xb, wb, None)
+
+
+def test_router_route_flip_floor_small():
+    say("router -> route: flips only where the exact top-k gap is within the bound")
+    T, E, H, k = 512, 128, 2048, 8
+    xb, wb, b = router_case(T, E, H, seed=77, bias=False)
+    got, exact, bound = check_router_logits(xb, wb, b)
+    gi, _ = oracle.route(got, k)
+    ei, _ = oracle.route(exact.astype(np.float32), k)
+    srt = -np.sort(-exact, axis=1)
+    gap = srt[:, k - 1] - srt[:, k]
+    flips = np.array([set(gi[t]) != set(ei[t]) for t in range(T)])
+    say(f"  flipped tokens: {int(flips.sum())} of {T}")
+    assert np.all(gap[flips] <= 2 * bound.max())
+    # the GPU's own route of its logits is bit-exact with the oracle's route of
+    # the same logits (the rule is exact on given fp32 logits)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    moe4.moe4_route(to_dev(got), k, idx, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), gi)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+@pytest.mark.parametrize("T,E,k,H", [(64, 8, 2, 256), (150, 128, 8, 2048), (9, 32, 4, 2880),
+                                     (3, 1024, 70, 64)])
+def test_route_backward(T, E, k, H, renorm):
+    say(f"route_backward T={T} E={E} k={k} H={H} renorm={renorm}")
+    spec = inp.QWEN3_30B_NF4.scaled(name="route_bwd", seed_id=106, E=E, k=k, H=H)
+    _, lg = inp.host_tokens(spec, T)
+    ri, rw = oracle.route(lg, k, renormalize=renorm)
+    _, slot_of_row, row_of_slot = oracle.permute(ri, E)
+    y = inp.host_slot_outputs(spec, T)          # expert outputs in permuted-row order
+    dout = inp.host_upstream_grad(spec, T)
+    dw_ref = oracle.routing_weight_grad(dout, y, row_of_slot, k)
+    dl_ref = oracle.routing_logit_grad(ri, rw, dw_ref, E, renormalize=renorm, logits=lg)
+    dw = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    dl = torch.full((T, E), float("nan"), dtype=torch.float32, device=DEV)
+    moe4.moe4_route_backward(to_dev(ri.astype(np.int32)), to_dev(rw.astype(np.float32)),
+                             to_dev(dout), to_dev(y), to_dev(row_of_slot), dw, dl,
+                             logits=to_dev(lg), renormalize=renorm)
+    torch.cuda.synchronize()
+    gdw, gdl = dw.cpu().numpy(), dl.cpu().numpy()
+    # dw: fp32 sums of H fp32 products, each product rounded once
+    d = np.abs(oracle.bf16_bits_to_f64(dout))
+    mag = np.einsum("th,tjh->tj", d, np.abs(y.astype(np.float64))[row_of_slot.reshape(T, k)])
+    n = H + 1
+    bound = (n * 2.0 ** -24 / (1 - n * 2.0 ** -24) + 2.0 ** -24) * mag
+    assert np.all(np.abs(gdw - dw_ref) <= bound)
+    assert_close(gdw, dw_ref, "dw")
+    assert_close(gdl, dl_ref, "dlogits")
+    assert np.max(np.abs(gdl - dl_ref)) <= 1e-4 * np.sqrt(np.mean(dl_ref ** 2))
+    if renorm:   # experts that were not chosen get exactly zero
+        mask = np.ones((T, E), bool)
+        np.put_along_axis(mask, ri.astype(np.int64), False, 1)
+        assert np.all(gdl[mask] == 0)
+
+
 # ------------------------------------------------------------------ routing
 
 def _route(lg, k, renorm=True):
