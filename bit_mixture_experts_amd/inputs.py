@@ -90,6 +90,24 @@ GPT_OSS_20B_MXFP4_LORA = LayerSpec("gpt_oss_20b_mxfp4_lora_r8", 6, "mxfp4", E=32
                                    act="swiglu_clamped", bias=True, lora_r=8, lora_alpha=16.0)
 
 
+def dq_code_book(kind="dynamic"):
+    """A 256-entry, strictly increasing fp32 code book for double-quantised
+    absmax (the pages name an 8-bit code book but print none; this one is our
+    own construction). "dynamic": 0, +-1 and, per octave [2^-(e+1), 2^-e) for
+    e = 0..7, sixteen evenly spaced values (finer steps near zero), trimmed to
+    128 positive and 127 negative entries. "linear": 256 evenly spaced values
+    from -1 to 1."""
+    if kind == "linear":
+        return (np.arange(256, dtype=np.float64) * (2.0 / 255.0) - 1.0).astype(np.float32)
+    grid = np.array([(16 + f) / 16.0 * 2.0 ** (-e - 1) for e in range(8) for f in range(16)])
+    grid = np.sort(grid)                       # 128 values in [2^-8, 31/32]
+    pos = np.concatenate([grid[1:], [1.0]])    # 128
+    neg = -np.concatenate([grid[2:], [1.0]])   # 127
+    book = np.sort(np.concatenate([neg, [0.0], pos])).astype(np.float32)
+    assert book.shape == (256,) and np.all(np.diff(book.astype(np.float64)) > 0)
+    return book
+
+
 def _rng(seed, spec, *path):
     return np.random.default_rng(np.random.SeedSequence([int(seed), spec.seed_id,
                                                          *[int(p) for p in path]]))

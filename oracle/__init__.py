@@ -39,7 +39,7 @@ published NF4 construction). No function is "parity unpinned".
 from .numerics import bf16_bits_from_f32, bf16_bits_to_f64, bf16_bits_to_f32, bf16_round_f64
 from .formats import (NF4_LEVELS, nf4_midpoints, quantize_nf4, dequantize_nf4,
                       dequantize_nf4_bf16, E2M1_MAGNITUDES, mxfp4_values, decode_mxfp4_bf16,
-                      convert_mxfp4_to_nf4)
+                      convert_mxfp4_to_nf4, dq_midpoints, compress_absmax, expand_absmax)
 from .routing import route, permute, gather_rows
 from .router import (router_logits, router_logits_error_bound, routing_weight_grad,
                      routing_logit_grad)
@@ -50,6 +50,7 @@ __all__ = [
     "bf16_bits_from_f32", "bf16_bits_to_f64", "bf16_bits_to_f32", "bf16_round_f64",
     "NF4_LEVELS", "nf4_midpoints", "quantize_nf4", "dequantize_nf4", "dequantize_nf4_bf16",
     "E2M1_MAGNITUDES", "mxfp4_values", "decode_mxfp4_bf16", "convert_mxfp4_to_nf4",
+    "dq_midpoints", "compress_absmax", "expand_absmax",
     "route", "permute", "gather_rows",
     "router_logits", "router_logits_error_bound", "routing_weight_grad", "routing_logit_grad",
     "ExpertWeights", "gate_up", "activation", "down", "combine",

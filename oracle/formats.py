@@ -181,3 +181,70 @@ def convert_mxfp4_to_nf4(blocks, scales):
     dec = bf16_bits_to_f64(decode_mxfp4_bf16(b, s)).astype(np.float32)
     packed, absmax = quantize_nf4(dec.reshape(-1))
     return packed.reshape(R, nb * 16), absmax.reshape(R, nb // 2)
+
+
+# ------------------------------------------- double-quantised NF4 absmax
+#
+# [experts4bit-qlora page], "Limitations -- qlora-fused-moe-experts", the
+# double-quantised absmax item: a resident NF4 stack may keep its fp32 absmax
+# (one per 64 weights) in a nested form -- one offset, an 8-bit code per
+# absmax and one fp32 scale per 256 absmax values -- at about a quarter of the
+# bytes; the absmax values change (lossy against fp32). Readings, where the
+# page is silent:
+# * offset = the fp32 rounding of the float64 mean of the stack's absmax;
+# * per 256 consecutive absmax values (the last group may be shorter):
+#   d = fp32(absmax - offset), absmax2 = max |d|, x = fp32(d / absmax2)
+#   (x = 0 when absmax2 = 0), code = nearest entry of a 256-entry code book,
+#   decided by the fp32 midpoints of adjacent entries (formed in float64, then
+#   rounded), a value on a midpoint taking the lower code;
+# * the page names the 8-bit code book but prints none: it is an input here
+#   (256 strictly increasing fp32 values), the same on both sides;
+# * decoded absmax = fp32(fp32(book[code] * absmax2) + offset): one fp32
+#   product and one fp32 sum, no fused multiply-add.
+
+DQ_BLOCK = 256
+
+
+def dq_midpoints(book):
+    """The 255 decision thresholds of a code book (fp32)."""
+    t = np.asarray(book, dtype=np.float32).astype(np.float64)
+    if t.shape != (256,) or not np.all(np.diff(t) > 0):
+        raise ValueError("the code book must hold 256 strictly increasing values")
+    return ((t[:-1] + t[1:]) / 2.0).astype(np.float32)
+
+
+def compress_absmax(absmax, book):
+    """fp32 absmax [n] -> (code uint8 [n], absmax2 float32 [ceil(n/256)],
+    offset float32)."""
+    a = np.ascontiguousarray(np.asarray(absmax, dtype=np.float32)).reshape(-1)
+    if not np.all(np.isfinite(a)):
+        raise ValueError("absmax must be finite")
+    mids = dq_midpoints(book)
+    n = a.size
+    if n == 0:
+        return np.zeros(0, np.uint8), np.zeros(0, np.float32), np.float32(0)
+    offset = np.float32(np.mean(a.astype(np.float64)))
+    d = (a - offset).astype(np.float32)                     # fp32 subtraction
+    nb = (n + DQ_BLOCK - 1) // DQ_BLOCK
+    pad = np.zeros(nb * DQ_BLOCK, np.float32)
+    pad[:n] = d
+    blocks = pad.reshape(nb, DQ_BLOCK)
+    a2 = np.max(np.abs(blocks), axis=1).astype(np.float32)
+    safe = np.where(a2 == 0, np.float32(1), a2).astype(np.float32)
+    x = (blocks / safe[:, None]).astype(np.float32)         # IEEE fp32 division
+    x[a2 == 0] = np.float32(0)
+    code = np.zeros(blocks.shape, dtype=np.int64)
+    for m in mids:
+        code += (x > m)
+    return code.reshape(-1)[:n].astype(np.uint8), a2, offset
+
+
+def expand_absmax(code, absmax2, offset, book):
+    """Decoded fp32 absmax [n]: fp32(fp32(book[code] * absmax2[i // 256]) + offset)."""
+    c = np.asarray(code, dtype=np.uint8).reshape(-1)
+    a2 = np.asarray(absmax2, dtype=np.float32).reshape(-1)
+    t = np.asarray(book, dtype=np.float32)
+    if a2.size != (c.size + DQ_BLOCK - 1) // DQ_BLOCK:
+        raise ValueError("absmax2 length does not match the codes")
+    prod = (t[c] * a2[np.arange(c.size) // DQ_BLOCK]).astype(np.float32)
+    return (prod + np.float32(offset)).astype(np.float32)

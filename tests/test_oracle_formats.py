@@ -14,7 +14,9 @@ import torch
 from scipy.stats import norm
 
 from oracle import (NF4_LEVELS, nf4_midpoints, quantize_nf4, dequantize_nf4,
-                    mxfp4_values, decode_mxfp4_bf16, convert_mxfp4_to_nf4)
+                    mxfp4_values, decode_mxfp4_bf16, convert_mxfp4_to_nf4, compress_absmax,
+                    expand_absmax, dq_midpoints)
+from bit_mixture_experts_amd.inputs import dq_code_book
 from oracle.formats import nf4_codes
 from tests.conftest import read_golden
 
@@ -296,3 +298,73 @@ def test_convert_mxfp4_nf4_round_trip_bound_and_refusals():
     bad[0, 0] = 255                       # e8m0 NaN
     with pytest.raises(ValueError):
         convert_mxfp4_to_nf4(blocks, bad)
+
+
+# ------------------------------------------------ double-quantised absmax
+
+def _absmax_sample(rng, n):
+    # absmax of NF4 blocks of N(0, 0.02^2) weights: positive, clustered
+    w = rng.standard_normal((n, 64)).astype(np.float32) * np.float32(0.02)
+    return np.abs(w).max(axis=1).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["dynamic", "linear"])
+def test_compress_absmax_brute_force(kind):
+    rng = np.random.default_rng(40)
+    book = dq_code_book(kind)
+    a = _absmax_sample(rng, 256 * 9 + 77)          # ragged last group
+    code, a2, off = compress_absmax(a, book)
+    assert code.shape == a.shape and a2.shape == (10,)
+    # offset: fp32 rounding of the exactly summed mean
+    assert off == np.float32(math.fsum(a.astype(np.float64)) / a.size)
+    d = (a - off).astype(np.float32)
+    for g in range(10):
+        blk = d[256 * g:256 * (g + 1)]
+        assert a2[g] == np.max(np.abs(blk))
+        x = (blk / a2[g]).astype(np.float32)
+        dist = np.abs(x.astype(np.float64)[:, None] - book.astype(np.float64)[None, :])
+        srt = np.sort(dist, axis=1)
+        assert np.all(srt[:, 0] < srt[:, 1])       # no exact ties in this sample
+        assert np.array_equal(code[256 * g:256 * (g + 1)], np.argmin(dist, axis=1))
+    if kind == "linear":
+        # closed form for evenly spaced entries: the nearest index
+        x = (d / a2[np.arange(a.size) // 256]).astype(np.float64)
+        assert np.array_equal(code, np.clip(np.floor((x + 1.0) * 127.5 + 0.5), 0, 255))
+
+
+def test_expand_absmax_round_trip_and_special_cases():
+    rng = np.random.default_rng(41)
+    book = dq_code_book("dynamic")
+    a = _absmax_sample(rng, 256 * 6)
+    code, a2, off = compress_absmax(a, book)
+    got = expand_absmax(code, a2, off, book)
+    gaps = np.diff(book.astype(np.float64))
+    err = np.abs(got.astype(np.float64) - a)
+    lim = (np.max(gaps) / 2) * np.repeat(a2, 256).astype(np.float64) + 4 * np.spacing(a)
+    assert np.all(err <= lim)
+    # each group's largest |d| sits on an end entry (+-1) and decodes to
+    # fp32(+-absmax2 + offset)
+    d = (a - off).astype(np.float32).reshape(6, 256)
+    arg = np.argmax(np.abs(d), axis=1)
+    for g in range(6):
+        c = code[256 * g + arg[g]]
+        assert c in (0, 255)
+        assert got[256 * g + arg[g]] == np.float32(np.float32(book[c] * a2[g]) + off)
+    # a stack of equal absmax: offset is that value, every group's scale 0,
+    # codes point at the zero entry, the decode is exact
+    code, a2, off = compress_absmax(np.full(300, 0.0375, np.float32), book)
+    assert off == np.float32(0.0375) and np.all(a2 == 0)
+    assert np.all(book[code] == 0) and np.all(expand_absmax(code, a2, off, book) == np.float32(0.0375))
+    # hand case: book[code] * absmax2 rounded to fp32, then + offset rounded
+    c = np.array([255, 0, 128], np.uint8)
+    got = expand_absmax(c, np.array([0.5], np.float32), np.float32(0.25), book)
+    assert np.array_equal(got, np.array([0.75, -0.25, 0.25 + 0.5 * float(book[128])], np.float32))
+
+
+def test_dq_book_and_midpoints():
+    book = dq_code_book("dynamic")
+    assert book[0] == -1 and book[255] == 1 and 0.0 in book
+    m = dq_midpoints(book)
+    assert m.shape == (255,) and np.all(book[:-1] < m) and np.all(m < book[1:])
+    with pytest.raises(ValueError):
+        dq_midpoints(np.sort(book)[::-1])
