@@ -95,6 +95,27 @@ def nf4_layer(moe4, inputs, spec, layer, seed, torch):
                         act=moe4.MOE4_ACT_SWIGLU, E=E, H=H, I=I, **lora)
 
 
+def nf4_dq_layer(moe4, inputs, spec, layer, seed, torch):
+    """NF4 stack whose absmax is double-quantised on the GPU (dynamic code book)."""
+    base = nf4_layer(moe4, inputs, spec, layer, seed, torch)
+    gq, gs, dq, ds = base.tensors[:4]
+    dev = gq.device
+    book = torch.from_numpy(inputs.dq_code_book("dynamic")).to(dev)
+    ws = torch.empty(moe4.MOE4_DQ_WS_BYTES, dtype=torch.uint8, device=dev)
+    parts = []
+    for a in (gs, ds):
+        n = a.numel()
+        code = torch.empty(a.shape, dtype=torch.uint8, device=dev)
+        a2 = torch.empty((n + 255) // 256, dtype=torch.float32, device=dev)
+        off = torch.empty(1, dtype=torch.float32, device=dev)
+        moe4.moe4_compress_absmax(a.reshape(-1), book, code, a2, off, ws)
+        parts.append((code, a2, off))
+    (gc, ga2, goff), (dc, da2, doff) = parts
+    return moe4.Experts(moe4.MOE4_FMT_NF4_DQ, gq, gc, dq, dc, gu_layout=moe4.MOE4_GU_HALVES,
+                        act=moe4.MOE4_ACT_SWIGLU, E=spec.E, H=spec.H, I=spec.I, gu_s2=ga2,
+                        dn_s2=da2, gu_soff=goff, dn_soff=doff, dq_book=book)
+
+
 def mxfp4_layer(moe4, inputs, spec, layer, seed, torch):
     E, H, I = spec.E, spec.H, spec.I
     gb, gsc, db, dsc = inputs.device_mxfp4_stack(spec, layer, seed)
@@ -122,6 +143,9 @@ def expert_bytes(spec):
     if spec.fmt == "nf4":
         gu = 2 * I * H // 2 + 2 * I * (H // 64) * 4
         dn = H * I // 2 + H * (I // 64) * 4
+    elif spec.fmt == "nf4_dq":   # 1-byte absmax codes + one fp32 per 256 of them
+        gu = 2 * I * H // 2 + 2 * I * (H // 64) + 2 * I * (H // 64) * 4 / 256
+        dn = H * I // 2 + H * (I // 64) + H * (I // 64) * 4 / 256
     else:
         gu = 2 * I * H // 2 + 2 * I * (H // 32)
         dn = H * I // 2 + H * (I // 32)
@@ -537,7 +561,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
-    ap.add_argument("--only", default="", help="comma list of sweep parts: qwen,gptoss,lora,router,convert,stack")
+    ap.add_argument("--only", default="", help="comma list of sweep parts: qwen,gptoss,lora,dq,router,convert,stack")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run the copy kernel of known size (for PMC scaling)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -613,6 +637,16 @@ def main():
             log("sweep:", json.dumps(r))
             sweep.append(r)
             del mex
+        if not only or "dq" in only:
+            dspec = spec.scaled(fmt="nf4_dq", name=spec.name + "_absmax_dq")
+            dex = [nf4_dq_layer(moe4, inputs, spec, r, args.seed, torch)
+                   for r in range(args.replicas)]
+            for T in (1, 16, 128, HEADLINE_T):
+                r, _ = bench_layer(torch, hip, moe4, inputs, dspec, T, dex,
+                                   reps * (2 if T < HEADLINE_T else 1), args.warmup, args.seed)
+                log("sweep:", json.dumps(r))
+                sweep.append(r)
+            del dex
         if not only or "router" in only:
             r = bench_router(torch, hip, moe4, inputs, spec, HEADLINE_T, reps, args.warmup,
                              args.seed)

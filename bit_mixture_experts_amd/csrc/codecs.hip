@@ -222,7 +222,174 @@ __global__ __launch_bounds__(256) void k_convert_mxfp4_nf4(const uint8_t* __rest
   }
 }
 
+// ------------------------------------------- double-quantised NF4 absmax
+//
+// The nested absmax form of a resident NF4 stack (project page
+// "experts4bit-qlora", "Limitations -- qlora-fused-moe-experts", the
+// double-quantised absmax item): offset = fp32 rounding of the float64 mean of
+// all absmax; per 256 consecutive values d = fp32(a - offset), absmax2 =
+// max |d|, code = the code-book entry nearest to fp32(d / absmax2) (decided by
+// fp32 midpoints formed in float64; a value on a midpoint takes the lower
+// code). Decoding: fp32(fp32(book[code] * absmax2) + offset), no fused
+// multiply-add.
+
+// float64 partial sums of contiguous chunks, one per workgroup
+__global__ __launch_bounds__(256) void k_dq_partial(const float* __restrict__ a, int64_t n,
+                                                    double* __restrict__ part) {
+  __shared__ double red[256];
+  const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = (int64_t)blockIdx.x * per, b1 = min(n, b0 + per);
+  double acc = 0.0;
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += blockDim.x) acc += (double)a[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// offset = fp32(sum of the partials / n), partials summed in a fixed order
+__global__ __launch_bounds__(256) void k_dq_offset(const double* __restrict__ part, int nparts,
+                                                   int64_t n, float* __restrict__ offset) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) acc += part[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) offset[0] = (float)(red[0] / (double)n);
+}
+
+// one wave per group of 256 absmax (4 per lane); the 255 midpoints of the
+// code book are formed once per workgroup in LDS and searched by bisection
+__global__ __launch_bounds__(256) void k_dq_compress(const float* __restrict__ a, int64_t n,
+                                                     const float* __restrict__ book,
+                                                     const float* __restrict__ offset,
+                                                     uint8_t* __restrict__ code,
+                                                     float* __restrict__ absmax2) {
+  __shared__ float mids[256];
+  if (threadIdx.x < 255)
+    mids[threadIdx.x] =
+        (float)(((double)book[threadIdx.x] + (double)book[threadIdx.x + 1]) * 0.5);
+  __syncthreads();
+  const int64_t g = (int64_t)blockIdx.x * 4 + wave_id();
+  const int64_t ngroups = (n + 255) / 256;
+  if (g >= ngroups) return;
+  const float off = offset[0];
+  const int l = lane_id();
+  float d[4];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t idx = g * 256 + 4 * l + i;
+    d[i] = idx < n ? __fsub_rn(a[idx], off) : 0.0f;
+    m = fmaxf(m, fabsf(d[i]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x = m == 0.0f ? 0.0f : __fdiv_rn(d[i], m);
+    // number of midpoints strictly below x
+    int lo = 0, hi = 255;   // answer in [lo, hi]
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int mid = (lo + hi) >> 1;
+      if (mids[mid] < x) lo = mid + 1;
+      else hi = mid;
+    }
+    packed |= (uint32_t)lo << (8 * i);
+  }
+  const int64_t base = g * 256 + 4 * l;
+  if (base + 3 < n) {
+    *reinterpret_cast<uint32_t*>(code + base) = packed;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (base + i < n) code[base + i] = (uint8_t)(packed >> (8 * i));
+  }
+  if (l == 0) absmax2[g] = m;
+}
+
+// decoded absmax, four per thread
+__global__ __launch_bounds__(256) void k_dq_expand(const uint8_t* __restrict__ code,
+                                                   const float* __restrict__ absmax2,
+                                                   const float* __restrict__ offset,
+                                                   const float* __restrict__ book, int64_t n,
+                                                   float* __restrict__ out) {
+  __shared__ float tb[256];
+  tb[threadIdx.x] = book[threadIdx.x];
+  __syncthreads();
+  const float off = offset[0];
+  const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i0 >= n) return;
+  const float s2 = absmax2[i0 >> 8];   // the four share one group (256 % 4 == 0)
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i0 + i < n) out[i0 + i] = mul_then_add(tb[code[i0 + i]], s2, off);
+}
+
 }  // namespace
+
+int dq_partials(int64_t n) {
+  const int64_t p = (n + 4095) / 4096;
+  return (int)(p < kDqPartials ? p : kDqPartials);
+}
+
+hipError_t launch_dq_compress(const float* absmax, int64_t n, const float* book, uint8_t* code,
+                              float* absmax2, float* offset, void* ws, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int np = dq_partials(n);
+  double* part = static_cast<double*>(ws);
+  hipLaunchKernelGGL(k_dq_partial, dim3(np), dim3(256), 0, s, absmax, n, part);
+  hipLaunchKernelGGL(k_dq_offset, dim3(1), dim3(256), 0, s, part, np, n, offset);
+  const int64_t ngroups = (n + 255) / 256;
+  hipLaunchKernelGGL(k_dq_compress, dim3((unsigned)((ngroups + 3) / 4)), dim3(256), 0, s, absmax,
+                     n, book, offset, code, absmax2);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_expand(const uint8_t* code, const float* absmax2, const float* offset,
+                            const float* book, int64_t n, float* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t threads = (n + 3) / 4;
+  hipLaunchKernelGGL(k_dq_expand, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, code,
+                     absmax2, offset, book, n, out);
+  return hipGetLastError();
+}
+
+size_t dq_expand_bytes(const moe4_experts& ex) {
+  if (ex.format != MOE4_FMT_NF4_DQ) return 0;
+  const int64_t ngu = (int64_t)ex.E * 2 * ex.I * (ex.H / 64);
+  const int64_t ndn = (int64_t)ex.E * ex.H * (ex.I / 64);
+  return align_up((size_t)ngu * 4, 256) + align_up((size_t)ndn * 4, 256);
+}
+
+hipError_t dq_expand_experts(const moe4_experts& ex, void* abs_ws, moe4_experts* out,
+                             hipStream_t s) {
+  const int64_t ngu = (int64_t)ex.E * 2 * ex.I * (ex.H / 64);
+  const int64_t ndn = (int64_t)ex.E * ex.H * (ex.I / 64);
+  float* gu = static_cast<float*>(abs_ws);
+  float* dn = reinterpret_cast<float*>(static_cast<char*>(abs_ws) + align_up((size_t)ngu * 4, 256));
+  hipError_t e = launch_dq_expand(static_cast<const uint8_t*>(ex.gu_s), ex.gu_s2, ex.gu_soff,
+                                  ex.dq_book, ngu, gu, s);
+  if (e != hipSuccess) return e;
+  e = launch_dq_expand(static_cast<const uint8_t*>(ex.dn_s), ex.dn_s2, ex.dn_soff, ex.dq_book,
+                       ndn, dn, s);
+  if (e != hipSuccess) return e;
+  *out = ex;
+  out->format = MOE4_FMT_NF4;
+  out->gu_s = gu;
+  out->dn_s = dn;
+  out->gu_s2 = out->dn_s2 = out->gu_soff = out->dn_soff = out->dq_book = nullptr;
+  return hipSuccess;
+}
 
 hipError_t launch_quantize_nf4(const float* w, int64_t n, uint8_t* packed, float* absmax,
                                hipStream_t s) {

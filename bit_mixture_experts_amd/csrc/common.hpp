@@ -70,6 +70,13 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// fp32(fp32(a * b) + c): one rounded product, one rounded sum; the pragma
+// keeps the compiler from contracting the pair into a fused multiply-add
+__device__ __forceinline__ float mul_then_add(float a, float b, float c) {
+#pragma clang fp contract(off)
+  return a * b + c;
+}
+
 // logistic function; v_exp_f32 and v_rcp_f32 (about 1 ulp each)
 __device__ __forceinline__ float sigmoidf_(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-z));

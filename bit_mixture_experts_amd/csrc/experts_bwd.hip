@@ -320,7 +320,7 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
 size_t backward_ws_bytes(const moe4_experts& ex, int rows) {
   size_t b = align_up((size_t)rows * 2 * ex.I * sizeof(uint16_t), 256);
   if (ex.lora_A) b += align_up((size_t)rows * ex.lora_r * sizeof(float), 256);
-  return b;
+  return b + dq_expand_bytes(ex);
 }
 
 hipError_t launch_expert_backward(const moe4_experts& ex, const uint16_t* x_perm,
@@ -333,7 +333,16 @@ hipError_t launch_expert_backward(const moe4_experts& ex, const uint16_t* x_perm
   uint16_t* dgu = reinterpret_cast<uint16_t*>(p);
   p += align_up((size_t)rows * 2 * ex.I * sizeof(uint16_t), 256);
   float* tbuf = ex.lora_A ? reinterpret_cast<float*>(p) : nullptr;
+  if (ex.lora_A) p += align_up((size_t)rows * ex.lora_r * sizeof(float), 256);
   if (rows == 0 && !ex.lora_A) return hipSuccess;
+  if (ex.format == MOE4_FMT_NF4_DQ) {
+    // expand the double-quantised absmax, then the plain NF4 dgrad
+    moe4_experts plain;
+    hipError_t err = dq_expand_experts(ex, p, &plain, s);
+    if (err != hipSuccess) return err;
+    return backward_fmt<MOE4_FMT_NF4>(plain, x_perm, offsets, rows, save_gu, save_xa, dy_perm,
+                                      dx_perm, dA, dB, dgu, tbuf, le, s);
+  }
   if (ex.format == MOE4_FMT_NF4)
     return backward_fmt<MOE4_FMT_NF4>(ex, x_perm, offsets, rows, save_gu, save_xa, dy_perm,
                                       dx_perm, dA, dB, dgu, tbuf, le, s);

@@ -42,7 +42,7 @@ namespace {
 template <int FMT>
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, float sc, const float2* lutf) {
   u32x4 r;
-  if constexpr (FMT == MOE4_FMT_NF4) {
+  if constexpr (FMT != MOE4_FMT_MXFP4) {
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
       const float2 v = lutf[(w >> (8 * bi)) & 255u];
@@ -70,7 +70,7 @@ __device__ __forceinline__ float scale_operand(uint32_t raw) {
 template <int NRT>
 struct SkinnyBatch {
   u32x4 wraw[2];
-  uint32_t sraw[2];
+  uint32_t sraw[2];    // scale word (fp32 absmax, e8m0 byte, or 8-bit absmax code)
   u32x4 av[NRT][4];
 };
 
@@ -79,6 +79,17 @@ struct SkinnyLane {
   rsrc_t rq, rs, ra;    // this expert's nibbles and scales; this row chunk's activations
   int qoff[2];          // byte offset of the lane's 16-byte column in weight row c, k = 0
   int srow[2];          // weight row index of column tile c (inside the expert)
+  int a2bnd;            // double-quantised NF4: per c (16 bits each), the first block
+                        // of weight row c that lies in the row's second absmax group
+};
+
+// Double-quantised NF4 in the skinny kernel: the workgroup's 32 weight rows
+// each span at most two groups of 256 absmax (rows of at most 256 blocks);
+// a2tab[2 * (16 c + n) + h] holds the group scale of half h of row (c, n).
+struct SkinnyDq {
+  const float* book;   // LDS: the 256-entry code book
+  const float* a2tab;  // LDS: [32 rows][2]
+  float off;           // the stack's absmax offset
 };
 
 // Each k-iteration covers 128 k: lane (n = l%16, g = l/16) loads 16 bytes
@@ -113,10 +124,26 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<NRT>& bt, const SkinnyLa
 
 template <int FMT, int NRT>
 __device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const float2* lutf,
-                                               f32x4 (&acc)[2][2]) {
+                                               const SkinnyLane& sl, const SkinnyDq& dq, int K,
+                                               int it, f32x4 (&acc)[2][2]) {
+  float scs[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const float sc = scale_operand<FMT>(bt.sraw[c]);
+    if constexpr (FMT == MOE4_FMT_NF4_DQ) {
+      // absmax = fp32(fp32(book[code] * absmax2) + offset); absmax2 is the
+      // row's first or second group scale
+      const int l = lane_id();
+      const int blk = 2 * it + (l >> 5);   // (128 it + 32 g) / 64
+      const int bnd = (sl.a2bnd >> (16 * c)) & 0xFFFF;
+      const float a2 = dq.a2tab[2 * (16 * c + (l & 15)) + (blk < bnd ? 0 : 1)];
+      scs[c] = mul_then_add(dq.book[bt.sraw[c] & 255u], a2, dq.off);
+    } else {
+      scs[c] = scale_operand<FMT>(bt.sraw[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const float sc = scs[c];
     u32x4 bq[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) bq[st] = dequant8<FMT>(bt.wraw[c][st], sc, lutf);
@@ -135,15 +162,16 @@ __device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const
 // and multiplied.
 template <int FMT, int NRT>
 __device__ __forceinline__ void skinny_kloop(const SkinnyLane& sl, int K, int it0, int it1,
-                                             const float2* lutf, f32x4 (&acc)[2][2]) {
+                                             const float2* lutf, const SkinnyDq& dq,
+                                             f32x4 (&acc)[2][2]) {
   SkinnyBatch<NRT> b0, b1;
   skinny_load<FMT>(b0, sl, K, it0, it1);
   for (int it = it0; it < it1; it += 2) {
     if (it + 1 < it1) skinny_load<FMT>(b1, sl, K, it + 1, it1);
-    skinny_compute<FMT>(b0, lutf, acc);
+    skinny_compute<FMT>(b0, lutf, sl, dq, K, it, acc);
     if (it + 1 >= it1) break;
     if (it + 2 < it1) skinny_load<FMT>(b0, sl, K, it + 2, it1);
-    skinny_compute<FMT>(b1, lutf, acc);
+    skinny_compute<FMT>(b1, lutf, sl, dq, K, it + 1, acc);
   }
 }
 
@@ -151,22 +179,41 @@ __device__ __forceinline__ void skinny_kloop(const SkinnyLane& sl, int K, int it
 // 16 (gate, up) pairs; down: 32 output columns); its S waves split K and are
 // reduced through LDS; the expert's rows are taken 32 at a time.
 template <int FMT, bool GATEUP>
-__global__ __launch_bounds__(512) void k_skinny(const GemmArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(3)))
+void k_skinny(const GemmArgs a) {
   using F = Format<FMT>;
-  constexpr bool NF4 = FMT == MOE4_FMT_NF4;
+  constexpr bool NF4 = FMT != MOE4_FMT_MXFP4;
+  constexpr bool DQ = FMT == MOE4_FMT_NF4_DQ;
   constexpr int MAXR = 2;
   constexpr int KB = F::kBlock;
-  // NF4 byte -> two fp32 levels
+  // NF4 byte -> two fp32 levels; the absmax code book of a double-quantised stack
   __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
+  __shared__ float dqbook[DQ ? 256 : 1];
+  __shared__ float a2tab[DQ ? 64 : 1];
   extern __shared__ __attribute__((aligned(16))) float red[];   // [S][MAXR][2][256]
   const int S = blockDim.x >> 6, w = wave_id(), l = lane_id();
   if (NF4)
     for (int i = threadIdx.x; i < 256; i += blockDim.x)
       lutf[i] = make_float2(F::level(i & 15), F::level(i >> 4));
+  if (DQ)
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) dqbook[i] = a.dqbook[i];
+  SkinnyDq dq{dqbook, a2tab, DQ ? a.dqoff[0] : 0.0f};
   const int item = blockIdx.x / a.ncg, cg = blockIdx.x - item * a.ncg;
   int e, unused;
   locate_item(a.offsets, a.E, item, [](int n) { return n > 0 ? 1 : 0; }, e, unused);
   e = __builtin_amdgcn_readfirstlane(e);
+  const int Nw0 = GATEUP ? 2 * a.I : a.N_out;
+  if (DQ && e >= 0 && threadIdx.x < 32) {
+    // group scales of the workgroup's 32 weight rows (row (c, n) = thread 16 c + n)
+    const int c = threadIdx.x >> 4, n = threadIdx.x & 15;
+    const int row = GATEUP ? (c == 0 ? gate_row(a.layout, a.I, cg * 16 + n)
+                                     : up_row(a.layout, a.I, cg * 16 + n))
+                           : cg * 32 + 16 * c + n;
+    const int64_t ng = ((int64_t)a.E * Nw0 * (a.K / KB) + 255) / 256;
+    const int64_t g0 = (((int64_t)e * Nw0 + row) * (a.K / KB)) >> 8;
+    a2tab[2 * threadIdx.x] = a.ws2[g0];
+    a2tab[2 * threadIdx.x + 1] = g0 + 1 < ng ? a.ws2[g0 + 1] : 0.0f;
+  }
   __syncthreads();
   if (e < 0) return;
   const int K = a.K;
@@ -184,9 +231,15 @@ __global__ __launch_bounds__(512) void k_skinny(const GemmArgs a) {
     sl.srow[1] = cg * 32 + 16 + nl;
   }
   sl.rq = make_rsrc(a.wq + (int64_t)e * Nw * (K / 2), (uint32_t)Nw * (K / 2));
-  constexpr int sbytes = NF4 ? 4 : 1;
+  constexpr int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
   sl.rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Nw * (K / KB) * sbytes,
                     (uint32_t)Nw * (K / KB) * sbytes);
+  if (DQ) {
+    sl.a2bnd = 0;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      sl.a2bnd |= (256 - (int)((((int64_t)e * Nw + sl.srow[c]) * (K / KB)) & 255)) << (16 * c);
+  }
 #pragma unroll
   for (int c = 0; c < 2; ++c) sl.qoff[c] = sl.srow[c] * (K / 2) + 16 * g;
   const int nit = (K + 127) / 128;
@@ -198,8 +251,8 @@ __global__ __launch_bounds__(512) void k_skinny(const GemmArgs a) {
     const int nrt = (nrows + 15) >> 4;
     f32x4 acc[2][2] = {{zero4, zero4}, {zero4, zero4}};
     sl.ra = make_rsrc(a.A + (int64_t)(rbeg + rc) * K, (uint32_t)nrows * K * 2);
-    if (nrt == 1) skinny_kloop<FMT, 1>(sl, K, it0, it1, lutf, acc);
-    else skinny_kloop<FMT, 2>(sl, K, it0, it1, lutf, acc);
+    if (nrt == 1) skinny_kloop<FMT, 1>(sl, K, it0, it1, lutf, dq, acc);
+    else skinny_kloop<FMT, 2>(sl, K, it0, it1, lutf, dq, acc);
     // reduce the S partial sums through LDS: red[w][rt][c][lane*4 + i]
 #pragma unroll
     for (int rt = 0; rt < MAXR; ++rt)
@@ -568,6 +621,13 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
   d.hout = nullptr;
   d.yout = y_perm;
   d.save_gu = nullptr;
+  // double-quantised NF4: the absmax codes, their per-256 scales and the offset
+  g.ws2 = ex.gu_s2;
+  g.dqoff = ex.gu_soff;
+  g.dqbook = ex.dq_book;
+  d.ws2 = ex.dn_s2;
+  d.dqoff = ex.dn_soff;
+  d.dqbook = ex.dq_book;
   const int touched = min(E, rows);
   hipError_t err;
   if (variant == MOE4_VARIANT_SKINNY) {
@@ -582,17 +642,21 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
     le.after(1, s);
     return err;
   }
-  const int ntiles = rows / kBM + touched;
-  g.ncg = (I + 127) / 128;
-  d.ncg = (H + 255) / 256;
-  le.before(0, s);
-  err = run_tiled<FMT, true>(g, ntiles, s);
-  le.after(0, s);
-  if (err != hipSuccess) return err;
-  le.before(1, s);
-  err = run_tiled<FMT, false>(d, ntiles, s);
-  le.after(1, s);
-  return err;
+  if constexpr (FMT == MOE4_FMT_NF4_DQ) {
+    return hipErrorInvalidValue;   // the tiled kernels take the expanded (plain NF4) view
+  } else {
+    const int ntiles = rows / kBM + touched;
+    g.ncg = (I + 127) / 128;
+    d.ncg = (H + 255) / 256;
+    le.before(0, s);
+    err = run_tiled<FMT, true>(g, ntiles, s);
+    le.after(0, s);
+    if (err != hipSuccess) return err;
+    le.before(1, s);
+    err = run_tiled<FMT, false>(d, ntiles, s);
+    le.after(1, s);
+    return err;
+  }
 }
 
 }  // namespace
@@ -600,7 +664,7 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
 size_t forward_ws_bytes(const moe4_experts& ex, int rows) {
   size_t b = align_up((size_t)rows * ex.I * sizeof(uint16_t), 256);
   if (ex.lora_A) b += align_up((size_t)rows * ex.lora_r * sizeof(float), 256);
-  return b;
+  return b + dq_expand_bytes(ex);
 }
 
 int choose_variant(const moe4_experts& ex, int rows) {
@@ -620,12 +684,26 @@ hipError_t launch_expert_forward(const moe4_experts& ex, const uint16_t* x_perm,
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(p);
   p += align_up((size_t)rows * ex.I * sizeof(uint16_t), 256);
   float* xa = nullptr;
+  char* abs_ws = p + (ex.lora_A ? align_up((size_t)rows * ex.lora_r * sizeof(float), 256) : 0);
   if (ex.lora_A) {
     xa = save_xa ? save_xa : reinterpret_cast<float*>(p);
     hipLaunchKernelGGL(k_lora_xa, dim3((rows + 3) / 4), dim3(256), 0, s, x_perm, offsets, ex.E,
                        rows, ex.H, ex.lora_A, ex.lora_r, xa);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+  }
+  if (ex.format == MOE4_FMT_NF4_DQ) {
+    // decode-sized (rows of at most 256 absmax, i.e. K <= 16384): both absmax
+    // levels decoded inside the kernel; otherwise expand the absmax once into
+    // the workspace, then the plain NF4 kernels
+    if (*variant == MOE4_VARIANT_SKINNY && ex.H / 64 <= 256 && ex.I / 64 <= 256)
+      return forward_fmt<MOE4_FMT_NF4_DQ>(ex, x_perm, offsets, rows, y_perm, save_gu, xa, hbuf,
+                                          *variant, le, s);
+    moe4_experts plain;
+    hipError_t err = dq_expand_experts(ex, abs_ws, &plain, s);
+    if (err != hipSuccess) return err;
+    return forward_fmt<MOE4_FMT_NF4>(plain, x_perm, offsets, rows, y_perm, save_gu, xa, hbuf,
+                                     *variant, le, s);
   }
   if (ex.format == MOE4_FMT_NF4)
     return forward_fmt<MOE4_FMT_NF4>(ex, x_perm, offsets, rows, y_perm, save_gu, xa, hbuf,

@@ -54,6 +54,15 @@ struct Format<MOE4_FMT_MXFP4> {
   }
 };
 
+// NF4 with double-quantised absmax: the same codes and blocks; the absmax
+// arrives as an 8-bit code plus a per-256 scale and a stack offset (decoded by
+// the kernels that read it; Format::scale is not used for it)
+template <>
+struct Format<MOE4_FMT_NF4_DQ> {
+  static constexpr int kBlock = 64;
+  __device__ static float level(int c) { return kNf4Levels[c]; }
+};
+
 // byte -> two bf16 levels (low nibble in the low half)
 template <int FMT>
 __device__ __forceinline__ uint32_t lut_bf16x2(int byte) {

@@ -10,7 +10,11 @@ namespace moe4 {
 // down) with activations A [rows, K] ordered by expert (offsets [E+1]).
 struct GemmArgs {
   const uint8_t* wq;    // packed nibbles, K/2 bytes per weight row
-  const void* ws;       // scales: f32 [E, Nw, K/64] (NF4) or u8 [E, Nw, K/32] (MXFP4)
+  const void* ws;       // scales: f32 [E, Nw, K/64] (NF4), u8 [E, Nw, K/32] (MXFP4), or
+                        // u8 absmax codes [E, Nw, K/64] (double-quantised NF4)
+  const float* ws2;     // double-quantised NF4: absmax2, one per 256 absmax of the stack
+  const float* dqoff;   // double-quantised NF4: the stack's absmax offset (one fp32)
+  const float* dqbook;  // double-quantised NF4: the 256-entry absmax code book
   int K;
   int N_out;            // gate_up: I (gate/up pairs); down: H
   int I;

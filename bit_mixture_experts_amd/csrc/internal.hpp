@@ -18,6 +18,20 @@ hipError_t launch_decode_mxfp4(const uint8_t* blocks, const uint8_t* scales, int
 hipError_t launch_convert_mxfp4_nf4(const uint8_t* blocks, const uint8_t* scales, int64_t R,
                                     int64_t K, uint8_t* packed, float* absmax, hipStream_t s);
 
+// ---- double-quantised NF4 absmax
+constexpr int kDqPartials = 1024;   // float64 partial sums in the workspace (8 KiB)
+int dq_partials(int64_t n);
+hipError_t launch_dq_compress(const float* absmax, int64_t n, const float* book, uint8_t* code,
+                              float* absmax2, float* offset, void* ws, hipStream_t s);
+hipError_t launch_dq_expand(const uint8_t* code, const float* absmax2, const float* offset,
+                            const float* book, int64_t n, float* out, hipStream_t s);
+
+// Plain-NF4 view of a double-quantised descriptor: both stacks' absmax
+// expanded into abs_ws (dq_expand_bytes of it; 0 for other formats).
+size_t dq_expand_bytes(const moe4_experts& ex);
+hipError_t dq_expand_experts(const moe4_experts& ex, void* abs_ws, moe4_experts* out,
+                             hipStream_t s);
+
 // ---- router step
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
                                 int H, int E, float* logits, hipStream_t s);

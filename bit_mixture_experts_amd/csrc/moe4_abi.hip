@@ -49,7 +49,8 @@ int launched(hipError_t e, const char* what) {
 // Shared checks of a moe4_experts descriptor.
 int check_experts(const moe4_experts* ex) {
   if (ex == nullptr) return fail(MOE4_EINVAL, "moe4_experts is NULL");
-  if (ex->format != MOE4_FMT_NF4 && ex->format != MOE4_FMT_MXFP4)
+  if (ex->format != MOE4_FMT_NF4 && ex->format != MOE4_FMT_MXFP4 &&
+      ex->format != MOE4_FMT_NF4_DQ)
     return fail(MOE4_EINVAL, "moe4_experts.format %s (%d)", ex->format ? "unknown" : "unset",
                 ex->format);
   if (ex->gu_layout != MOE4_GU_HALVES && ex->gu_layout != MOE4_GU_INTERLEAVED)
@@ -64,7 +65,7 @@ int check_experts(const moe4_experts* ex) {
     return fail(MOE4_ESHAPE, "moe4_experts.E = %d outside [1, 1024]", ex->E);
   if (ex->H <= 0 || ex->I <= 0)
     return fail(MOE4_ESHAPE, "moe4_experts.H = %d, I = %d must be positive", ex->H, ex->I);
-  const int blk = ex->format == MOE4_FMT_NF4 ? 64 : 32;
+  const int blk = ex->format == MOE4_FMT_MXFP4 ? 32 : 64;
   if (ex->H % blk)
     return fail(MOE4_ESHAPE, "moe4_experts.H = %d is not a multiple of %d", ex->H, blk);
   if (ex->I % blk)
@@ -85,6 +86,21 @@ int check_experts(const moe4_experts* ex) {
   if (ex->format == MOE4_FMT_NF4) {
     REQUIRE_ALIGN(ex->gu_s, 4, "moe4_experts.gu_s");
     REQUIRE_ALIGN(ex->dn_s, 4, "moe4_experts.dn_s");
+  }
+  if (ex->format == MOE4_FMT_NF4_DQ) {
+    REQUIRE_PTR(ex->gu_s2, "moe4_experts.gu_s2");
+    REQUIRE_PTR(ex->dn_s2, "moe4_experts.dn_s2");
+    REQUIRE_PTR(ex->gu_soff, "moe4_experts.gu_soff");
+    REQUIRE_PTR(ex->dn_soff, "moe4_experts.dn_soff");
+    REQUIRE_PTR(ex->dq_book, "moe4_experts.dq_book");
+    REQUIRE_ALIGN(ex->gu_s2, 4, "moe4_experts.gu_s2");
+    REQUIRE_ALIGN(ex->dn_s2, 4, "moe4_experts.dn_s2");
+    REQUIRE_ALIGN(ex->gu_soff, 4, "moe4_experts.gu_soff");
+    REQUIRE_ALIGN(ex->dn_soff, 4, "moe4_experts.dn_soff");
+    REQUIRE_ALIGN(ex->dq_book, 4, "moe4_experts.dq_book");
+  } else if (ex->gu_s2 || ex->dn_s2 || ex->gu_soff || ex->dn_soff || ex->dq_book) {
+    return fail(MOE4_EINVAL, "moe4_experts: double-quantised absmax fields given for format %d",
+                ex->format);
   }
   REQUIRE_ALIGN(ex->gu_bias, 2, "moe4_experts.gu_bias");
   REQUIRE_ALIGN(ex->dn_bias, 2, "moe4_experts.dn_bias");
@@ -149,6 +165,48 @@ int moe4_decode_mxfp4(const uint8_t* blocks, const uint8_t* scales, int64_t R, i
   REQUIRE_ALIGN(out, 16, "out");
   return launched(moe4::launch_decode_mxfp4(blocks, scales, R, K, out, (hipStream_t)stream),
                   "moe4_decode_mxfp4");
+}
+
+int moe4_compress_absmax(const float* absmax, int64_t n, const float* book, uint8_t* code,
+                         float* absmax2, float* offset, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (n < 0) return fail(MOE4_ESHAPE, "n = %lld is negative", (long long)n);
+  if (n == 0) return ok();
+  REQUIRE_PTR(absmax, "absmax");
+  REQUIRE_PTR(book, "book");
+  REQUIRE_PTR(code, "code");
+  REQUIRE_PTR(absmax2, "absmax2");
+  REQUIRE_PTR(offset, "offset");
+  REQUIRE_ALIGN(absmax, 4, "absmax");
+  REQUIRE_ALIGN(book, 4, "book");
+  REQUIRE_ALIGN(code, 4, "code");
+  REQUIRE_ALIGN(absmax2, 4, "absmax2");
+  REQUIRE_ALIGN(offset, 4, "offset");
+  if (ws == nullptr || ws_bytes < (size_t)MOE4_DQ_WS_BYTES)
+    return fail(MOE4_EWORKSPACE, "moe4_compress_absmax: workspace of %zu bytes given, %d needed",
+                ws ? ws_bytes : (size_t)0, (int)MOE4_DQ_WS_BYTES);
+  if (!aligned(ws, 8)) return fail(MOE4_EALIGN, "moe4_compress_absmax: ws is not 8-byte aligned");
+  return launched(moe4::launch_dq_compress(absmax, n, book, code, absmax2, offset, ws,
+                                           (hipStream_t)stream),
+                  "moe4_compress_absmax");
+}
+
+int moe4_expand_absmax(const uint8_t* code, const float* absmax2, const float* offset,
+                       const float* book, int64_t n, float* out, void* stream) {
+  if (n < 0) return fail(MOE4_ESHAPE, "n = %lld is negative", (long long)n);
+  if (n == 0) return ok();
+  REQUIRE_PTR(code, "code");
+  REQUIRE_PTR(absmax2, "absmax2");
+  REQUIRE_PTR(offset, "offset");
+  REQUIRE_PTR(book, "book");
+  REQUIRE_PTR(out, "out");
+  REQUIRE_ALIGN(absmax2, 4, "absmax2");
+  REQUIRE_ALIGN(offset, 4, "offset");
+  REQUIRE_ALIGN(book, 4, "book");
+  REQUIRE_ALIGN(out, 4, "out");
+  return launched(moe4::launch_dq_expand(code, absmax2, offset, book, n, out,
+                                         (hipStream_t)stream),
+                  "moe4_expand_absmax");
 }
 
 int moe4_convert_mxfp4_nf4(const uint8_t* blocks, const uint8_t* scales, int64_t R, int64_t K,

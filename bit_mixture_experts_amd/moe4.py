@@ -22,14 +22,16 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MOE4_OK, MOE4_EINVAL, MOE4_EUNSUPPORTED, MOE4_ESHAPE = 0, -1, -2, -3
 MOE4_EALIGN, MOE4_EWORKSPACE, MOE4_EDEVICE = -4, -5, -6
-MOE4_FMT_NF4, MOE4_FMT_MXFP4 = 1, 2
+MOE4_FMT_NF4, MOE4_FMT_MXFP4, MOE4_FMT_NF4_DQ = 1, 2, 3
+MOE4_DQ_WS_BYTES = 8192
 MOE4_GU_HALVES, MOE4_GU_INTERLEAVED = 1, 2
 MOE4_ACT_SWIGLU, MOE4_ACT_SWIGLU_CLAMPED = 1, 2
 MOE4_VARIANT_AUTO, MOE4_VARIANT_SKINNY, MOE4_VARIANT_TILED = 0, 1, 2
 MOE4_DTYPE_BF16, MOE4_DTYPE_F32 = 1, 2
 
 # every symbol declared in include/moe4.h
-EXPORTS = ("moe4_quantize_nf4", "moe4_decode_mxfp4", "moe4_convert_mxfp4_nf4",
+EXPORTS = ("moe4_quantize_nf4", "moe4_compress_absmax", "moe4_expand_absmax",
+           "moe4_decode_mxfp4", "moe4_convert_mxfp4_nf4",
            "moe4_router_logits", "moe4_route", "moe4_route_backward", "moe4_permute",
            "moe4_expert_forward", "moe4_combine", "moe4_expert_backward",
            "moe4_workspace_size", "moe4_set_timing_events", "moe4_last_error",
@@ -48,6 +50,9 @@ class Moe4Experts(ctypes.Structure):
         ("lora_A", ctypes.c_void_p), ("lora_B", ctypes.c_void_p),
         ("lora_r", ctypes.c_int32), ("lora_scale", ctypes.c_float),
         ("variant", ctypes.c_int32),
+        ("gu_s2", ctypes.c_void_p), ("dn_s2", ctypes.c_void_p),
+        ("gu_soff", ctypes.c_void_p), ("dn_soff", ctypes.c_void_p),
+        ("dq_book", ctypes.c_void_p),
     ]
 
 
@@ -56,6 +61,8 @@ _P = ctypes.POINTER(Moe4Experts)
 _SIGS = {
     "moe4_quantize_nf4": ([_vp, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
     "moe4_decode_mxfp4": ([_vp, _vp, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "moe4_compress_absmax": ([_vp, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "moe4_expand_absmax": ([_vp, _vp, _vp, _vp, _i64, _vp, _vp], ctypes.c_int),
     "moe4_convert_mxfp4_nf4": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "moe4_route": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "moe4_router_logits": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp], ctypes.c_int),
@@ -128,9 +135,14 @@ class Experts:
 
     def __init__(self, fmt, gu_q, gu_s, dn_q, dn_s, *, gu_layout, act, E, H, I,
                  gu_bias=None, dn_bias=None, lora_A=None, lora_B=None, lora_scale=0.0,
-                 act_alpha=1.702, act_limit=7.0, variant=MOE4_VARIANT_AUTO):
+                 act_alpha=1.702, act_limit=7.0, variant=MOE4_VARIANT_AUTO,
+                 gu_s2=None, dn_s2=None, gu_soff=None, dn_soff=None, dq_book=None):
+        """fmt MOE4_FMT_NF4_DQ: gu_s / dn_s are the u8 absmax codes and
+        gu_s2, dn_s2, gu_soff, dn_soff, dq_book the rest of the nested absmax
+        (see moe4_compress_absmax)."""
         sdt = _F32 if fmt == MOE4_FMT_NF4 else _U8
-        self.tensors = (gu_q, gu_s, dn_q, dn_s, gu_bias, dn_bias, lora_A, lora_B)
+        self.tensors = (gu_q, gu_s, dn_q, dn_s, gu_bias, dn_bias, lora_A, lora_B,
+                        gu_s2, dn_s2, gu_soff, dn_soff, dq_book)
         self.desc = Moe4Experts(
             format=fmt, E=E, H=H, I=I, gu_layout=gu_layout, act=act,
             act_alpha=act_alpha, act_limit=act_limit,
@@ -139,7 +151,10 @@ class Experts:
             gu_bias=_ptr(gu_bias, _BF16, "gu_bias"), dn_bias=_ptr(dn_bias, _BF16, "dn_bias"),
             lora_A=_ptr(lora_A, _BF16, "lora_A"), lora_B=_ptr(lora_B, _BF16, "lora_B"),
             lora_r=0 if lora_A is None else int(lora_A.shape[1]),
-            lora_scale=lora_scale, variant=variant)
+            lora_scale=lora_scale, variant=variant,
+            gu_s2=_ptr(gu_s2, _F32, "gu_s2"), dn_s2=_ptr(dn_s2, _F32, "dn_s2"),
+            gu_soff=_ptr(gu_soff, _F32, "gu_soff"), dn_soff=_ptr(dn_soff, _F32, "dn_soff"),
+            dq_book=_ptr(dq_book, _F32, "dq_book"))
         self.E, self.H, self.I = E, H, I
         self.lora_r = self.desc.lora_r
 
@@ -157,6 +172,27 @@ def moe4_quantize_nf4(w, packed, absmax, blocksize=64, stream=None):
     _check(_lib.moe4_quantize_nf4(_ptr(w, _F32, "w"), w.numel(), blocksize,
                                   _ptr(packed, _U8, "packed"), _ptr(absmax, _F32, "absmax"),
                                   _stream(stream)))
+
+
+def moe4_compress_absmax(absmax, book, code, absmax2, offset, ws, stream=None):
+    """absmax f32 [n] -> code u8 [n], absmax2 f32 [ceil(n/256)], offset f32 [1];
+    ws: at least MOE4_DQ_WS_BYTES bytes of device scratch."""
+    n = absmax.numel()
+    if code.numel() != n or absmax2.numel() != (n + 255) // 256 or offset.numel() != 1:
+        raise ValueError("compress_absmax: output sizes do not match n")
+    _check(_lib.moe4_compress_absmax(_ptr(absmax, _F32, "absmax"), n, _ptr(book, _F32, "book"),
+                                     _ptr(code, _U8, "code"), _ptr(absmax2, _F32, "absmax2"),
+                                     _ptr(offset, _F32, "offset"), _ptr(ws, None, "ws"),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe4_expand_absmax(code, absmax2, offset, book, out, stream=None):
+    n = code.numel()
+    if out.numel() != n or absmax2.numel() != (n + 255) // 256:
+        raise ValueError("expand_absmax: sizes do not match")
+    _check(_lib.moe4_expand_absmax(_ptr(code, _U8, "code"), _ptr(absmax2, _F32, "absmax2"),
+                                   _ptr(offset, _F32, "offset"), _ptr(book, _F32, "book"), n,
+                                   _ptr(out, _F32, "out"), _stream(stream)))
 
 
 def moe4_decode_mxfp4(blocks, scales, out, stream=None):

@@ -64,7 +64,7 @@ enum {
 };
 
 /* storage format of an expert stack */
-enum { MOE4_FMT_NF4 = 1, MOE4_FMT_MXFP4 = 2 };
+enum { MOE4_FMT_NF4 = 1, MOE4_FMT_MXFP4 = 2, MOE4_FMT_NF4_DQ = 3 };
 /* where gate and up rows sit in the fused [2I, H] stack (no default) */
 enum { MOE4_GU_HALVES = 1, MOE4_GU_INTERLEAVED = 2 };
 /* expert activation (no default) */
@@ -82,6 +82,15 @@ enum { MOE4_VARIANT_AUTO = 0, MOE4_VARIANT_SKINNY = 1, MOE4_VARIANT_TILED = 2 };
  * byte, even element in the low nibble; w = NF4[code] * absmax):
  *   gu_q u8 [E, 2I, H/2]   gu_s f32 [E, 2I, H/64]
  *   dn_q u8 [E, H, I/2]    dn_s f32 [E, H, I/64]
+ * NF4_DQ (NF4 whose absmax is double-quantised, see moe4_compress_absmax):
+ *   gu_q, dn_q as NF4; gu_s u8 [E, 2I, H/64] and dn_s u8 [E, H, I/64] absmax
+ *   codes; gu_s2 / dn_s2 f32 [ceil(n/256)] absmax2 and gu_soff / dn_soff f32
+ *   [1] offset of each stack (n = its number of absmax); dq_book f32 [256].
+ *   absmax = fp32(fp32(dq_book[code] * absmax2[i / 256]) + offset), i the
+ *   flat absmax index in the stack. The decode-sized kernel decodes both
+ *   levels in place; the prefill-sized kernel and the backward expand the
+ *   absmax into the workspace first (the workspace grows by the two fp32
+ *   absmax arrays).
  * MXFP4 (OCP MX: e2m1 nibbles, 32 per block, one e8m0 scale per block; even
  * element in the low nibble; w = e2m1(n) * 2^(scale - 127)):
  *   gu_q u8 [E, 2I, H/32, 16]   gu_s u8 [E, 2I, H/32]
@@ -118,6 +127,12 @@ typedef struct moe4_experts {
   int32_t lora_r;
   float lora_scale;
   int32_t variant;
+  /* MOE4_FMT_NF4_DQ only (NULL otherwise) */
+  const float* gu_s2;
+  const float* dn_s2;
+  const float* gu_soff;
+  const float* dn_soff;
+  const float* dq_book;
 } moe4_experts;
 
 /*
@@ -135,6 +150,37 @@ typedef struct moe4_experts {
  */
 int moe4_quantize_nf4(const float* w, int64_t n, int32_t blocksize,
                       uint8_t* packed, float* absmax, void* stream);
+
+/*
+ * Double quantisation of an NF4 stack's absmax [experts4bit-qlora page,
+ * "Limitations -- qlora-fused-moe-experts", the double-quantised absmax item:
+ * one offset, an 8-bit code per absmax and one fp32 per 256 absmax, about a
+ * quarter of the bytes, lossy against the fp32 absmax]. The pages name the
+ * 8-bit code book but print none: it is an argument, 256 strictly increasing
+ * fp32 values (else the codes are unspecified).
+ *   offset[0] = fp32 rounding of the float64 mean of absmax[0..n)
+ *   per group g of 256 (the last may be shorter): d = fp32(absmax - offset),
+ *   absmax2[g] = max |d|, code = the book entry nearest to fp32(d / absmax2[g])
+ *   (0 when absmax2[g] = 0), decided by the fp32 midpoints of adjacent
+ *   entries formed in float64; a value on a midpoint takes the lower code.
+ *   absmax f32 [n] (finite), book f32 [256]; code u8 [n] out (4-byte aligned),
+ *   absmax2 f32 [ceil(n/256)] out, offset f32 [1] out (device memory)
+ *   ws: at least MOE4_DQ_WS_BYTES bytes of device scratch (8-byte aligned)
+ */
+enum { MOE4_DQ_WS_BYTES = 8192 };
+int moe4_compress_absmax(const float* absmax, int64_t n, const float* book, uint8_t* code,
+                         float* absmax2, float* offset, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * The decoded absmax of a double-quantised stack [same page and item]:
+ * out[i] = fp32(fp32(book[code[i]] * absmax2[i / 256]) + offset[0]), one fp32
+ * product and one fp32 sum (no fused multiply-add).
+ *   code u8 [n], absmax2 f32 [ceil(n/256)], offset f32 [1], book f32 [256]
+ *   (device memory); out f32 [n] out
+ */
+int moe4_expand_absmax(const uint8_t* code, const float* absmax2, const float* offset,
+                       const float* book, int64_t n, float* out, void* stream);
 
 /*
  * Bit-exact MXFP4 -> bf16 decode [MXFP4 page, "Why it happens" and "Two

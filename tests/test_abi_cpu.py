@@ -72,6 +72,26 @@ def test_decode_route_combine_refusals():
     assert "out_dtype unset" in moe4.moe4_last_error()
 
 
+def test_double_quant_refusals():
+    c = lib.moe4_compress_absmax
+    assert c(FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE, 8192, None) == moe4.MOE4_ESHAPE
+    assert c(FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None) == moe4.MOE4_EWORKSPACE
+    assert c(FAKE, 100, None, FAKE, FAKE, FAKE, FAKE, 8192, None) == moe4.MOE4_EINVAL
+    assert c(FAKE, 100, FAKE, FAKE_MIS + 1, FAKE, FAKE, FAKE, 8192, None) == moe4.MOE4_EALIGN
+    assert c(None, 0, None, None, None, None, None, 0, None) == moe4.MOE4_OK
+    x = lib.moe4_expand_absmax
+    assert x(FAKE, FAKE, None, FAKE, 10, FAKE, None) == moe4.MOE4_EINVAL
+    assert x(None, None, None, None, 0, None, None) == moe4.MOE4_OK
+    # descriptor: the nested absmax fields are required with NF4_DQ, refused otherwise
+    d = _desc(format=moe4.MOE4_FMT_NF4_DQ)
+    assert _fwd(d) == moe4.MOE4_EINVAL and "gu_s2" in moe4.moe4_last_error()
+    d = _desc(format=moe4.MOE4_FMT_NF4, dq_book=FAKE)
+    assert _fwd(d) == moe4.MOE4_EINVAL and "double-quantised" in moe4.moe4_last_error()
+    d = _desc(format=moe4.MOE4_FMT_NF4_DQ, gu_s2=FAKE, dn_s2=FAKE, gu_soff=FAKE, dn_soff=FAKE,
+              dq_book=FAKE, H=96)
+    assert _fwd(d) == moe4.MOE4_ESHAPE
+
+
 def test_router_refusals():
     r = lib.moe4_router_logits
     assert r(FAKE, FAKE, None, 4, 64, 0, FAKE, None) == moe4.MOE4_ESHAPE

@@ -139,6 +139,57 @@ def qwen_layer():
     return BigNF4Layer(inp.QWEN3_30B_NF4)
 
 
+def test_qwen3_30b_a3b_nf4_double_quant_full(qwen_layer):
+    """The full Qwen3-shaped stack with double-quantised absmax: the GPU's
+    compression of its (bit-exact) absmax is bit-exact with the oracle's
+    compression of the oracle's own absmax; the layer runs at a decode and a
+    prefill token count on the nested form."""
+    spec = inp.QWEN3_30B_NF4
+    L = qwen_layer
+    book = inp.dq_code_book("dynamic")
+    say("  oracle absmax of every expert (host quantisation of the seeded source)")
+    ga, da = [], []
+    for e in range(spec.E):
+        g, d = inp.host_nf4_source(spec, e, L.layer, L.seed)
+        ga.append(oracle.quantize_nf4(g.reshape(-1))[1])
+        da.append(oracle.quantize_nf4(d.reshape(-1))[1])
+    ref = {"gu": oracle.compress_absmax(np.concatenate(ga), book),
+           "dn": oracle.compress_absmax(np.concatenate(da), book)}
+    dev = {}
+    ws = torch.empty(moe4.MOE4_DQ_WS_BYTES, dtype=torch.uint8, device=DEV)
+    for name, a in (("gu", L.gs), ("dn", L.ds)):
+        n = a.numel()
+        code = torch.empty(a.shape, dtype=torch.uint8, device=DEV)
+        a2 = torch.empty((n + 255) // 256, dtype=torch.float32, device=DEV)
+        off = torch.empty(1, dtype=torch.float32, device=DEV)
+        moe4.moe4_compress_absmax(a.reshape(-1), to_dev(book), code, a2, off, ws)
+        torch.cuda.synchronize()
+        rc, ra2, roff = ref[name]
+        assert off.cpu().numpy()[0] == roff
+        assert np.array_equal(code.cpu().numpy().reshape(-1), rc)
+        assert np.array_equal(a2.cpu().numpy().view(np.uint32), ra2.view(np.uint32))
+        dev[name] = (code, a2, off)
+    exp = {k: oracle.expand_absmax(*ref[k], book) for k in ref}
+    I, H = spec.I, spec.H
+    ng, nd = 2 * I * H // 64, H * I // 64
+
+    def expert(e):
+        q = L.oracle_expert(e)
+        return (q[0], exp["gu"][e * ng:(e + 1) * ng], q[2], exp["dn"][e * nd:(e + 1) * nd])
+
+    W = oracle.ExpertWeights(
+        E=spec.E, H=H, I=I, layout=spec.layout, act=spec.act,
+        gu=lambda e: oracle.dequantize_nf4_bf16(*expert(e)[:2]).reshape(2 * I, H),
+        dn=lambda e: oracle.dequantize_nf4_bf16(*expert(e)[2:]).reshape(H, I))
+    (gc, ga2, goff), (dc, da2, doff) = dev["gu"], dev["dn"]
+    ex = moe4.Experts(moe4.MOE4_FMT_NF4_DQ, L.gq, gc, L.dq, dc, gu_layout=moe4.MOE4_GU_HALVES,
+                      act=moe4.MOE4_ACT_SWIGLU, E=spec.E, H=H, I=I, gu_s2=ga2, dn_s2=da2,
+                      gu_soff=goff, dn_soff=doff, dq_book=to_dev(book))
+    for T in (16, 4096):
+        say(f"  T={T}")
+        _check_layer(spec, W, ex, T, 6)
+
+
 @pytest.fixture(scope="module")
 def gptoss_layer():
     say("building the gpt-oss-20b-shaped MXFP4 stack")

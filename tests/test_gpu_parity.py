@@ -141,6 +141,117 @@ def test_convert_mxfp4_nf4_bit_exact():
                                 torch.empty((0, 1), dtype=torch.float32, device=DEV))
 
 
+# ------------------------------------------------ double-quantised absmax
+
+def _gpu_compress(a, book):
+    n = a.size
+    code = torch.empty(n, dtype=torch.uint8, device=DEV)
+    a2 = torch.empty((n + 255) // 256, dtype=torch.float32, device=DEV)
+    off = torch.empty(1, dtype=torch.float32, device=DEV)
+    ws = torch.empty(moe4.MOE4_DQ_WS_BYTES, dtype=torch.uint8, device=DEV)
+    moe4.moe4_compress_absmax(to_dev(a.reshape(-1)), to_dev(book), code, a2, off, ws)
+    torch.cuda.synchronize()
+    return code, a2, off
+
+
+def test_compress_expand_absmax_bit_exact():
+    say("compress/expand absmax: small stacks, ragged, large, constant; two code books")
+    L = layer_of(QWEN_SMALL)
+    rng = np.random.default_rng(22)
+    arrays = [L.gu_s, np.ascontiguousarray(L.dn_s[:, :37]),
+              (np.abs(rng.standard_normal(256 * 3000 + 13)) * 0.05).astype(np.float32),
+              np.full(700, 0.03125, np.float32)]
+    for kind in ("dynamic", "linear"):
+        book = inp.dq_code_book(kind)
+        for a in arrays:
+            code, a2, off = _gpu_compress(a, book)
+            rc, ra2, roff = oracle.compress_absmax(a, book)
+            assert off.cpu().numpy()[0] == roff
+            assert np.array_equal(a2.cpu().numpy().view(np.uint32), ra2.view(np.uint32))
+            assert np.array_equal(code.cpu().numpy(), rc)
+            out = torch.empty(a.size, dtype=torch.float32, device=DEV)
+            moe4.moe4_expand_absmax(code, a2, off, to_dev(book), out)
+            torch.cuda.synchronize()
+            want = oracle.expand_absmax(rc, ra2, roff, book)
+            assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+class DQLayer:
+    """An NF4 layer whose absmax is double-quantised on the GPU (bit-exact with
+    the oracle's), and the oracle's weights built on the decoded absmax."""
+
+    def __init__(self, spec, kind="dynamic"):
+        L = layer_of(spec)
+        self.L, self.spec = L, spec
+        self.book = inp.dq_code_book(kind)
+        self.dev = {}
+        expanded = []
+        for name, a in (("gu", L.gu_s), ("dn", L.dn_s)):
+            code, a2, off = _gpu_compress(a, self.book)
+            rc, ra2, roff = oracle.compress_absmax(a, self.book)
+            assert np.array_equal(code.cpu().numpy(), rc) and off.cpu().numpy()[0] == roff
+            self.dev[name] = (code.view(a.shape), a2, off)
+            expanded.append(oracle.expand_absmax(rc, ra2, roff, self.book).reshape(a.shape))
+        kw = dict(layout=spec.layout, act=spec.act, lora_A=L.lora_A, lora_B=L.lora_B,
+                  lora_scale=spec.lora_scale)
+        self.W = oracle.ExpertWeights.from_nf4(L.gu_q, expanded[0], L.dn_q, expanded[1], **kw)
+
+    def device(self, variant=0):
+        L, s = self.L, self.spec
+        t = lambda a: None if a is None else to_dev(a)
+        (gc, ga2, goff), (dc, da2, doff) = self.dev["gu"], self.dev["dn"]
+        return moe4.Experts(moe4.MOE4_FMT_NF4_DQ, t(L.gu_q), gc, t(L.dn_q), dc,
+                            gu_layout=moe4.MOE4_GU_HALVES, act=moe4.MOE4_ACT_SWIGLU,
+                            E=s.E, H=s.H, I=s.I, lora_A=t(L.lora_A), lora_B=t(L.lora_B),
+                            lora_scale=s.lora_scale, variant=variant, gu_s2=ga2, dn_s2=da2,
+                            gu_soff=goff, dn_soff=doff, dq_book=to_dev(self.book))
+
+
+DQ_CASES = [(QWEN_SMALL, 5, "dynamic"), (QWEN_SMALL, 100, "linear"), (LORA_SMALL, 150, "dynamic")]
+
+
+@pytest.mark.parametrize("variant", [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED])
+@pytest.mark.parametrize("spec,T,kind", DQ_CASES, ids=[f"{s.name}-T{t}-{k}" for s, t, k in DQ_CASES])
+def test_layer_forward_double_quant(spec, T, kind, variant):
+    say(f"forward, double-quantised absmax: {spec.name} T={T} book={kind} variant={variant}")
+    D = DQLayer(spec, kind)
+    x, lg = inp.host_tokens(spec, T)
+    res = run_layer(D.device(variant), to_dev(x), to_dev(lg), spec.k, save=True)
+    assert res["variant"] == variant
+    ri, rw = oracle.route(lg, spec.k)
+    ref = oracle.layer_forward(x, ri, rw, D.W, keep=True)
+    assert_close(res["save_gu"].cpu().numpy(), ref["gu"], "gu")
+    assert_close(res["y_perm"].cpu().numpy(), ref["y"], "y_perm")
+    assert_close(res["out32"].cpu().numpy(), ref["out"], "out")
+
+
+def test_layer_backward_double_quant():
+    spec, T = LORA_SMALL, 150
+    say(f"backward, double-quantised absmax: {spec.name} T={T}")
+    D = DQLayer(spec)
+    ex = D.device()
+    x, lg = inp.host_tokens(spec, T)
+    dout = inp.host_upstream_grad(spec, T)
+    res = run_layer(ex, to_dev(x), to_dev(lg), spec.k, save=True)
+    S = T * spec.k
+    dy = torch.empty((S, spec.H), dtype=torch.bfloat16, device=DEV)
+    e0 = torch.empty(S, dtype=torch.int32, device=DEV)
+    moe4.moe4_permute(res["idx"], spec.E, torch.empty_like(res["offsets"]), e0,
+                      torch.empty_like(e0), x=to_dev(dout), row_scale=res["w"].reshape(-1),
+                      x_perm=dy, ws=res["ws"])
+    dx_perm = torch.empty((S, spec.H), dtype=torch.float32, device=DEV)
+    dA = torch.empty((spec.E, spec.lora_r, spec.H), device=DEV)
+    dB = torch.empty((spec.E, 2 * spec.I, spec.lora_r), device=DEV)
+    moe4.moe4_expert_backward(ex, res["x_perm"], res["offsets"], res["save_gu"], res["save_xa"],
+                              dy, dx_perm, dA, dB, ws=res["ws"])
+    torch.cuda.synchronize()
+    ri, rw = oracle.route(lg, spec.k)
+    ref = oracle.layer_backward(x, ri, rw, dout, D.W)
+    assert_close(dx_perm.cpu().numpy(), ref["dx_perm"], "dx_perm")
+    assert_close(dA.cpu().numpy(), ref["dA"], "dA")
+    assert_close(dB.cpu().numpy(), ref["dB"], "dB")
+
+
 # --------------------------------------------------------------- router step
 
 def router_case(T, E, H, seed, bias=True):
