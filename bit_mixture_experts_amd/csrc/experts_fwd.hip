@@ -291,17 +291,27 @@ void k_skinny(const GemmArgs a) {
 
 // ------------------------------------------------------------- tiled kernel
 
-constexpr int kBM = 128, kBK = 64, kStages = 3;
-// One LDS stage holds a k-tile of 64: the A tile [128 rows][128 B] with the
+// One workgroup per CU: eight waves, an expert tile of up to kBM rows and 256
+// weight rows (gate_up: 128 (gate, up) pairs; down: 256 output columns).
+// Wave w owns 32 of the weight rows -- one 32-wide MFMA column tile -- against
+// every row of the tile, so each weight is dequantised once per workgroup and
+// each wave's dequantisation work per MFMA is a quarter of a 128-row tile's
+// with two column tiles per wave. An expert whose rows fit in kBM takes one
+// tile; larger experts are cut into equal tiles (multiples of 32 rows).
+constexpr int kBM = 320, kBN = 256, kBK = 64, kStages = 3, kTiledWaves = 8;
+constexpr int kMaxRowTiles = kBM / 32;
+// One LDS stage holds a k-tile of 64: the A tile [kBM rows][128 B] with the
 // 16-byte chunks of row r stored at chunk ^ (r & 7) (conflict-free MFMA
-// operand reads), each wave's packed nibbles [c][32 rows][32 B], and each
-// wave's scales (NF4: [c][32] fp32; MXFP4: [h][c][32] e8m0 bytes, each in
-// the low byte of a 4-byte slot: sub-dword loads to LDS advance 4 bytes a lane).
+// operand reads), each wave's packed nibbles [32 rows][32 B], and each wave's
+// scales in 4-byte slots (NF4: slot n = row n's fp32 absmax; MXFP4: slot
+// 32 h + n = the e8m0 byte of half h of row n; sub-dword loads to LDS advance
+// 4 bytes a lane).
 constexpr int kStageA = kBM * kBK * 2;
-constexpr int kStageB = 4 * 2 * 32 * 32;
-constexpr int kStageS = 4 * 512;
+constexpr int kStageB = kTiledWaves * 32 * 32;
+constexpr int kStageS = kTiledWaves * 64 * 4;
 constexpr int kStageBytes = kStageA + kStageB + kStageS;
 constexpr int kTiledLds = kStages * kStageBytes;
+static_assert(kTiledLds + 256 * 8 <= 160 * 1024, "tiled kernel LDS");
 
 #define MOE4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -319,53 +329,93 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Tiled grouped GEMM: one workgroup = one 128-row tile of one expert's
-// permuted rows x 128 output columns (gate_up: 128 (gate, up) pairs, i.e. 256
-// weight rows; down: 256 output columns); wave w owns 64 weight rows (two
-// 32-column MFMA tiles) against all 128 rows. The activations, nibbles and
-// scales of k-tile kt+2 stream into LDS by buffer loads straight to LDS while
-// k-tile kt is multiplied (three stages, one barrier per k-tile); rows past
-// the tile, k past K and weight rows past the stack read as zeros.
+// Row tiles of an expert with n rows: ceil(n / kBM) tiles of R rows each
+// (R a multiple of 32), the last one shorter.
+__device__ __forceinline__ int tiles_of(int n) { return (n + kBM - 1) / kBM; }
+__device__ __forceinline__ int tile_rows(int n) {
+  const int nt = tiles_of(n);
+  return nt ? ((n + nt - 1) / nt + 31) / 32 * 32 : 0;
+}
+
+// Work item of workgroup b: (expert e, row tile u, column group cg). Items are
+// (tile, column group) pairs, column group fastest, experts in order. The
+// dispatcher deals workgroup ids round-robin over the 8 XCDs (each with its
+// own L2); XCD x gets a contiguous 1/8 of the items, so the column groups of
+// one tile (which share its activation rows) and the tiles of one expert
+// (which share its weights) stay on one XCD. The grid needs at least
+// items + 8 workgroups; the rest get e = -1.
+__device__ __forceinline__ void locate_tile(const int32_t* __restrict__ offsets, int E, int ncg,
+                                            int b, int& e_out, int& u_out, int& cg_out) {
+  constexpr int kXcd = 8;
+  const int l = lane_id();
+  const int per = (E + kWave - 1) / kWave;
+  const int e0 = l * per;
+  int nt = 0;
+  if (e0 < E) {
+    int prev = offsets[e0];
+    for (int i = 0; i < per && e0 + i < E; ++i) {
+      const int nx = offsets[e0 + i + 1];
+      nt += tiles_of(nx - prev);
+      prev = nx;
+    }
+  }
+  const int N = __shfl(wave_inclusive_scan(nt), kWave - 1, kWave) * ncg;
+  const int x = b % kXcd, i = b / kXcd;
+  const int f0 = (int)((int64_t)N * x / kXcd), f1 = (int)((int64_t)N * (x + 1) / kXcd);
+  int e = -1, u = 0, item = 0;
+  if (i < f1 - f0) {
+    item = f0 + i;
+    locate_item(offsets, E, item / ncg, [](int n) { return tiles_of(n); }, e, u);
+  }
+  e_out = e;
+  u_out = u;
+  cg_out = item % ncg;
+}
+
 template <int FMT, bool GATEUP>
-__global__ __launch_bounds__(256, 2) void k_tiled(const GemmArgs a) {
+__global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   using F = Format<FMT>;
   constexpr bool NF4 = FMT == MOE4_FMT_NF4;
   constexpr int KB = F::kBlock;
-  constexpr int kLoadsPerTile = 4 + 2 + (NF4 ? 1 : 2);
+  constexpr int kLoadsPerTile = kBM / 64 + 1 + 1;
   __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t stage_mem[];
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  if (NF4) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
+  if (NF4 && tid < 256) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
   int e, ut, cg;
-  locate_tile_xcd<kBM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
+  locate_tile(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
   // wave-uniform by construction; make it visible to the compiler so that the
   // buffer resources below live in scalar registers
   e = __builtin_amdgcn_readfirstlane(e);
   ut = __builtin_amdgcn_readfirstlane(ut);
+  cg = __builtin_amdgcn_readfirstlane(cg);
   __syncthreads();
   if (e < 0) return;
   const int K = a.K;
-  const int row0 = min(a.offsets[e], a.rows) + ut * kBM;
-  const int nrows = min(kBM, min(a.offsets[e + 1], a.rows) - row0);
+  const int ebeg = min(a.offsets[e], a.rows);
+  const int n_e = min(a.offsets[e + 1], a.rows) - ebeg;
+  const int R = tile_rows(n_e);
+  const int row0 = ebeg + ut * R;
+  const int nrows = min(R, ebeg + n_e - row0);
   const int nrt = (nrows + 31) >> 5;
   const int n32 = l & 31, h = l >> 5;
   const int Nw = GATEUP ? 2 * a.I : a.N_out;
-  // weight rows of this wave's two column tiles, as seen by MFMA lane n32
-  int wrow[2];
-  bool tact[2];
-  if (GATEUP) {
-    const int jb = cg * 128 + w * 32;
-    tact[0] = tact[1] = jb < a.I;
-    const int j = tact[0] ? jb + n32 : 0;
-    wrow[0] = gate_row(a.layout, a.I, j);
-    wrow[1] = up_row(a.layout, a.I, j);
-  } else {
-    const int c0 = cg * 256 + w * 64;
-    tact[0] = c0 < a.N_out;
-    tact[1] = c0 + 32 < a.N_out;
-    wrow[0] = tact[0] ? c0 + n32 : 0;
-    wrow[1] = tact[1] ? c0 + 32 + n32 : 0;
-  }
+
+  // weight row of MFMA column n of this wave (gate_up: columns 0..15 are the
+  // gate rows of pairs j0 .. j0+15, columns 16..31 their up rows)
+  const int j0 = cg * 128 + w * 16;
+  auto wrow_of = [&](int n, bool& on) {
+    if (GATEUP) {
+      const int j = j0 + (n & 15);
+      on = j < a.I;
+      const int jj = on ? j : 0;
+      return n < 16 ? gate_row(a.layout, a.I, jj) : up_row(a.layout, a.I, jj);
+    }
+    const int c = cg * kBN + w * 32 + n;
+    on = c < a.N_out;
+    return on ? c : 0;
+  };
+
   const rsrc_t ra = make_rsrc(a.A + (int64_t)row0 * K, (uint32_t)nrows * K * 2);
   const rsrc_t rq = make_rsrc(a.wq + (int64_t)e * Nw * (K / 2), (uint32_t)Nw * (K / 2));
   constexpr int sbytes = NF4 ? 4 : 1;
@@ -373,30 +423,22 @@ __global__ __launch_bounds__(256, 2) void k_tiled(const GemmArgs a) {
                               (uint32_t)Nw * (K / KB) * sbytes);
 
   // ---- loader roles (lane-contiguous LDS destinations)
-  // A: load i of lane (w, l) fills LDS bytes i*4096 + w*1024 + 16*l of the A
-  //    tile = row 32i + 8w + l/8, physical chunk l%8 = logical chunk ^ (row & 7)
-  int a_off[4], a_col[4];
+  // A: load p of lane (w, l) fills LDS bytes p*8192 + w*1024 + 16*l of the A
+  //    tile = row 64p + 8w + l/8, physical chunk l%8 = logical chunk ^ (row & 7)
+  int a_off[kBM / 64], a_col[kBM / 64];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 32 * i + 8 * w + (l >> 3);
-    a_col[i] = 8 * ((l & 7) ^ (row & 7));
-    a_off[i] = (row * K + a_col[i]) * 2;
+  for (int p = 0; p < kBM / 64; ++p) {
+    const int row = 64 * p + 8 * w + (l >> 3);
+    a_col[p] = 8 * ((l & 7) ^ (row & 7));
+    a_off[p] = (row * K + a_col[p]) * 2;
   }
-  // B: load c of lane l fills [c][l/2][16*(l%2)] of this wave's nibble block
-  //    (weight row of column-tile lane n = l/2, bytes 16*(l%2) of the k-tile)
-  const int bn = l >> 1;
-  int b_off[2];
-  bool b_on[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int n = __shfl(wrow[c], bn, kWave);
-    b_on[c] = tact[c];
-    b_off[c] = n * (K / 2) + 16 * (l & 1);
-  }
-  // scales: lane l covers column tile c = l/32, lane n = l%32
-  const int s_row0 = __shfl(wrow[0], l & 31, kWave), s_row1 = __shfl(wrow[1], l & 31, kWave);
-  const int s_row = (l >> 5) ? s_row1 : s_row0;
-  const bool s_on = tact[l >> 5];
+  // B: lane l fills [l/2][16 (l%2)] of this wave's nibble block (row n = l/2,
+  //    bytes 16 (l%2) of the k-tile's 32)
+  bool b_on;
+  const int b_off = wrow_of(l >> 1, b_on) * (K / 2) + 16 * (l & 1);
+  // scales: NF4 lane l < 32 covers row l; MXFP4 lane l covers half l/32 of row l%32
+  bool s_on;
+  const int s_row = wrow_of(n32, s_on);
   const int s_off = s_row * (K / KB) * sbytes;
 
   auto stage = [&](int st) { return stage_mem + st * kStageBytes; };
@@ -404,46 +446,39 @@ __global__ __launch_bounds__(256, 2) void k_tiled(const GemmArgs a) {
     uint8_t* base = stage(kt % kStages);
     const int kb = kt * kBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int p = 0; p < kBM / 64; ++p)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, MOE4_LDS(base + i * 4096 + w * 1024), 16,
-          kb + a_col[i] < K ? a_off[i] + 2 * kb : kOob, 0, 0, 0);
-    uint8_t* bbase = base + kStageA + w * 2048;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rq, MOE4_LDS(bbase + c * 1024), 16,
-          (b_on[c] && kb + 32 * (l & 1) < K) ? b_off[c] + kb / 2 : kOob, 0, 0, 0);
-    uint8_t* sbase = base + kStageA + kStageB + w * 512;
+          ra, MOE4_LDS(base + p * 8192 + w * 1024), 16,
+          kb + a_col[p] < K ? a_off[p] + 2 * kb : kOob, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rq, MOE4_LDS(base + kStageA + w * 1024), 16,
+        (b_on && kb + 32 * (l & 1) < K) ? b_off + kb / 2 : kOob, 0, 0, 0);
+    uint8_t* sbase = base + kStageA + kStageB + w * 256;
     if (NF4) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE4_LDS(sbase), 4,
-                                               s_on ? s_off + (kb / 64) * 4 : kOob, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, MOE4_LDS(sbase), 4, (s_on && h == 0) ? s_off + (kb / 64) * 4 : kOob, 0, 0, 0);
     } else {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, MOE4_LDS(sbase + hh * 256), 1,
-            (s_on && kb + 32 * hh < K) ? s_off + kb / 32 + hh : kOob, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, MOE4_LDS(sbase), 1, (s_on && kb + 32 * h < K) ? s_off + kb / 32 + h : kOob, 0, 0,
+          0);
     }
   };
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rt][c][i] = 0.0f;
-
-  // Per k-tile: wait for its loads, dequantise this wave's weights into
-  // registers, then start the loads of k-tile kt+2 and run the MFMAs. (The
-  // table reads of the dequantisation come before the new loads: the compiler
-  // makes LDS table reads wait for every load still streaming into LDS.) The
-  // loop is instantiated per count of live 32-row tiles so that its body is
-  // straight-line code.
+  // Per k-tile: wait for its loads, dequantise this wave's 32 weight rows into
+  // registers (the table reads come before the next loads: the compiler makes
+  // LDS reads wait for loads still streaming into LDS), start the loads of
+  // k-tile kt+2, then run the MFMAs over every live 32-row tile. The loop is
+  // instantiated per count of live row tiles.
   const int nk = (K + kBK - 1) / kBK;
+  bool col_on;
+  const int col_row = wrow_of(n32, col_on);
   auto kloop = [&](auto nrt_c) {
     constexpr int NRT = decltype(nrt_c)::value;
+    f32x16 acc[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rt][i] = 0.0f;
     issue(0);
     if (nk > 1) issue(1);
     for (int kt = 0; kt < nk; ++kt) {
@@ -452,73 +487,126 @@ __global__ __launch_bounds__(256, 2) void k_tiled(const GemmArgs a) {
       lds_barrier();   // k-tile kt is in LDS everywhere; stage (kt+2)%3 is free
       const uint8_t* base = stage(kt % kStages);
       const uint16_t* As = reinterpret_cast<const uint16_t*>(base);
-      const uint8_t* Bw = base + kStageA + w * 2048;
-      const uint8_t* Sw = base + kStageA + kStageB + w * 512;
-      // A operands of MFMA step s for every live row tile (chunk 4h + s of
-      // row rt*32 + n32, stored at chunk ^ (row & 7))
-      auto load_af = [&](bf16x8 (&af)[NRT], int s) {
+      const u32x4 braw =
+          *reinterpret_cast<const u32x4*>(base + kStageA + w * 1024 + n32 * 32 + 16 * h);
+      const uint8_t* Sw = base + kStageA + kStageB + w * 256;
+      const float sc = NF4 ? reinterpret_cast<const float*>(Sw)[n32]
+                           : __uint_as_float((uint32_t)Sw[(h * 32 + n32) * 4] << 23);
+      u32x4 bq[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bq[s] = dequant8<FMT>(braw[s], sc, lutf);
+      if (kt + 2 < nk) issue(kt + 2);
+      // A operand of row tile rt, step s: chunk 4h + s of row 32 rt + n32
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
           const int row = rt * 32 + n32;
-          af[rt] = *reinterpret_cast<const bf16x8*>(As + row * kBK + (((4 * h + s) ^ (row & 7)) * 8));
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+              As + row * kBK + (((4 * h + s) ^ (row & 7)) * 8));
+          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              af, __builtin_bit_cast(bf16x8, bq[s]), acc[rt], 0, 0, 0);
         }
-      };
-      bf16x8 af0[NRT], af1[NRT];
-      load_af(af0, 0);
-      u32x4 bq[2][4];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4 braw = *reinterpret_cast<const u32x4*>(Bw + c * 1024 + n32 * 32 + 16 * h);
-        const float sc = NF4 ? reinterpret_cast<const float*>(Sw)[c * 32 + n32]
-                             : __uint_as_float((uint32_t)Sw[h * 256 + (c * 32 + n32) * 4] << 23);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bq[c][s] = dequant8<FMT>(braw[s], sc, lutf);
-        // keep the two column tiles' table reads apart (register pressure)
-        if (NF4 && c == 0) __builtin_amdgcn_sched_barrier(0);
       }
-      if (kt + 2 < nk) issue(kt + 2);
-      auto mfmas = [&](const bf16x8 (&af)[NRT], int s) {
+    }
+    // ---- epilogue. Lane holds column n32 of each 32x32 tile, rows
+    // 8*(i/4) + 4*h + i%4. Per-column constants (bias, LoRA row) are read once.
+    if constexpr (GATEUP) {
+      // The gate of pair j0 + n sits in column n, its up in column n + 16 (same
+      // rows): a shuffle gives each lane the pair; lanes n32 < 16 finish entries
+      // i < 8 and lanes n32 >= 16 entries i >= 8. h is staged through LDS (the
+      // stages are free once every wave is past its last k-tile) and written
+      // out as whole 16-byte chunks of each row.
+      const int jl = n32 & 15, j = j0 + jl;
+      const bool jon = j < a.I;
+      const int ng = gate_row(a.layout, a.I, jon ? j : 0), nu = up_row(a.layout, a.I, jon ? j : 0);
+      float bg = 0.0f, bu = 0.0f;
+      if (a.bias && jon) {
+        bg = bf16_to_f32(a.bias[(int64_t)e * 2 * a.I + ng]);
+        bu = bf16_to_f32(a.bias[(int64_t)e * 2 * a.I + nu]);
+      }
+      const bool gate_lane = n32 < 16;
+      uint16_t* hs = reinterpret_cast<uint16_t*>(stage_mem);   // [kBM][128] bf16
+      // both activations in one branch-free form: h = gc sigma(al gc) (uc + c1),
+      // gc = min(g, lim), uc = clamp(u, -lim, lim); SwiGLU is al = 1, lim = inf,
+      // c1 = 0
+      const bool clamped = a.act == MOE4_ACT_SWIGLU_CLAMPED;
+      const float al = clamped ? a.alpha : 1.0f;
+      const float lim = clamped ? a.limit : __int_as_float(0x7F800000);
+      const float c1 = clamped ? 1.0f : 0.0f;
+      const bool extra = a.r || a.save_gu;   // LoRA term or saved pre-activations
+      __syncthreads();
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
+      for (int rt = 0; rt < NRT; ++rt) {
+        // entry i' < 8 of a gate lane and entry i' + 8 of an up lane are
+        // finished by that lane; each sends the partner the other half
+        typedef float f32x8 __attribute__((ext_vector_type(8)));
+        const f32x8 lo = __builtin_shufflevector(acc[rt], acc[rt], 0, 1, 2, 3, 4, 5, 6, 7);
+        const f32x8 hi = __builtin_shufflevector(acc[rt], acc[rt], 8, 9, 10, 11, 12, 13, 14, 15);
+        const f32x8 send = gate_lane ? hi : lo, keep = gate_lane ? lo : hi;
+        float recv[8];
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
-            acc[rt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                af[rt], __builtin_bit_cast(bf16x8, bq[c][s]), acc[rt][c], 0, 0, 0);
-      };
-      // operands of step s+1 are read while step s multiplies
-      load_af(af1, 1);
-      mfmas(af0, 0);
-      load_af(af0, 2);
-      mfmas(af1, 1);
-      load_af(af1, 3);
-      mfmas(af0, 2);
-      mfmas(af1, 3);
+        for (int q = 0; q < 8; ++q) recv[q] = __shfl_xor(send[q], 16, kWave);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float mine = keep[q];
+          float g = (gate_lane ? mine : recv[q]) + bg;
+          float u = (gate_lane ? recv[q] : mine) + bu;
+          const int rt_row = rt * 32 + 8 * (q >> 2) + (gate_lane ? 0 : 16) + 4 * h + (q & 3);
+          if (rt_row < nrows && jon) {
+            if (extra) {
+              const int row = row0 + rt_row;
+              if (a.r) {
+                g += lora_term(a, e, row, ng);
+                u += lora_term(a, e, row, nu);
+              }
+              if (a.save_gu) {
+                float* sg = a.save_gu + (int64_t)row * 2 * a.I;
+                sg[ng] = g;
+                sg[nu] = u;
+              }
+            }
+            const float gc = fminf(g, lim);
+            const float uc = fminf(fmaxf(u, -lim), lim);
+            hs[rt_row * 128 + w * 16 + jl] = f32_to_bf16(gc * sigmoidf_(al * gc) * (uc + c1));
+          }
+        }
+      }
+      __syncthreads();
+      const int pbase = cg * 128;
+      for (int idx = tid; idx < nrows * 16; idx += 64 * kTiledWaves) {
+        const int r = idx >> 4, c = idx & 15;
+        if (pbase + 8 * c < a.I)
+          __builtin_nontemporal_store(
+              *reinterpret_cast<const u32x4*>(hs + r * 128 + 8 * c),
+              reinterpret_cast<u32x4*>(a.hout + (int64_t)(row0 + r) * a.I + pbase + 8 * c));
+      }
+    } else {
+      const float bd = (a.bias && col_on) ? bf16_to_f32(a.bias[(int64_t)e * a.N_out + col_row]) : 0.0f;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int rt_row = rt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (col_on && rt_row < nrows)
+            __builtin_nontemporal_store(acc[rt][i] + bd,
+                                        a.yout + (int64_t)(row0 + rt_row) * a.N_out + col_row);
+        }
+      }
     }
   };
   switch (nrt) {
     case 1: kloop(std::integral_constant<int, 1>{}); break;
     case 2: kloop(std::integral_constant<int, 2>{}); break;
     case 3: kloop(std::integral_constant<int, 3>{}); break;
-    default: kloop(std::integral_constant<int, 4>{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 5: kloop(std::integral_constant<int, 5>{}); break;
+    case 6: kloop(std::integral_constant<int, 6>{}); break;
+    case 7: kloop(std::integral_constant<int, 7>{}); break;
+    case 8: kloop(std::integral_constant<int, 8>{}); break;
+    case 9: kloop(std::integral_constant<int, 9>{}); break;
+    default: kloop(std::integral_constant<int, 10>{}); break;
   }
-
-  // epilogue: lane holds column n32 of each 32x32 tile, rows 8*(i/4) + 4*h + i%4
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rt_row = rt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (rt_row < nrows) {
-        const int row = row0 + rt_row;
-        if (GATEUP) {
-          if (tact[0])
-            gate_up_epilogue(a, e, row, cg * 128 + w * 32 + n32, acc[rt][0][i], acc[rt][1][i]);
-        } else {
-          if (tact[0]) down_epilogue(a, e, row, wrow[0], acc[rt][0][i]);
-          if (tact[1]) down_epilogue(a, e, row, wrow[1], acc[rt][1][i]);
-        }
-      }
-    }
 }
 
 // -------------------------------------------------------------- LoRA x A^T
@@ -568,14 +656,15 @@ hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
 template <int FMT, bool GATEUP>
 hipError_t run_tiled(const GemmArgs& a, int ntiles, hipStream_t s) {
   if (ntiles == 0) return hipSuccess;
-  // ntiles bounds full + partial tiles; 16 spare ids keep every XCD's share
-  // of the items within the ids it is dealt
-  const int nwg = ntiles * a.ncg + 16;
+  // ntiles bounds the row tiles; 8 spare ids keep every XCD's share of the
+  // items within the ids it is dealt
+  const int nwg = ntiles * a.ncg + 8;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tiled<FMT, GATEUP>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kTiledLds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_tiled<FMT, GATEUP>), dim3(nwg), dim3(256), kTiledLds, s, a);
+  hipLaunchKernelGGL((k_tiled<FMT, GATEUP>), dim3(nwg), dim3(64 * kTiledWaves), kTiledLds, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -645,9 +734,10 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
   if constexpr (FMT == MOE4_FMT_NF4_DQ) {
     return hipErrorInvalidValue;   // the tiled kernels take the expanded (plain NF4) view
   } else {
+    // row tiles: at most rows / kBM + (one per touched expert)
     const int ntiles = rows / kBM + touched;
     g.ncg = (I + 127) / 128;
-    d.ncg = (H + 255) / 256;
+    d.ncg = (H + kBN - 1) / kBN;
     le.before(0, s);
     err = run_tiled<FMT, true>(g, ntiles, s);
     le.after(0, s);
