@@ -45,7 +45,10 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float sc, const float2* lu
   if constexpr (FMT != MOE4_FMT_MXFP4) {
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
-      const float2 v = lutf[(w >> (8 * bi)) & 255u];
+      // read through the vector type: the compiler then leaves these reads
+      // free of a wait for every LDS-DMA load in flight (the loop's own
+      // counted waits and barriers order them)
+      const f32x2 v = reinterpret_cast<const f32x2*>(lutf)[(w >> (8 * bi)) & 255u];
       r[bi] = pack_bf16x2(v.x * sc, v.y * sc);
     }
   } else {
@@ -55,6 +58,29 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float sc, const float2* lu
     r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
   }
   return r;
+}
+
+// dequant8 in two parts, so that the table reads can be issued well before
+// the arithmetic: fetch8 reads the NF4 levels of the dword's four bytes,
+// apply8 scales and rounds them (MXFP4: the hardware conversion of w).
+template <int FMT>
+__device__ __forceinline__ void fetch8(uint32_t w, const float2* lutf, f32x2 (&v)[4]) {
+  if constexpr (FMT != MOE4_FMT_MXFP4) {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+      v[bi] = reinterpret_cast<const f32x2*>(lutf)[(w >> (8 * bi)) & 255u];
+  }
+}
+template <int FMT>
+__device__ __forceinline__ u32x4 apply8(uint32_t w, const f32x2 (&v)[4], float sc) {
+  if constexpr (FMT != MOE4_FMT_MXFP4) {
+    u32x4 r;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) r[bi] = pack_bf16x2(v[bi].x * sc, v[bi].y * sc);
+    return r;
+  } else {
+    return dequant8<FMT>(w, sc, nullptr);
+  }
 }
 
 // scale operand of dequant8 from a raw scale word: NF4 fp32 absmax bits, or an
@@ -301,11 +327,15 @@ void k_skinny(const GemmArgs a) {
 constexpr int kBM = 320, kBN = 256, kBK = 64, kStages = 3, kTiledWaves = 8;
 constexpr int kMaxRowTiles = kBM / 32;
 // One LDS stage holds a k-tile of 64: the A tile [kBM rows][128 B] with the
-// 16-byte chunks of row r stored at chunk ^ (r & 7) (conflict-free MFMA
-// operand reads), each wave's packed nibbles [32 rows][32 B], and each wave's
+// 16-byte chunks of row r stored at chunk ^ ((r >> 1) & 7), each wave's packed
+// nibbles [32 rows][32 B], and each wave's
 // scales in 4-byte slots (NF4: slot n = row n's fp32 absmax; MXFP4: slot
 // 32 h + n = the e8m0 byte of half h of row n; sub-dword loads to LDS advance
 // 4 bytes a lane).
+// The LDS has 64 four-byte banks: a 16-byte operand read serves 16 lanes
+// (rows r .. r+15 of one chunk column) per pass, and rows r and r + 1 share a
+// 256-byte bank line, so the swizzle keys on r / 2 to give those 16 rows 16
+// different 16-byte bank groups.
 constexpr int kStageA = kBM * kBK * 2;
 constexpr int kStageB = kTiledWaves * 32 * 32;
 constexpr int kStageS = kTiledWaves * 64 * 4;
@@ -424,14 +454,11 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
 
   // ---- loader roles (lane-contiguous LDS destinations)
   // A: load p of lane (w, l) fills LDS bytes p*8192 + w*1024 + 16*l of the A
-  //    tile = row 64p + 8w + l/8, physical chunk l%8 = logical chunk ^ (row & 7)
-  int a_off[kBM / 64], a_col[kBM / 64];
-#pragma unroll
-  for (int p = 0; p < kBM / 64; ++p) {
-    const int row = 64 * p + 8 * w + (l >> 3);
-    a_col[p] = 8 * ((l & 7) ^ (row & 7));
-    a_off[p] = (row * K + a_col[p]) * 2;
-  }
+  //    tile = row 64p + 8w + l/8, physical chunk l%8 = logical chunk ^ ((row >> 1) & 7)
+  //    ((row >> 1) & 7 does not depend on p: load p is load 0 moved down 64
+  //    rows, an offset passed in a scalar register)
+  const int a_col = 8 * ((l & 7) ^ (((8 * w + (l >> 3)) >> 1) & 7));
+  const int a_off = ((8 * w + (l >> 3)) * K + a_col) * 2;
   // B: lane l fills [l/2][16 (l%2)] of this wave's nibble block (row n = l/2,
   //    bytes 16 (l%2) of the k-tile's 32)
   bool b_on;
@@ -442,33 +469,55 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   const int s_off = s_row * (K / KB) * sbytes;
 
   auto stage = [&](int st) { return stage_mem + st * kStageBytes; };
-  auto issue = [&](int kt) {
-    uint8_t* base = stage(kt % kStages);
+  // Batch j holds the A tile of k-tile j and the wave's weights of k-tile
+  // j + 1, the A tile in stage j % 3 and the weights in stage (j + 1) % 3, so
+  // that a k-tile's weights are in LDS one k-tile before its A tile and can be
+  // dequantised between the MFMAs of the k-tile before.
+  auto issue_b = [&](int kt, int st) {
+    uint8_t* base = stage(st);
     const int kb = kt * kBK;
-#pragma unroll
-    for (int p = 0; p < kBM / 64; ++p)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, MOE4_LDS(base + p * 8192 + w * 1024), 16,
-          kb + a_col[p] < K ? a_off[p] + 2 * kb : kOob, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rq, MOE4_LDS(base + kStageA + w * 1024), 16,
         (b_on && kb + 32 * (l & 1) < K) ? b_off + kb / 2 : kOob, 0, 0, 0);
     uint8_t* sbase = base + kStageA + kStageB + w * 256;
     if (NF4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, MOE4_LDS(sbase), 4, (s_on && h == 0) ? s_off + (kb / 64) * 4 : kOob, 0, 0, 0);
+          rs, MOE4_LDS(sbase), 4, (s_on && h == 0 && kb < K) ? s_off + (kb / 64) * 4 : kOob, 0,
+          0, 0);
     } else {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, MOE4_LDS(sbase), 1, (s_on && kb + 32 * h < K) ? s_off + kb / 32 + h : kOob, 0, 0,
           0);
     }
   };
+  // part j of batch kt: A load j (j < kBM / 64), else the weights
+  constexpr int kParts = kBM / 64 + 1;
+  auto issue_part = [&](int kt, int j) {
+    if (j < kBM / 64) {
+      const int kb = kt * kBK;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, MOE4_LDS(stage(kt % kStages) + j * 8192 + w * 1024), 16,
+          kb + a_col < K ? a_off + 2 * kb : kOob, j * 64 * K * 2, 0, 0);
+    } else {
+      issue_b(kt + 1, (kt + 1) % kStages);
+    }
+  };
+  auto issue = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < kParts; ++j) issue_part(kt, j);
+  };
+  // this lane's raw nibbles (k 32h .. 32h+31 of row n32) and scale of the
+  // weights in stage st (LDS reads through vector types: see dequant8)
+  auto read_b = [&](int st, u32x4& braw, float& sc) {
+    const uint8_t* base = stage(st);
+    braw = *reinterpret_cast<const u32x4*>(base + kStageA + w * 1024 + n32 * 32 + 16 * h);
+    const f32x2* Sw = reinterpret_cast<const f32x2*>(base + kStageA + kStageB + w * 256);
+    const int slot = NF4 ? n32 : h * 32 + n32;
+    const f32x2 pr = Sw[slot >> 1];
+    const float raw = (slot & 1) ? pr.y : pr.x;
+    sc = NF4 ? raw : __uint_as_float((__float_as_uint(raw) & 255u) << 23);
+  };
 
-  // Per k-tile: wait for its loads, dequantise this wave's 32 weight rows into
-  // registers (the table reads come before the next loads: the compiler makes
-  // LDS reads wait for loads still streaming into LDS), start the loads of
-  // k-tile kt+2, then run the MFMAs over every live 32-row tile. The loop is
-  // instantiated per count of live row tiles.
   const int nk = (K + kBK - 1) / kBK;
   bool col_on;
   const int col_row = wrow_of(n32, col_on);
@@ -479,34 +528,71 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[rt][i] = 0.0f;
+    // A operand f = NRT s + rt of a k-tile: chunk 4h + s of row 32 rt + n32
+    constexpr int kN = 4 * NRT, kPre = 4;
+    auto rd = [&](const uint16_t* As, int f) {
+      const int s = f / NRT, rt = f % NRT, row = rt * 32 + n32;
+      return *reinterpret_cast<const bf16x8*>(As + row * kBK + (((4 * h + s) ^ ((row >> 1) & 7)) * 8));
+    };
+    // Piece p of a k-tile's weights = the bf16 operands of step p (dword p of
+    // the lane's nibbles). Its table reads (NF4) are issued one block of NRT
+    // MFMAs before its arithmetic, which overwrites bq[p] once the MFMAs of
+    // step p of the previous k-tile are issued: in block s of k-tile kt the
+    // wave finishes piece s - 1 of k-tile kt + 1 (s = 0: piece 3 of kt) and
+    // starts the table reads of piece s of kt + 1.
+    u32x4 bq[4];
+    u32x4 braw, braw_n;
+    float sc, sc_n;
+    f32x2 lv[4];
+    issue_b(0, 0);
     issue(0);
     if (nk > 1) issue(1);
+    if (nk > 1) wait_vmcnt<2 * kLoadsPerTile>();
+    else wait_vmcnt<kLoadsPerTile>();
+    read_b(0, braw, sc);   // the wave's own loads: no barrier needed
+#pragma unroll
+    for (int p = 0; p < 3; ++p) bq[p] = dequant8<FMT>(braw[p], sc, lutf);
+    fetch8<FMT>(braw[3], lutf, lv);
+    uint32_t wpend = braw[3];   // nibbles of the piece whose table reads are in lv
+    float scpend = sc;
     for (int kt = 0; kt < nk; ++kt) {
       if (kt + 1 < nk) wait_vmcnt<kLoadsPerTile>();
       else wait_vmcnt<0>();
-      lds_barrier();   // k-tile kt is in LDS everywhere; stage (kt+2)%3 is free
-      const uint8_t* base = stage(kt % kStages);
-      const uint16_t* As = reinterpret_cast<const uint16_t*>(base);
-      const u32x4 braw =
-          *reinterpret_cast<const u32x4*>(base + kStageA + w * 1024 + n32 * 32 + 16 * h);
-      const uint8_t* Sw = base + kStageA + kStageB + w * 256;
-      const float sc = NF4 ? reinterpret_cast<const float*>(Sw)[n32]
-                           : __uint_as_float((uint32_t)Sw[(h * 32 + n32) * 4] << 23);
-      u32x4 bq[4];
+      // batch kt is in LDS everywhere (its weights are k-tile kt + 1's);
+      // stage (kt + 2) % 3's A area and stage kt % 3's B area are free
+      lds_barrier();
+      // batch kt + 2 is issued part by part between the MFMAs below
+      const bool more = kt + 2 < nk;
+      const uint16_t* As = reinterpret_cast<const uint16_t*>(stage(kt % kStages));
+      // after the last k-tile the B area holds zeros or stale nibbles:
+      // decoded and never used
+      read_b((kt + 1) % kStages, braw_n, sc_n);
+      bf16x8 ring[kPre];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bq[s] = dequant8<FMT>(braw[s], sc, lutf);
-      if (kt + 2 < nk) issue(kt + 2);
-      // A operand of row tile rt, step s: chunk 4h + s of row 32 rt + n32
+      for (int f = 0; f < kPre; ++f)
+        if (f < kN) ring[f] = rd(As, f);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-          const int row = rt * 32 + n32;
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(
-              As + row * kBK + (((4 * h + s) ^ (row & 7)) * 8));
-          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              af, __builtin_bit_cast(bf16x8, bq[s]), acc[rt], 0, 0, 0);
+      for (int f = 0; f < kN; ++f) {
+        const int s = f / NRT, rt = f % NRT;
+        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ring[f % kPre], __builtin_bit_cast(bf16x8, bq[s]), acc[rt], 0, 0, 0);
+        if (f + kPre < kN) ring[f % kPre] = rd(As, f + kPre);
+        if (rt == 0) {
+          // finish the pending piece: s = 0 -> piece 3 of k-tile kt, else
+          // piece s - 1 of k-tile kt + 1
+          bq[(s + 3) & 3] = apply8<FMT>(wpend, lv, scpend);
         }
+        if (rt == NRT / 2) {
+          // table reads of piece s of k-tile kt + 1
+          wpend = braw_n[s];
+          scpend = sc_n;
+          fetch8<FMT>(wpend, lutf, lv);
+        }
+#pragma unroll
+        for (int j = 0; j < kParts; ++j)
+          if (f == j * kN / kParts && more) issue_part(kt + 2, j);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // ---- epilogue. Lane holds column n32 of each 32x32 tile, rows
