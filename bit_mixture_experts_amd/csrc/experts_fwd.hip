@@ -595,6 +595,41 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // LoRA delta as a last stretch of the reduction: the rank index q is the
+    // k of extra MFMA steps, operand A = bf16(xa[row][q]) and operand B =
+    // bf16(lora_scale * B[e][n][q]) (zero past r and for idle columns).
+    if constexpr (GATEUP) {
+      if (a.r) {
+        bool on;
+        const int wr = wrow_of(n32, on);
+        const uint16_t* brow = a.loraB + ((int64_t)e * 2 * a.I + wr) * a.r;
+        for (int q0 = 0; q0 < a.r; q0 += 16) {
+          u32x4 bl;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int q = q0 + 8 * h + 2 * jj;
+            const float v0 = (on && q < a.r) ? a.lscale * bf16_to_f32(brow[q]) : 0.0f;
+            const float v1 = (on && q + 1 < a.r) ? a.lscale * bf16_to_f32(brow[q + 1]) : 0.0f;
+            bl[jj] = pack_bf16x2(v0, v1);
+          }
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            const int row = rt * 32 + n32;
+            const float* xr = a.xa + (int64_t)(row0 + row) * a.r;
+            u32x4 al;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int q = q0 + 8 * h + 2 * jj;
+              const float v0 = (row < nrows && q < a.r) ? xr[q] : 0.0f;
+              const float v1 = (row < nrows && q + 1 < a.r) ? xr[q + 1] : 0.0f;
+              al[jj] = pack_bf16x2(v0, v1);
+            }
+            acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, bl), acc[rt], 0, 0, 0);
+          }
+        }
+      }
+    }
     // ---- epilogue. Lane holds column n32 of each 32x32 tile, rows
     // 8*(i/4) + 4*h + i%4. Per-column constants (bias, LoRA row) are read once.
     if constexpr (GATEUP) {
@@ -620,7 +655,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
       const float al = clamped ? a.alpha : 1.0f;
       const float lim = clamped ? a.limit : __int_as_float(0x7F800000);
       const float c1 = clamped ? 1.0f : 0.0f;
-      const bool extra = a.r || a.save_gu;   // LoRA term or saved pre-activations
+      const bool extra = a.save_gu != nullptr;   // saved pre-activations
       __syncthreads();
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
@@ -641,16 +676,9 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
           const int rt_row = rt * 32 + 8 * (q >> 2) + (gate_lane ? 0 : 16) + 4 * h + (q & 3);
           if (rt_row < nrows && jon) {
             if (extra) {
-              const int row = row0 + rt_row;
-              if (a.r) {
-                g += lora_term(a, e, row, ng);
-                u += lora_term(a, e, row, nu);
-              }
-              if (a.save_gu) {
-                float* sg = a.save_gu + (int64_t)row * 2 * a.I;
-                sg[ng] = g;
-                sg[nu] = u;
-              }
+              float* sg = a.save_gu + (int64_t)(row0 + rt_row) * 2 * a.I;
+              sg[ng] = g;
+              sg[nu] = u;
             }
             const float gc = fminf(g, lim);
             const float uc = fminf(fmaxf(u, -lim), lim);
