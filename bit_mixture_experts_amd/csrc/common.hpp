@@ -11,6 +11,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
@@ -189,6 +190,77 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   const int xcd = bid % kXcd, local = bid / kXcd;
   // XCDs < r hold q+1 logical ids, the rest hold q
   return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+}
+
+// ---------------------------------------------------------------- LDS-DMA
+
+#define MOE4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// wait until at most N vector-memory loads of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// wait for every LDS access of this wave (vector-memory loads untouched)
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+// workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding LDS-DMA load); compiler-level ordering only
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ------------------------------------------------------ equal-split row tiles
+
+// Row tiles of an expert with n rows: ceil(n / BM) tiles of R rows each (R a
+// multiple of 32), the last one shorter.
+template <int BM>
+__device__ __forceinline__ int eq_tiles(int n) { return (n + BM - 1) / BM; }
+template <int BM>
+__device__ __forceinline__ int eq_tile_rows(int n) {
+  const int nt = eq_tiles<BM>(n);
+  return nt ? ((n + nt - 1) / nt + 31) / 32 * 32 : 0;
+}
+
+// Work item of workgroup b: (expert e, row tile u, column group cg). Items are
+// (tile, column group) pairs, column group fastest, experts in order. The
+// dispatcher deals workgroup ids round-robin over the 8 XCDs (each with its
+// own L2); XCD x gets a contiguous 1/8 of the items, so the column groups of
+// one tile (which share its activation rows) and the tiles of one expert
+// (which share its weights) stay on one XCD. The grid needs at least
+// items + 8 workgroups; the rest get e = -1.
+template <int BM>
+__device__ __forceinline__ void locate_tile_eq(const int32_t* __restrict__ offsets, int E,
+                                               int ncg, int b, int& e_out, int& u_out,
+                                               int& cg_out) {
+  constexpr int kXcd = 8;
+  const int l = lane_id();
+  const int per = (E + kWave - 1) / kWave;
+  const int e0 = l * per;
+  int nt = 0;
+  if (e0 < E) {
+    int prev = offsets[e0];
+    for (int i = 0; i < per && e0 + i < E; ++i) {
+      const int nx = offsets[e0 + i + 1];
+      nt += eq_tiles<BM>(nx - prev);
+      prev = nx;
+    }
+  }
+  const int N = __shfl(wave_inclusive_scan(nt), kWave - 1, kWave) * ncg;
+  const int x = b % kXcd, i = b / kXcd;
+  const int f0 = (int)((int64_t)N * x / kXcd), f1 = (int)((int64_t)N * (x + 1) / kXcd);
+  int e = -1, u = 0, item = 0;
+  if (i < f1 - f0) {
+    item = f0 + i;
+    locate_item(offsets, E, item / ncg, [](int n) { return eq_tiles<BM>(n); }, e, u);
+  }
+  e_out = e;
+  u_out = u;
+  cg_out = item % ncg;
 }
 
 }  // namespace moe4

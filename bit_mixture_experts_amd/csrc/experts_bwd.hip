@@ -6,9 +6,9 @@
 // fused-experts entry) and get no gradient.
 //
 // The dgrad GEMMs contract over the weight rows, the opposite orientation of
-// the forward: a [32 x 128] tile of packed weights (rows along the reduction)
-// is dequantised by the whole workgroup into LDS, transposed so that each
-// MFMA lane reads 8 consecutive reduction values with one 128-bit LDS load.
+// the forward: each k-tile of packed weights (rows along the reduction) is
+// dequantised by the whole workgroup into LDS, transposed so that each MFMA
+// lane reads 8 consecutive reduction values with one 128-bit LDS load.
 #include "common.hpp"
 #include "formats.hpp"
 #include "gemm_common.hpp"
@@ -16,8 +16,6 @@
 
 namespace moe4 {
 namespace {
-
-constexpr int kDM = 128, kDN = 128, kDK = 32, kDL = kDK + 8;
 
 enum { DGRAD_DOWN = 0, DGRAD_GATEUP = 1 };
 
@@ -55,106 +53,274 @@ __device__ __forceinline__ void act_backward(int act, float g, float u, float dh
   }
 }
 
+// One workgroup per CU: eight waves, an expert tile of up to kGM rows and kGN
+// output columns, k-tiles of kGK weight rows. A k-tile's packed weights
+// [kGK rows][kGN/2 B] and their scales come to LDS by direct loads one k-tile
+// ahead of its activation tile; while the MFMAs of k-tile kt run, every thread
+// dequantises its share of k-tile kt + 1 (8 weight rows x 2 columns) into a
+// transposed bf16 buffer Bt [kGN columns][kGK], which the next k-tile's MFMAs
+// read as their B operand. Wave w computes rows 128 (w / 4) .. +127 and
+// columns 64 (w % 4) .. +63 of the tile (4 x 2 MFMA tiles of 32 x 32).
+constexpr int kGM = 256, kGN = 256, kGK = 32, kGStages = 4;
+// Stage: A [kGM rows][kGK] bf16 (four 16-byte chunks a row, chunk c of row r
+// stored at c ^ ((r >> 2) & 3): 16 consecutive rows of one chunk column fall
+// in 16 different 16-byte bank groups of the 64-bank LDS), the packed weights
+// [kGK rows][kGN / 2 B] (16-byte chunk c of row r stored at c ^ ((r >> 3) & 3),
+// so that the dequantising threads' byte reads spread over the banks), and
+// the scales in 4-byte slots 32 b + r (block b of weight row r: NF4 the fp32
+// absmax, MXFP4 the e8m0 byte).
+constexpr int kGStageA = kGM * kGK * 2;
+constexpr int kGStageB = kGK * kGN / 2;
+constexpr int kGStageS = 1024;
+constexpr int kGStage = kGStageA + kGStageB + kGStageS;
+// Bt [kGN columns][kGK] bf16 at a pitch of 80 bytes: the MFMA operand reads
+// of 16 consecutive columns hit 16 different 16-byte bank groups
+constexpr int kGBtPitch = kGK * 2 + 16;
+constexpr int kGBt = kGN * kGBtPitch;
+constexpr int kGLds = kGStages * kGStage + 2 * kGBt;
+constexpr int kGLoads = 3;   // direct loads per thread and batch
+static_assert(kGLds + 256 * 8 <= 160 * 1024, "dgrad LDS");
+
 template <int FMT, int MODE>
-__global__ __launch_bounds__(256) void k_dgrad(const DgradArgs a) {
+__global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
   using F = Format<FMT>;
+  constexpr bool NF4 = FMT == MOE4_FMT_NF4;
   constexpr int KB = F::kBlock;
-  __shared__ float2 lutf[256];
-  __shared__ __attribute__((aligned(16))) uint16_t As[kDM * kDL];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kDN * kDL];
+  __shared__ __attribute__((aligned(16))) float2 lutf[256];
+  extern __shared__ __attribute__((aligned(16))) uint8_t gmem[];
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
+  if (tid < 256) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
   int e, ut, cg;
-  locate_tile_xcd<kDM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
+  locate_tile_eq<kGM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
   e = __builtin_amdgcn_readfirstlane(e);
   ut = __builtin_amdgcn_readfirstlane(ut);
   cg = __builtin_amdgcn_readfirstlane(cg);
   __syncthreads();
   if (e < 0) return;
-  const int row0 = min(a.offsets[e], a.rows) + ut * kDM;
-  const int nrows = min(kDM, min(a.offsets[e + 1], a.rows) - row0);
-  const int nb = cg * kDN;
-  const int64_t wrow0 = (int64_t)e * a.Kw;
-  const int bytes_per_row = a.Nw / 2;
-  // B loader role: rows kb + 2*kp, +1; columns nb + 8*no .. +8
-  const int kp = tid >> 4, no = tid & 15;
-  const int ncol0 = nb + 8 * no;
-  const bool bcol_ok = ncol0 < a.Nw;
-  const int wm = w >> 1, wn = w & 1, n32 = l & 31, h = l >> 5;
-  f32x16 acc[2][2];
+  const int Kw = a.Kw, Nw = a.Nw;
+  const int ebeg = min(a.offsets[e], a.rows);
+  const int n_e = min(a.offsets[e + 1], a.rows) - ebeg;
+  const int R = eq_tile_rows<kGM>(n_e);
+  const int row0 = ebeg + ut * R;
+  const int nrows = min(R, ebeg + n_e - row0);
+  const int n32 = l & 31, h = l >> 5;
+  const int wr = w >> 2, wc = w & 3;
+  const int nb = cg * kGN;
+
+  const rsrc_t ra = make_rsrc(a.A + (int64_t)row0 * Kw, (uint32_t)nrows * Kw * 2);
+  const rsrc_t rq = make_rsrc(a.wq + (int64_t)e * Kw * (Nw / 2), (uint32_t)Kw * (Nw / 2));
+  constexpr int sbytes = NF4 ? 4 : 1;
+  const rsrc_t rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Kw * (Nw / KB) * sbytes,
+                              (uint32_t)Kw * (Nw / KB) * sbytes);
+  auto stage = [&](int st) { return gmem + st * kGStage; };
+  uint8_t* bt = gmem + kGStages * kGStage;
+
+  // ---- loader roles (lane-contiguous LDS destinations)
+  // A: load p of thread t fills bytes 8192 p + 16 t of the A tile = row
+  //    128 p + t / 4, physical chunk t % 4
+  const int arow = tid >> 2;
+  const int a_col = 8 * ((tid & 3) ^ ((arow >> 2) & 3));
+  const int a_off = (arow * Kw + a_col) * 2;
+  // weights (waves 0..3): thread t fills bytes 16 t of the packed tile = row
+  //    t / 8, physical chunk t % 8 = logical chunk ^ ((row >> 3) & 3)
+  // scales (waves 4..7): thread 256 + i fills slot i = 32 b + r (NF4: slots
+  //    past 127 read zeros)
+  const int bq_row = (tid & 255) >> 3;
+  const int bq_byte = 16 * ((tid & 7) ^ ((bq_row >> 3) & 3));
+  const bool bq_on = nb / 2 + bq_byte < Nw / 2;
+  const int si = tid & 255;
+  const int s_row = si & 31, s_blk = si >> 5;
+  const bool s_on = (NF4 ? si < 128 : true) && (nb / KB + s_blk) < Nw / KB;
+  auto issue_w = [&](int kt, int st) {   // weights / scales of k-tile kt
+    uint8_t* base = stage(st);
+    const int kb = kt * kGK;
+    if (w < 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, MOE4_LDS(base + kGStageA + w * 1024), 16,
+          (bq_on && kb + bq_row < Kw) ? (kb + bq_row) * (Nw / 2) + nb / 2 + bq_byte : kOob, 0, 0,
+          0);
+    } else {
+      const int soff =
+          (s_on && kb + s_row < Kw) ? ((kb + s_row) * (Nw / KB) + nb / KB + s_blk) * sbytes : kOob;
+      if constexpr (NF4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, MOE4_LDS(base + kGStageA + kGStageB + (w - 4) * 256), 4, soff, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, MOE4_LDS(base + kGStageA + kGStageB + (w - 4) * 256), 1, soff, 0, 0, 0);
+    }
+  };
+  // batch kt: the A tile of k-tile kt (stage kt % 4) and the weights of
+  // k-tile kt + 1 (stage (kt + 1) % 4)
+  auto issue = [&](int kt) {
+    const int kb = kt * kGK;
+    const int aoff = kb + a_col < Kw ? a_off + 2 * kb : kOob;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int p = 0; p < 2; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, MOE4_LDS(stage(kt % kGStages) + p * 8192 + w * 1024), 16,
+          aoff == kOob ? kOob : aoff, p * 128 * Kw * 2, 0, 0);
+    issue_w(kt + 1, (kt + 1) % kGStages);
+  };
+  // dequantise the packed weights of stage st into Bt buffer bi: thread t
+  // takes weight rows 8 (t % 4) .. +7 (chunk t % 4 of a Bt column) and byte
+  // t / 4 (columns 2 (t / 4), +1). LDS reads go through vector types (the
+  // compiler then does not wait for the LDS-DMA loads in flight).
+  const int dq_c = tid & 3, dq_j = tid >> 2;
+  const int dq_chunk = dq_j >> 4, dq_in = dq_j & 15;
+  const int dq_blk = NF4 ? dq_j >> 5 : dq_j >> 4;
+  auto dequant_to_bt = [&](int st, int bi) {
+    const uint8_t* base = stage(st);
+    const uint8_t* qb = base + kGStageA;
+    const u32x4* sv = reinterpret_cast<const u32x4*>(base + kGStageA + kGStageB) + 8 * dq_blk + 2 * dq_c;
+    const u32x4 s0 = sv[0], s1 = sv[1];   // scale slots of rows 8 dq_c .. +7
+    float v0[8], v1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * dq_c + i;
+      // the 8 bytes holding byte dq_in of the row's chunk dq_chunk
+      const u32x2 pr = *reinterpret_cast<const u32x2*>(
+          qb + row * (kGN / 2) + 16 * (dq_chunk ^ ((row >> 3) & 3)) + 8 * (dq_in >> 3));
+      const uint32_t wd = (dq_in & 4) ? pr.y : pr.x;
+      const uint32_t byte = (wd >> (8 * (dq_in & 3))) & 255u;
+      const uint32_t sraw = i < 4 ? s0[i] : s1[i - 4];
+      if constexpr (NF4) {
+        const float sc = __uint_as_float(sraw);
+        const f32x2 lv = reinterpret_cast<const f32x2*>(lutf)[byte];
+        v0[i] = lv.x * sc;
+        v1[i] = lv.y * sc;
+      } else {
+        const float sc = __uint_as_float((sraw & 255u) << 23);
+        const uint32_t p =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(byte, sc, 0));
+        v0[i] = bf16lo(p);
+        v1[i] = bf16hi(p);
+      }
+    }
+    uint8_t* bb = bt + bi * kGBt;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float* v = q ? v1 : v0;
+      const u32x4 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+      *reinterpret_cast<u32x4*>(bb + (2 * dq_j + q) * kGBtPitch + 16 * dq_c) = pk;
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int z = 0; z < 16; ++z) acc[i][j][z] = 0.0f;
 
-  for (int kb = 0; kb < a.Kw; kb += kDK) {
-    // global -> registers
-    u32x4 areg[2];
+  const int nk = (Kw + kGK - 1) / kGK;
+  // prologue: weights of k-tile 0, batches 0 .. 2, then k-tile 0 into Bt 0
+  issue_w(0, 0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = tid + 256 * i, r = id >> 2, cidx = (id & 3) * 8;
-      areg[i] = (r < nrows) ? *reinterpret_cast<const u32x4*>(a.A + (int64_t)(row0 + r) * a.Kw +
-                                                              kb + cidx)
-                            : u32x4{0u, 0u, 0u, 0u};
-    }
-    uint32_t braw[2] = {0u, 0u};
-    float bsc[2] = {0.0f, 0.0f};
-    if (bcol_ok) {
+  for (int j = 0; j < kGStages - 1; ++j)
+    if (j < nk) issue(j);
+  if (nk >= 3) wait_vmcnt<3 * kGLoads>();
+  else if (nk == 2) wait_vmcnt<2 * kGLoads>();
+  else wait_vmcnt<kGLoads>();
+  lds_barrier();   // the weights of k-tile 0 come from every wave's loads
+  dequant_to_bt(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // batch kt landed (for this wave); then everyone's, and every wave's Bt
+    // writes of the previous step, behind the barrier
+    if (kt + 2 < nk) wait_vmcnt<2 * kGLoads>();
+    else if (kt + 1 < nk) wait_vmcnt<kGLoads>();
+    else wait_vmcnt<0>();
+    wait_lgkm0();
+    lds_barrier();
+    if (kt + kGStages - 1 < nk) issue(kt + kGStages - 1);
+    const uint8_t* As = stage(kt % kGStages);
+    const uint8_t* Bs = bt + (kt & 1) * kGBt;
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int64_t wr = wrow0 + kb + 2 * kp + rr;
-        braw[rr] = *reinterpret_cast<const uint32_t*>(a.wq + wr * bytes_per_row + ncol0 / 2);
-        bsc[rr] = F::scale(a.ws, wr, a.Nw, ncol0 / KB);
-      }
-    }
-    __syncthreads();   // previous iteration's LDS reads are done
+    for (int s = 0; s < kGK / 16; ++s) {
+      bf16x8 av[4], bv[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = tid + 256 * i, r = id >> 2, cidx = (id & 3) * 8;
-      *reinterpret_cast<u32x4*>(&As[r * kDL + cidx]) = areg[i];
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float2 v0 = lutf[(braw[0] >> (8 * (c >> 1))) & 255u];
-      const float2 v1 = lutf[(braw[1] >> (8 * (c >> 1))) & 255u];
-      const float w0 = ((c & 1) ? v0.y : v0.x) * bsc[0];
-      const float w1 = ((c & 1) ? v1.y : v1.x) * bsc[1];
-      *reinterpret_cast<uint32_t*>(&Bs[(8 * no + c) * kDL + 2 * kp]) = pack_bf16x2(w0, w1);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < kDK / 16; ++s) {
-      bf16x8 av[2], bv[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        av[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 32 + n32) * kDL + 16 * s + 8 * h]);
-        bv[i] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + i * 32 + n32) * kDL + 16 * s + 8 * h]);
+      for (int i = 0; i < 4; ++i) {
+        const int r = wr * 128 + i * 32 + n32;
+        av[i] = *reinterpret_cast<const bf16x8*>(As + r * 64 + 16 * ((2 * s + h) ^ ((r >> 2) & 3)));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const int c = wc * 64 + j * 32 + n32;
+        bv[j] = *reinterpret_cast<const bf16x8*>(Bs + c * kGBtPitch + 16 * (2 * s + h));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
+    // next k-tile's weights into the other Bt buffer (after the last k-tile
+    // the stage holds zeros or stale bytes: decoded and never read)
+    dequant_to_bt((kt + 1) % kGStages, (kt + 1) & 1);
   }
 
+  // LoRA delta of dx (gate_up dgrad) as extra reduction steps over the rank:
+  // A = bf16(t[row][q]), B = bf16(lora_scale * A_e[q][n])
+  if (MODE == DGRAD_GATEUP && a.r) {
+    for (int q0 = 0; q0 < a.r; q0 += 16) {
+      bf16x8 bl[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const int n = nb + wc * 64 + j * 32 + n32;
+        u32x4 pk;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = nb + wn * 64 + j * 32 + n32;
-      if (n >= a.Nw) continue;
+        for (int jj = 0; jj < 4; ++jj) {
+          const int q = q0 + 8 * h + 2 * jj;
+          const uint16_t* ar = a.loraA + ((int64_t)e * a.r) * Nw + n;
+          const float x0 = (n < Nw && q < a.r) ? a.lscale * bf16_to_f32(ar[(int64_t)q * Nw]) : 0.0f;
+          const float x1 = (n < Nw && q + 1 < a.r) ? a.lscale * bf16_to_f32(ar[(int64_t)(q + 1) * Nw]) : 0.0f;
+          pk[jj] = pack_bf16x2(x0, x1);
+        }
+        bl[j] = __builtin_bit_cast(bf16x8, pk);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = wr * 128 + i * 32 + n32;
+        const float* tr = a.t + (int64_t)(row0 + rr) * a.r;
+        u32x4 pk;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int q = q0 + 8 * h + 2 * jj;
+          const float x0 = (rr < nrows && q < a.r) ? tr[q] : 0.0f;
+          const float x1 = (rr < nrows && q + 1 < a.r) ? tr[q + 1] : 0.0f;
+          pk[jj] = pack_bf16x2(x0, x1);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
+                                                              bl[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: lane holds column n32 of each 32 x 32 tile, rows
+  // 8 (z / 4) + 4 h + z % 4
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = nb + wc * 64 + j * 32 + n32;
+    if (n >= Nw) continue;
+    int ng = 0, nu = 0;
+    if (MODE == DGRAD_DOWN) {
+      ng = gate_row(a.layout, a.I, n);
+      nu = up_row(a.layout, a.I, n);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int z = 0; z < 16; ++z) {
-        const int rr = wm * 64 + i * 32 + 8 * (z >> 2) + 4 * h + (z & 3);
+        const int rr = wr * 128 + i * 32 + 8 * (z >> 2) + 4 * h + (z & 3);
         if (rr >= nrows) continue;
         const int row = row0 + rr;
         const float v = acc[i][j][z];
         if (MODE == DGRAD_DOWN) {
           // n indexes the intermediate dimension: dH[row][n]
-          const int ng = gate_row(a.layout, a.I, n), nu = up_row(a.layout, a.I, n);
           const float* sg = a.save_gu + (int64_t)row * 2 * a.I;
           float dg, du;
           act_backward(a.act, sg[ng], sg[nu], v, a.alpha, a.limit, dg, du);
@@ -162,18 +328,11 @@ __global__ __launch_bounds__(256) void k_dgrad(const DgradArgs a) {
           d[ng] = f32_to_bf16(dg);
           d[nu] = f32_to_bf16(du);
         } else {
-          float x = v;
-          if (a.r) {
-            const float* tr = a.t + (int64_t)row * a.r;
-            const uint16_t* ar = a.loraA + (int64_t)e * a.r * a.Nw + n;
-            float s = 0.0f;
-            for (int qq = 0; qq < a.r; ++qq) s += round_bf16(tr[qq]) * bf16_to_f32(ar[(int64_t)qq * a.Nw]);
-            x += a.lscale * s;
-          }
-          a.dx[(int64_t)row * a.Nw + n] = x;
+          a.dx[(int64_t)row * Nw + n] = v;
         }
       }
     }
+  }
 }
 
 // t[row][q] = sum_n dGU[row][n] * B[e][n][q] (fp32); one wave per row.
@@ -248,6 +407,15 @@ hipError_t run_lora_reduce(const uint16_t* mat, int ncols, const float* vec, int
 }
 
 template <int FMT>
+hipError_t set_dgrad_lds() {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dgrad<FMT, DGRAD_DOWN>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dgrad<FMT, DGRAD_GATEUP>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
+}
+
+template <int FMT>
 hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int32_t* offsets,
                         int rows, const float* save_gu, const float* save_xa,
                         const uint16_t* dy_perm, float* dx_perm, float* dA, float* dB,
@@ -255,7 +423,9 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   const int E = ex.E, H = ex.H, I = ex.I;
   const bool lora = ex.lora_A != nullptr;
   const int touched = min(E, rows);
-  const int ntiles = rows / kDM + touched;
+  const int ntiles = rows / kGM + touched;
+  static const hipError_t attr = set_dgrad_lds<FMT>();
+  if (attr != hipSuccess) return attr;
   DgradArgs d{};
   d.offsets = offsets;
   d.E = E;
@@ -273,11 +443,13 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   d.A = dy_perm;
   d.save_gu = save_gu;
   d.dgu = dgu;
-  d.ncg = (I + kDN - 1) / kDN;
+  d.ncg = (I + kGN - 1) / kGN;
   le.before(0, s);
   if (ntiles * d.ncg > 0)
-    // 16 spare ids keep every XCD's share of the items within the ids it is dealt
-    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_DOWN>), dim3(ntiles * d.ncg + 16), dim3(256), 0, s, d);
+    // ntiles bounds the row tiles; 8 spare ids keep every XCD's share of the
+    // items within the ids it is dealt
+    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_DOWN>), dim3(ntiles * d.ncg + 8), dim3(512), kGLds, s,
+                       d);
   le.after(0, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -299,11 +471,11 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   g.r = lora ? ex.lora_r : 0;
   g.lscale = ex.lora_scale;
   g.dx = dx_perm;
-  g.ncg = (H + kDN - 1) / kDN;
+  g.ncg = (H + kGN - 1) / kGN;
   le.before(1, s);
   if (ntiles * g.ncg > 0)
-    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_GATEUP>), dim3(ntiles * g.ncg + 16), dim3(256), 0, s,
-                       g);
+    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_GATEUP>), dim3(ntiles * g.ncg + 8), dim3(512), kGLds,
+                       s, g);
   le.after(1, s);
   err = hipGetLastError();
   if (err != hipSuccess || !lora) return err;

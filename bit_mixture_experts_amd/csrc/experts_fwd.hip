@@ -343,65 +343,6 @@ constexpr int kStageBytes = kStageA + kStageB + kStageS;
 constexpr int kTiledLds = kStages * kStageBytes;
 static_assert(kTiledLds + 256 * 8 <= 160 * 1024, "tiled kernel LDS");
 
-#define MOE4_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-// wait until at most N vector-memory loads of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-// workgroup barrier without the memory fence of __syncthreads (which would
-// wait for every outstanding LDS-DMA load); compiler-level ordering only
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Row tiles of an expert with n rows: ceil(n / kBM) tiles of R rows each
-// (R a multiple of 32), the last one shorter.
-__device__ __forceinline__ int tiles_of(int n) { return (n + kBM - 1) / kBM; }
-__device__ __forceinline__ int tile_rows(int n) {
-  const int nt = tiles_of(n);
-  return nt ? ((n + nt - 1) / nt + 31) / 32 * 32 : 0;
-}
-
-// Work item of workgroup b: (expert e, row tile u, column group cg). Items are
-// (tile, column group) pairs, column group fastest, experts in order. The
-// dispatcher deals workgroup ids round-robin over the 8 XCDs (each with its
-// own L2); XCD x gets a contiguous 1/8 of the items, so the column groups of
-// one tile (which share its activation rows) and the tiles of one expert
-// (which share its weights) stay on one XCD. The grid needs at least
-// items + 8 workgroups; the rest get e = -1.
-__device__ __forceinline__ void locate_tile(const int32_t* __restrict__ offsets, int E, int ncg,
-                                            int b, int& e_out, int& u_out, int& cg_out) {
-  constexpr int kXcd = 8;
-  const int l = lane_id();
-  const int per = (E + kWave - 1) / kWave;
-  const int e0 = l * per;
-  int nt = 0;
-  if (e0 < E) {
-    int prev = offsets[e0];
-    for (int i = 0; i < per && e0 + i < E; ++i) {
-      const int nx = offsets[e0 + i + 1];
-      nt += tiles_of(nx - prev);
-      prev = nx;
-    }
-  }
-  const int N = __shfl(wave_inclusive_scan(nt), kWave - 1, kWave) * ncg;
-  const int x = b % kXcd, i = b / kXcd;
-  const int f0 = (int)((int64_t)N * x / kXcd), f1 = (int)((int64_t)N * (x + 1) / kXcd);
-  int e = -1, u = 0, item = 0;
-  if (i < f1 - f0) {
-    item = f0 + i;
-    locate_item(offsets, E, item / ncg, [](int n) { return tiles_of(n); }, e, u);
-  }
-  e_out = e;
-  u_out = u;
-  cg_out = item % ncg;
-}
-
 template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   using F = Format<FMT>;
@@ -413,7 +354,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   if (NF4 && tid < 256) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
   int e, ut, cg;
-  locate_tile(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
+  locate_tile_eq<kBM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
   // wave-uniform by construction; make it visible to the compiler so that the
   // buffer resources below live in scalar registers
   e = __builtin_amdgcn_readfirstlane(e);
@@ -424,7 +365,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   const int K = a.K;
   const int ebeg = min(a.offsets[e], a.rows);
   const int n_e = min(a.offsets[e + 1], a.rows) - ebeg;
-  const int R = tile_rows(n_e);
+  const int R = eq_tile_rows<kBM>(n_e);
   const int row0 = ebeg + ut * R;
   const int nrows = min(R, ebeg + n_e - row0);
   const int nrt = (nrows + 31) >> 5;
