@@ -335,77 +335,6 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
   }
 }
 
-// t[row][q] = sum_n dGU[row][n] * B[e][n][q] (fp32); one wave per row.
-__global__ __launch_bounds__(256) void k_lora_t(const uint16_t* __restrict__ dgu,
-                                                const int32_t* __restrict__ offsets, int E,
-                                                int rows, int N2, const uint16_t* __restrict__ B,
-                                                int r, float* __restrict__ t) {
-  const int row = (int)((blockIdx.x * (unsigned)blockDim.x + threadIdx.x) >> 6);
-  if (row >= rows) return;
-  const int e = expert_of_row(offsets, E, row);
-  const int l = lane_id();
-  const uint16_t* dr = dgu + (int64_t)row * N2;
-  const uint16_t* be = B + (int64_t)e * N2 * r;
-  for (int qq = 0; qq < r; ++qq) {
-    float p = 0.0f;
-    for (int n = l; n < N2; n += kWave) p += bf16_to_f32(dr[n]) * bf16_to_f32(be[(int64_t)n * r + qq]);
-    p = wave_sum(p);
-    if (l == 0) t[(int64_t)row * r + qq] = p;
-  }
-}
-
-// out[e][col][q] (TRANSPOSED=false) or out[e][q][col] (true) =
-//   lscale * sum_{rows of e} bf16(vec[row][q]) * mat[row][col]
-// Thread per column; vec fp32 [rows, r] (rounded to bf16), mat bf16 [rows, ncols].
-template <int RMAX, bool TRANSPOSED>
-__global__ __launch_bounds__(256) void k_lora_reduce(const uint16_t* __restrict__ mat, int ncols,
-                                                     const float* __restrict__ vec, int r,
-                                                     const int32_t* __restrict__ offsets,
-                                                     int rows, float lscale,
-                                                     float* __restrict__ out) {
-  const int e = blockIdx.y;
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= ncols) return;
-  const int r0 = min(offsets[e], rows), r1 = min(offsets[e + 1], rows);
-  float acc[RMAX];
-#pragma unroll
-  for (int qq = 0; qq < RMAX; ++qq) acc[qq] = 0.0f;
-  for (int row = r0; row < r1; ++row) {
-    const float m = bf16_to_f32(mat[(int64_t)row * ncols + col]);
-    const float* vr = vec + (int64_t)row * r;
-#pragma unroll
-    for (int qq = 0; qq < RMAX; ++qq)
-      if (qq < r) acc[qq] += round_bf16(vr[qq]) * m;
-  }
-#pragma unroll
-  for (int qq = 0; qq < RMAX; ++qq)
-    if (qq < r) {
-      const int64_t o = TRANSPOSED ? ((int64_t)e * r + qq) * ncols + col
-                                   : ((int64_t)e * ncols + col) * r + qq;
-      out[o] = lscale * acc[qq];
-    }
-}
-
-template <bool TRANSPOSED>
-hipError_t run_lora_reduce(const uint16_t* mat, int ncols, const float* vec, int r,
-                           const int32_t* offsets, int rows, int E, float lscale, float* out,
-                           hipStream_t s) {
-  const dim3 grid((unsigned)((ncols + 255) / 256), (unsigned)E);
-  if (r <= 8)
-    hipLaunchKernelGGL((k_lora_reduce<8, TRANSPOSED>), grid, dim3(256), 0, s, mat, ncols, vec, r,
-                       offsets, rows, lscale, out);
-  else if (r <= 16)
-    hipLaunchKernelGGL((k_lora_reduce<16, TRANSPOSED>), grid, dim3(256), 0, s, mat, ncols, vec, r,
-                       offsets, rows, lscale, out);
-  else if (r <= 32)
-    hipLaunchKernelGGL((k_lora_reduce<32, TRANSPOSED>), grid, dim3(256), 0, s, mat, ncols, vec, r,
-                       offsets, rows, lscale, out);
-  else
-    hipLaunchKernelGGL((k_lora_reduce<64, TRANSPOSED>), grid, dim3(256), 0, s, mat, ncols, vec, r,
-                       offsets, rows, lscale, out);
-  return hipGetLastError();
-}
-
 template <int FMT>
 hipError_t set_dgrad_lds() {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dgrad<FMT, DGRAD_DOWN>),
@@ -419,7 +348,8 @@ template <int FMT>
 hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int32_t* offsets,
                         int rows, const float* save_gu, const float* save_xa,
                         const uint16_t* dy_perm, float* dx_perm, float* dA, float* dB,
-                        uint16_t* dgu, float* tbuf, const LaunchEvents& le, hipStream_t s) {
+                        uint16_t* dgu, float* tbuf, uint16_t* bt_ws, const LaunchEvents& le,
+                        hipStream_t s) {
   const int E = ex.E, H = ex.H, I = ex.I;
   const bool lora = ex.lora_A != nullptr;
   const int touched = min(E, rows);
@@ -454,9 +384,10 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (lora && rows > 0) {
-    hipLaunchKernelGGL(k_lora_t, dim3((rows + 3) / 4), dim3(256), 0, s, dgu, offsets, E, rows,
-                       2 * I, ex.lora_B, ex.lora_r, tbuf);
-    err = hipGetLastError();
+    // t = dGU B_e as a projection onto the rank against B_e^T
+    err = launch_transpose_rank(ex.lora_B, E, 2 * I, ex.lora_r, bt_ws, s);
+    if (err != hipSuccess) return err;
+    err = launch_rank_proj(dgu, offsets, E, rows, 2 * I, bt_ws, ex.lora_r, tbuf, s);
     if (err != hipSuccess) return err;
   }
   // dx = dGU W_gu[e] (+ LoRA): W_gu is [2I (reduction), H]
@@ -480,18 +411,21 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   err = hipGetLastError();
   if (err != hipSuccess || !lora) return err;
   // dB[e] = s * dGU^T bf16(xa)  -> [E, 2I, r];  dA[e] = s * bf16(t)^T x -> [E, r, H]
-  err = run_lora_reduce<false>(dgu, 2 * I, save_xa, ex.lora_r, offsets, rows, E, ex.lora_scale,
-                               dB, s);
+  err = launch_rank_reduce(dgu, 2 * I, save_xa, ex.lora_r, offsets, rows, E, ex.lora_scale, dB,
+                           false, s);
   if (err != hipSuccess) return err;
-  return run_lora_reduce<true>(x_perm, H, tbuf, ex.lora_r, offsets, rows, E, ex.lora_scale, dA,
-                               s);
+  return launch_rank_reduce(x_perm, H, tbuf, ex.lora_r, offsets, rows, E, ex.lora_scale, dA, true,
+                            s);
 }
 
 }  // namespace
 
 size_t backward_ws_bytes(const moe4_experts& ex, int rows) {
   size_t b = align_up((size_t)rows * 2 * ex.I * sizeof(uint16_t), 256);
-  if (ex.lora_A) b += align_up((size_t)rows * ex.lora_r * sizeof(float), 256);
+  if (ex.lora_A) {
+    b += align_up((size_t)rows * ex.lora_r * sizeof(float), 256);
+    b += align_up((size_t)ex.E * ex.lora_r * 2 * ex.I * sizeof(uint16_t), 256);   // B^T
+  }
   return b + dq_expand_bytes(ex);
 }
 
@@ -506,6 +440,8 @@ hipError_t launch_expert_backward(const moe4_experts& ex, const uint16_t* x_perm
   p += align_up((size_t)rows * 2 * ex.I * sizeof(uint16_t), 256);
   float* tbuf = ex.lora_A ? reinterpret_cast<float*>(p) : nullptr;
   if (ex.lora_A) p += align_up((size_t)rows * ex.lora_r * sizeof(float), 256);
+  uint16_t* bt_ws = ex.lora_A ? reinterpret_cast<uint16_t*>(p) : nullptr;
+  if (ex.lora_A) p += align_up((size_t)ex.E * ex.lora_r * 2 * ex.I * sizeof(uint16_t), 256);
   if (rows == 0 && !ex.lora_A) return hipSuccess;
   if (ex.format == MOE4_FMT_NF4_DQ) {
     // expand the double-quantised absmax, then the plain NF4 dgrad
@@ -513,13 +449,13 @@ hipError_t launch_expert_backward(const moe4_experts& ex, const uint16_t* x_perm
     hipError_t err = dq_expand_experts(ex, p, &plain, s);
     if (err != hipSuccess) return err;
     return backward_fmt<MOE4_FMT_NF4>(plain, x_perm, offsets, rows, save_gu, save_xa, dy_perm,
-                                      dx_perm, dA, dB, dgu, tbuf, le, s);
+                                      dx_perm, dA, dB, dgu, tbuf, bt_ws, le, s);
   }
   if (ex.format == MOE4_FMT_NF4)
     return backward_fmt<MOE4_FMT_NF4>(ex, x_perm, offsets, rows, save_gu, save_xa, dy_perm,
-                                      dx_perm, dA, dB, dgu, tbuf, le, s);
+                                      dx_perm, dA, dB, dgu, tbuf, bt_ws, le, s);
   return backward_fmt<MOE4_FMT_MXFP4>(ex, x_perm, offsets, rows, save_gu, save_xa, dy_perm,
-                                      dx_perm, dA, dB, dgu, tbuf, le, s);
+                                      dx_perm, dA, dB, dgu, tbuf, bt_ws, le, s);
 }
 
 }  // namespace moe4

@@ -664,31 +664,6 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   }
 }
 
-// -------------------------------------------------------------- LoRA x A^T
-
-// xa[row][q] = sum_h x_perm[row][h] * A[e(row)][q][h], fp32; one wave per row.
-__global__ __launch_bounds__(256) void k_lora_xa(const uint16_t* __restrict__ x,
-                                                 const int32_t* __restrict__ offsets, int E,
-                                                 int rows, int H, const uint16_t* __restrict__ A,
-                                                 int r, float* __restrict__ xa) {
-  const int row = (int)((blockIdx.x * (unsigned)blockDim.x + threadIdx.x) >> 6);
-  if (row >= rows) return;
-  const int e = expert_of_row(offsets, E, row);
-  const int l = lane_id();
-  const u32x4* xr = reinterpret_cast<const u32x4*>(x + (int64_t)row * H);
-  for (int qq = 0; qq < r; ++qq) {
-    const u32x4* ar = reinterpret_cast<const u32x4*>(A + ((int64_t)e * r + qq) * H);
-    float p = 0.0f;
-    for (int c = l; c < H / 8; c += kWave) {
-      const u32x4 xv = xr[c], av = ar[c];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p += bf16lo(xv[i]) * bf16lo(av[i]) + bf16hi(xv[i]) * bf16hi(av[i]);
-    }
-    p = wave_sum(p);
-    if (l == 0) xa[(int64_t)row * r + qq] = p;
-  }
-}
-
 template <int FMT, bool GATEUP>
 hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
   const int nwg = nitems * a.ncg;
@@ -832,9 +807,8 @@ hipError_t launch_expert_forward(const moe4_experts& ex, const uint16_t* x_perm,
   char* abs_ws = p + (ex.lora_A ? align_up((size_t)rows * ex.lora_r * sizeof(float), 256) : 0);
   if (ex.lora_A) {
     xa = save_xa ? save_xa : reinterpret_cast<float*>(p);
-    hipLaunchKernelGGL(k_lora_xa, dim3((rows + 3) / 4), dim3(256), 0, s, x_perm, offsets, ex.E,
-                       rows, ex.H, ex.lora_A, ex.lora_r, xa);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_rank_proj(x_perm, offsets, ex.E, rows, ex.H, ex.lora_A, ex.lora_r,
+                                      xa, s);
     if (err != hipSuccess) return err;
   }
   if (ex.format == MOE4_FMT_NF4_DQ) {

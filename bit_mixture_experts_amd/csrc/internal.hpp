@@ -32,6 +32,19 @@ size_t dq_expand_bytes(const moe4_experts& ex);
 hipError_t dq_expand_experts(const moe4_experts& ex, void* abs_ws, moe4_experts* out,
                              hipStream_t s);
 
+// ---- LoRA rank pieces
+// out[row][q] = sum_k M[row][k] P[e(row)][q][k] (fp32), M bf16 [rows, K], P bf16 [E, r, K]
+hipError_t launch_rank_proj(const uint16_t* M, const int32_t* offsets, int E, int rows, int K,
+                            const uint16_t* P, int r, float* out, hipStream_t s);
+// BT[e][q][n] = B[e][n][q]
+hipError_t launch_transpose_rank(const uint16_t* B, int E, int N, int r, uint16_t* BT,
+                                 hipStream_t s);
+// out[e][col][q] (or [e][q][col] when transposed) =
+//   lscale * sum over e's rows of bf16(vec[row][q]) * mat[row][col]
+hipError_t launch_rank_reduce(const uint16_t* mat, int ncols, const float* vec, int r,
+                              const int32_t* offsets, int rows, int E, float lscale, float* out,
+                              bool transposed, hipStream_t s);
+
 // ---- router step
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
                                 int H, int E, float* logits, hipStream_t s);
