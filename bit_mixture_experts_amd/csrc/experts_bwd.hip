@@ -9,6 +9,8 @@
 // the forward: each k-tile of packed weights (rows along the reduction) is
 // dequantised by the whole workgroup into LDS, transposed so that each MFMA
 // lane reads 8 consecutive reduction values with one 128-bit LDS load.
+#include <type_traits>
+
 #include "common.hpp"
 #include "formats.hpp"
 #include "gemm_common.hpp"
@@ -59,8 +61,9 @@ __device__ __forceinline__ void act_backward(int act, float g, float u, float dh
 // ahead of its activation tile; while the MFMAs of k-tile kt run, every thread
 // dequantises its share of k-tile kt + 1 (8 weight rows x 2 columns) into a
 // transposed bf16 buffer Bt [kGN columns][kGK], which the next k-tile's MFMAs
-// read as their B operand. Wave w computes rows 128 (w / 4) .. +127 and
-// columns 64 (w % 4) .. +63 of the tile (4 x 2 MFMA tiles of 32 x 32).
+// read as their B operand. Wave w computes columns 32 w .. +31 of the tile
+// against every 32-row tile (the loop is instantiated per count of row tiles,
+// so that short expert tiles keep all eight waves busy).
 constexpr int kGM = 256, kGN = 256, kGK = 32, kGStages = 4;
 // Stage: A [kGM rows][kGK] bf16 (four 16-byte chunks a row, chunk c of row r
 // stored at c ^ ((r >> 2) & 3): 16 consecutive rows of one chunk column fall
@@ -104,7 +107,6 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
   const int row0 = ebeg + ut * R;
   const int nrows = min(R, ebeg + n_e - row0);
   const int n32 = l & 31, h = l >> 5;
-  const int wr = w >> 2, wc = w & 3;
   const int nb = cg * kGN;
 
   const rsrc_t ra = make_rsrc(a.A + (int64_t)row0 * Kw, (uint32_t)nrows * Kw * 2);
@@ -207,118 +209,106 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
     }
   };
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int z = 0; z < 16; ++z) acc[i][j][z] = 0.0f;
-
   const int nk = (Kw + kGK - 1) / kGK;
-  // prologue: weights of k-tile 0, batches 0 .. 2, then k-tile 0 into Bt 0
-  issue_w(0, 0);
+  const int nrt = (nrows + 31) >> 5;
+  // column of this wave's MFMA B operand and output (wave w: columns
+  // nb + 32 w .. +31 against every row tile)
+  const int col = 32 * w + n32;
+  const int n = nb + col;
+  auto kloop = [&](auto nrt_c) {
+    constexpr int NRT = decltype(nrt_c)::value;
+    f32x16 acc[NRT];
 #pragma unroll
-  for (int j = 0; j < kGStages - 1; ++j)
-    if (j < nk) issue(j);
-  if (nk >= 3) wait_vmcnt<3 * kGLoads>();
-  else if (nk == 2) wait_vmcnt<2 * kGLoads>();
-  else wait_vmcnt<kGLoads>();
-  lds_barrier();   // the weights of k-tile 0 come from every wave's loads
-  dequant_to_bt(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // batch kt landed (for this wave); then everyone's, and every wave's Bt
-    // writes of the previous step, behind the barrier
-    if (kt + 2 < nk) wait_vmcnt<2 * kGLoads>();
-    else if (kt + 1 < nk) wait_vmcnt<kGLoads>();
-    else wait_vmcnt<0>();
-    wait_lgkm0();
-    lds_barrier();
-    if (kt + kGStages - 1 < nk) issue(kt + kGStages - 1);
-    const uint8_t* As = stage(kt % kGStages);
-    const uint8_t* Bs = bt + (kt & 1) * kGBt;
+    for (int i = 0; i < NRT; ++i)
 #pragma unroll
-    for (int s = 0; s < kGK / 16; ++s) {
-      bf16x8 av[4], bv[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wr * 128 + i * 32 + n32;
-        av[i] = *reinterpret_cast<const bf16x8*>(As + r * 64 + 16 * ((2 * s + h) ^ ((r >> 2) & 3)));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = wc * 64 + j * 32 + n32;
-        bv[j] = *reinterpret_cast<const bf16x8*>(Bs + c * kGBtPitch + 16 * (2 * s + h));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
-    // next k-tile's weights into the other Bt buffer (after the last k-tile
-    // the stage holds zeros or stale bytes: decoded and never read)
-    dequant_to_bt((kt + 1) % kGStages, (kt + 1) & 1);
-  }
+      for (int z = 0; z < 16; ++z) acc[i][z] = 0.0f;
 
-  // LoRA delta of dx (gate_up dgrad) as extra reduction steps over the rank:
-  // A = bf16(t[row][q]), B = bf16(lora_scale * A_e[q][n])
-  if (MODE == DGRAD_GATEUP && a.r) {
-    for (int q0 = 0; q0 < a.r; q0 += 16) {
-      bf16x8 bl[2];
+    // prologue: weights of k-tile 0, batches 0 .. 2, then k-tile 0 into Bt 0
+    issue_w(0, 0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = nb + wc * 64 + j * 32 + n32;
-        u32x4 pk;
+    for (int j = 0; j < kGStages - 1; ++j)
+      if (j < nk) issue(j);
+    if (nk >= 3) wait_vmcnt<3 * kGLoads>();
+    else if (nk == 2) wait_vmcnt<2 * kGLoads>();
+    else wait_vmcnt<kGLoads>();
+    lds_barrier();   // the weights of k-tile 0 come from every wave's loads
+    dequant_to_bt(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      // batch kt landed (for this wave); then everyone's, and every wave's Bt
+      // writes of the previous step, behind the barrier
+      if (kt + 2 < nk) wait_vmcnt<2 * kGLoads>();
+      else if (kt + 1 < nk) wait_vmcnt<kGLoads>();
+      else wait_vmcnt<0>();
+      wait_lgkm0();
+      lds_barrier();
+      if (kt + kGStages - 1 < nk) issue(kt + kGStages - 1);
+      const uint8_t* As = stage(kt % kGStages);
+      const uint8_t* Bs = bt + (kt & 1) * kGBt;
+#pragma unroll
+      for (int s = 0; s < kGK / 16; ++s) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Bs + col * kGBtPitch + 16 * (2 * s + h));
+#pragma unroll
+        for (int i = 0; i < NRT; ++i) {
+          const int r = i * 32 + n32;
+          const bf16x8 av =
+              *reinterpret_cast<const bf16x8*>(As + r * 64 + 16 * ((2 * s + h) ^ ((r >> 2) & 3)));
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
+        }
+      }
+      // next k-tile's weights into the other Bt buffer (after the last k-tile
+      // the stage holds zeros or stale bytes: decoded and never read)
+      dequant_to_bt((kt + 1) % kGStages, (kt + 1) & 1);
+    }
+
+    // LoRA delta of dx (gate_up dgrad) as extra reduction steps over the rank:
+    // A = bf16(t[row][q]), B = bf16(lora_scale * A_e[q][n])
+    if (MODE == DGRAD_GATEUP && a.r) {
+      for (int q0 = 0; q0 < a.r; q0 += 16) {
+        u32x4 pb;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int q = q0 + 8 * h + 2 * jj;
           const uint16_t* ar = a.loraA + ((int64_t)e * a.r) * Nw + n;
           const float x0 = (n < Nw && q < a.r) ? a.lscale * bf16_to_f32(ar[(int64_t)q * Nw]) : 0.0f;
-          const float x1 = (n < Nw && q + 1 < a.r) ? a.lscale * bf16_to_f32(ar[(int64_t)(q + 1) * Nw]) : 0.0f;
-          pk[jj] = pack_bf16x2(x0, x1);
-        }
-        bl[j] = __builtin_bit_cast(bf16x8, pk);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = wr * 128 + i * 32 + n32;
-        const float* tr = a.t + (int64_t)(row0 + rr) * a.r;
-        u32x4 pk;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int q = q0 + 8 * h + 2 * jj;
-          const float x0 = (rr < nrows && q < a.r) ? tr[q] : 0.0f;
-          const float x1 = (rr < nrows && q + 1 < a.r) ? tr[q + 1] : 0.0f;
-          pk[jj] = pack_bf16x2(x0, x1);
+          const float x1 =
+              (n < Nw && q + 1 < a.r) ? a.lscale * bf16_to_f32(ar[(int64_t)(q + 1) * Nw]) : 0.0f;
+          pb[jj] = pack_bf16x2(x0, x1);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
-                                                              bl[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < NRT; ++i) {
+          const int rr = i * 32 + n32;
+          const float* tr = a.t + (int64_t)(row0 + rr) * a.r;
+          u32x4 pk;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int q = q0 + 8 * h + 2 * jj;
+            const float x0 = (rr < nrows && q < a.r) ? tr[q] : 0.0f;
+            const float x1 = (rr < nrows && q + 1 < a.r) ? tr[q + 1] : 0.0f;
+            pk[jj] = pack_bf16x2(x0, x1);
+          }
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
+                                                           __builtin_bit_cast(bf16x8, pb), acc[i],
+                                                           0, 0, 0);
+        }
       }
     }
-  }
 
-  // ---- epilogue: lane holds column n32 of each 32 x 32 tile, rows
-  // 8 (z / 4) + 4 h + z % 4
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = nb + wc * 64 + j * 32 + n32;
-    if (n >= Nw) continue;
+    // ---- epilogue: lane holds column n of each 32 x 32 row tile, rows
+    // 8 (z / 4) + 4 h + z % 4
+    if (n >= Nw) return;
     int ng = 0, nu = 0;
     if (MODE == DGRAD_DOWN) {
       ng = gate_row(a.layout, a.I, n);
       nu = up_row(a.layout, a.I, n);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NRT; ++i) {
 #pragma unroll
       for (int z = 0; z < 16; ++z) {
-        const int rr = wr * 128 + i * 32 + 8 * (z >> 2) + 4 * h + (z & 3);
+        const int rr = i * 32 + 8 * (z >> 2) + 4 * h + (z & 3);
         if (rr >= nrows) continue;
         const int row = row0 + rr;
-        const float v = acc[i][j][z];
+        const float v = acc[i][z];
         if (MODE == DGRAD_DOWN) {
           // n indexes the intermediate dimension: dH[row][n]
           const float* sg = a.save_gu + (int64_t)row * 2 * a.I;
@@ -332,6 +322,16 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
         }
       }
     }
+  };
+  switch (nrt) {
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 5: kloop(std::integral_constant<int, 5>{}); break;
+    case 6: kloop(std::integral_constant<int, 6>{}); break;
+    case 7: kloop(std::integral_constant<int, 7>{}); break;
+    default: kloop(std::integral_constant<int, kGM / 32>{}); break;
   }
 }
 
