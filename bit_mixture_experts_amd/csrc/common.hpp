@@ -263,4 +263,72 @@ __device__ __forceinline__ void locate_tile_eq(const int32_t* __restrict__ offse
   cg_out = item % ncg;
 }
 
+// Row-tile count (32-row MFMA tiles) of tile u of an expert with n rows.
+template <int BM>
+__device__ __forceinline__ int eq_tile_nrt(int n, int u) {
+  const int nt = eq_tiles<BM>(n), R = eq_tile_rows<BM>(n);
+  const int rows = u < nt - 1 ? R : n - (nt - 1) * R;
+  return (rows + 31) >> 5;
+}
+
+// As locate_tile_eq, with the tiles dealt largest first: tiles are ordered by
+// their count of 32-row MFMA tiles (descending; experts in order within a
+// count), tile j of that order goes to XCD j % 8, and each XCD takes its tiles
+// in order, column group fastest. The dispatcher starts workgroups in id order,
+// so every XCD starts its largest tiles first and fills in with the small ones
+// (longest-first list scheduling). The grid needs (tiles + 7) * ncg
+// workgroups; the rest get e = -1.
+template <int BM>
+__device__ __forceinline__ void locate_tile_sorted(const int32_t* __restrict__ offsets, int E,
+                                                   int ncg, int b, int& e_out, int& u_out,
+                                                   int& cg_out) {
+  constexpr int kXcd = 8, kC = BM / 32;
+  const int l = lane_id();
+  const int per = (E + kWave - 1) / kWave;
+  const int e0 = l * per;
+  int cnt[kC];
+#pragma unroll
+  for (int c = 0; c < kC; ++c) cnt[c] = 0;
+  if (e0 < E) {
+    int prev = offsets[e0];
+    for (int i = 0; i < per && e0 + i < E; ++i) {
+      const int nx = offsets[e0 + i + 1], n = nx - prev;
+      prev = nx;
+      const int nt = eq_tiles<BM>(n);
+      if (nt == 0) continue;
+      const int cf = eq_tile_nrt<BM>(n, 0), cl = eq_tile_nrt<BM>(n, nt - 1);
+#pragma unroll
+      for (int c = 0; c < kC; ++c) cnt[c] += (cf == c + 1 ? nt - 1 : 0) + (cl == c + 1 ? 1 : 0);
+    }
+  }
+  const int x = b % kXcd, i = b / kXcd;
+  const int j = (i / ncg) * kXcd + x;   // position in the largest-first order
+  cg_out = i % ncg;
+  e_out = -1;
+  u_out = 0;
+  int before = 0;
+#pragma unroll
+  for (int c = kC - 1; c >= 0; --c) {
+    const int tot = __shfl(wave_inclusive_scan(cnt[c]), kWave - 1, kWave);
+    if (j >= before && j < before + tot) {
+      const int k = j - before;   // k-th tile of count c + 1, experts in order
+      const int C = c + 1;
+      int e, idx;
+      locate_item(offsets, E, k, [&](int n) {
+        const int nt = eq_tiles<BM>(n);
+        if (nt == 0) return 0;
+        return (eq_tile_nrt<BM>(n, 0) == C ? nt - 1 : 0) + (eq_tile_nrt<BM>(n, nt - 1) == C ? 1 : 0);
+      }, e, idx);
+      if (e >= 0) {
+        const int n = offsets[e + 1] - offsets[e], nt = eq_tiles<BM>(n);
+        const int nfull = eq_tile_nrt<BM>(n, 0) == C ? nt - 1 : 0;
+        e_out = e;
+        u_out = idx < nfull ? idx : nt - 1;
+      }
+      return;
+    }
+    before += tot;
+  }
+}
+
 }  // namespace moe4

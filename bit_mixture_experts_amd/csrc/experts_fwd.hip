@@ -354,7 +354,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   if (NF4 && tid < 256) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
   int e, ut, cg;
-  locate_tile_eq<kBM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
+  locate_tile_sorted<kBM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
   // wave-uniform by construction; make it visible to the compiler so that the
   // buffer resources below live in scalar registers
   e = __builtin_amdgcn_readfirstlane(e);
@@ -686,9 +686,9 @@ hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
 template <int FMT, bool GATEUP>
 hipError_t run_tiled(const GemmArgs& a, int ntiles, hipStream_t s) {
   if (ntiles == 0) return hipSuccess;
-  // ntiles bounds the row tiles; 8 spare ids keep every XCD's share of the
-  // items within the ids it is dealt
-  const int nwg = ntiles * a.ncg + 8;
+  // ntiles bounds the row tiles; tile j of the largest-first order runs on
+  // XCD j % 8, so every XCD needs ceil(tiles / 8) * ncg ids
+  const int nwg = (ntiles + 7) * a.ncg;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tiled<FMT, GATEUP>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kTiledLds);
