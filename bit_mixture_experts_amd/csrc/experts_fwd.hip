@@ -601,19 +601,18 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
         // entry i' < 8 of a gate lane and entry i' + 8 of an up lane are
-        // finished by that lane; each sends the partner the other half
-        typedef float f32x8 __attribute__((ext_vector_type(8)));
-        const f32x8 lo = __builtin_shufflevector(acc[rt], acc[rt], 0, 1, 2, 3, 4, 5, 6, 7);
-        const f32x8 hi = __builtin_shufflevector(acc[rt], acc[rt], 8, 9, 10, 11, 12, 13, 14, 15);
-        const f32x8 send = gate_lane ? hi : lo, keep = gate_lane ? lo : hi;
-        float recv[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) recv[q] = __shfl_xor(send[q], 16, kWave);
+        // finished by that lane; the partner lane (16 apart) holds the other
+        // half of the pair
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const float mine = keep[q];
-          float g = (gate_lane ? mine : recv[q]) + bg;
-          float u = (gate_lane ? recv[q] : mine) + bu;
+          // v_permlane16_swap(lo, hi) swaps rows 1 and 3 of lo with rows 0
+          // and 2 of hi (16-lane rows): every lane then holds the gate value
+          // of its entry in the first result and the up value in the second
+          // (a gate lane keeps its own entries i < 8, an up lane its i >= 8)
+          const auto gu = __builtin_amdgcn_permlane16_swap(
+              __float_as_uint(acc[rt][q]), __float_as_uint(acc[rt][q + 8]), false, false);
+          float g = __uint_as_float(gu[0]) + bg;
+          float u = __uint_as_float(gu[1]) + bu;
           const int rt_row = rt * 32 + 8 * (q >> 2) + (gate_lane ? 0 : 16) + 4 * h + (q & 3);
           if (rt_row < nrows && jon) {
             if (extra) {
