@@ -495,12 +495,14 @@ def test_auto_variant_choice():
         assert res["variant"] == want
 
 
-def test_forward_single_expert_overflow_rows():
-    """All tokens on one expert: the skinny kernel loops over row chunks and the
-    tiled kernel over several 128-row tiles."""
+@pytest.mark.parametrize("T", [300, 700])
+def test_forward_single_expert_overflow_rows(T):
+    """All tokens on two experts: the skinny kernel loops over row chunks; at
+    T=700 the tiled kernel cuts each expert into three equal tiles (of up to
+    320 rows), which the largest-first order deals with the other experts'
+    empty ones."""
     spec = inp.TINY_NF4
     L = layer_of(spec)
-    T = 300
     x, _ = inp.host_tokens(spec, T)
     lg = np.full((T, spec.E), -5.0, np.float32)
     lg[:, 3] = 5.0
@@ -508,9 +510,9 @@ def test_forward_single_expert_overflow_rows():
     ri, rw = oracle.route(lg, spec.k)
     ref = oracle.layer_forward(x, ri, rw, L.W)
     for variant in (moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED):
-        say(f"forward skewed variant={variant}")
+        say(f"forward skewed T={T} variant={variant}")
         res = run_layer(L.device(variant), to_dev(x), to_dev(lg), spec.k)
-        assert_close(res["out32"].cpu().numpy(), ref["out"], f"out skewed v{variant}")
+        assert_close(res["out32"].cpu().numpy(), ref["out"], f"out skewed T={T} v{variant}")
 
 
 def test_forward_deterministic():
@@ -550,6 +552,44 @@ def test_empty_inputs():
 # ----------------------------------------------------------------- backward
 
 BWD_CASES = [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40)]
+
+
+def test_layer_backward_skewed():
+    """All tokens on two experts (300 rows each): the dgrad kernels cut each
+    expert into two 160-row tiles, and the adapter reductions run over long
+    row ranges."""
+    spec = LORA_SMALL
+    T = 300
+    say(f"backward skewed {spec.name} T={T}")
+    L = layer_of(spec)
+    ex = L.device()
+    x, _ = inp.host_tokens(spec, T)
+    lg = np.full((T, spec.E), -5.0, np.float32)
+    lg[:, 2] = 5.0
+    lg[:, 5] = 4.0
+    dout = inp.host_upstream_grad(spec, T)
+    res = run_layer(ex, to_dev(x), to_dev(lg), spec.k, save=True)
+    S = T * spec.k
+    dy = torch.empty((S, spec.H), dtype=torch.bfloat16, device=DEV)
+    e0 = torch.empty(S, dtype=torch.int32, device=DEV)
+    moe4.moe4_permute(res["idx"], spec.E, torch.empty_like(res["offsets"]), e0,
+                      torch.empty_like(e0), x=to_dev(dout), row_scale=res["w"].reshape(-1),
+                      x_perm=dy, ws=res["ws"])
+    dx_perm = torch.empty((S, spec.H), dtype=torch.float32, device=DEV)
+    dA = torch.full((spec.E, spec.lora_r, spec.H), float("nan"), device=DEV)
+    dB = torch.full((spec.E, 2 * spec.I, spec.lora_r), float("nan"), device=DEV)
+    moe4.moe4_expert_backward(ex, res["x_perm"], res["offsets"], res["save_gu"], res["save_xa"],
+                              dy, dx_perm, dA, dB, ws=res["ws"])
+    torch.cuda.synchronize()
+    ri, rw = oracle.route(lg, spec.k)
+    ref = oracle.layer_backward(x, ri, rw, dout, L.W)
+    assert_close(dx_perm.cpu().numpy(), ref["dx_perm"], "dx_perm")
+    dA_h, dB_h = dA.cpu().numpy(), dB.cpu().numpy()
+    for e in range(spec.E):
+        if e not in (2, 5):
+            assert np.all(dA_h[e] == 0) and np.all(dB_h[e] == 0)
+    assert_close(dA_h, ref["dA"], "dA")
+    assert_close(dB_h, ref["dB"], "dB")
 
 
 @pytest.mark.parametrize("spec,T", BWD_CASES, ids=[s.name for s, _ in BWD_CASES])
