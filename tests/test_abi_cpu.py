@@ -156,8 +156,9 @@ def test_lora_rank_and_workspace():
     assert _fwd(d) == moe4.MOE4_ESHAPE
     d = _desc(lora_A=FAKE, lora_B=FAKE, lora_r=8, lora_scale=2.0)
     need = lib.moe4_workspace_size(ctypes.byref(d), 64, 2)
-    # h [128, 512] bf16 + xa [128, 8] f32 (both 256-aligned) vs dGU [128, 1024] bf16 + t
-    assert need == max(128 * 512 * 2 + 128 * 8 * 4, 128 * 1024 * 2 + 128 * 8 * 4)
+    # forward: h [128, 512] bf16 + xa [128, 8] f32; backward: dGU [128, 1024] bf16 +
+    # t [128, 8] f32 + the transposed adapter B [8 experts, 8, 1024] bf16 (all 256-aligned)
+    assert need == max(128 * 512 * 2 + 128 * 8 * 4, 128 * 1024 * 2 + 128 * 8 * 4 + 8 * 8 * 1024 * 2)
     fwd_need = 128 * 512 * 2 + 128 * 8 * 4
     assert _fwd(d, rows=128, ws=FAKE, ws_bytes=fwd_need - 1) == moe4.MOE4_EWORKSPACE
     assert "131072" in moe4.moe4_last_error() or str(fwd_need) in moe4.moe4_last_error()
