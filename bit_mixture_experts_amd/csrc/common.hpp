@@ -85,11 +85,13 @@ __device__ __forceinline__ float sigmoidf_(float z) {
 
 // Locate work item q when expert e owns units(n_e) consecutive items
 // (n_e = offsets[e+1] - offsets[e]). Every lane of the wave gets the same
-// answer: e = -1 when q is past the last item, else the expert and the item's
-// index inside it. Offsets are read once per lane (a contiguous chunk).
+// answer: e = -1 when q is past the last item, else the expert, the item's
+// index inside it and the expert's row range [beg, end) = [offsets[e],
+// offsets[e+1]). Offsets are read once per lane (a contiguous chunk).
 template <typename Units>
 __device__ __forceinline__ void locate_item(const int32_t* __restrict__ offsets, int E, int q,
-                                            Units units, int& e_out, int& u_out) {
+                                            Units units, int& e_out, int& u_out, int& beg_out,
+                                            int& end_out) {
   const int l = lane_id();
   const int per = (E + kWave - 1) / kWave;
   const int e0 = l * per;
@@ -109,10 +111,11 @@ __device__ __forceinline__ void locate_item(const int32_t* __restrict__ offsets,
   if (b == 0ull) {
     e_out = -1;
     u_out = 0;
+    beg_out = end_out = 0;
     return;
   }
   int owner = __ffsll((long long)b) - 1;
-  int ef = -1, uf = 0;
+  int ef = -1, uf = 0, bf = 0, nf = 0;
   if (own) {
     int acc = excl;
     int prev = offsets[e0];
@@ -122,6 +125,8 @@ __device__ __forceinline__ void locate_item(const int32_t* __restrict__ offsets,
       if (q < acc + u) {
         ef = e0 + i;
         uf = q - acc;
+        bf = prev;
+        nf = nx;
         break;
       }
       acc += u;
@@ -130,6 +135,64 @@ __device__ __forceinline__ void locate_item(const int32_t* __restrict__ offsets,
   }
   e_out = __shfl(ef, owner, kWave);
   u_out = __shfl(uf, owner, kWave);
+  beg_out = __shfl(bf, owner, kWave);
+  end_out = __shfl(nf, owner, kWave);
+}
+// locate_item for E <= 64 * PER: each lane reads its PER + 1 offsets as one
+// batch of loads (no dependent round trips), keeps them in registers for the
+// second pass, and the answer is the same.
+template <int PER, typename Units>
+__device__ __forceinline__ void locate_item_batched(const int32_t* __restrict__ offsets, int E,
+                                                    int q, Units units, int& e_out, int& u_out,
+                                                    int& beg_out, int& end_out) {
+  const int l = lane_id();
+  const int e0 = l * PER;
+  const rsrc_t ro = make_rsrc(offsets, (uint32_t)(E + 1) * 4);
+  int o[PER + 1];
+#pragma unroll
+  for (int i = 0; i <= PER; ++i) o[i] = (int)buf_load_b32(ro, e0 + i <= E ? 4 * (e0 + i) : kOob);
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (e0 + i < E) cnt += units(o[i + 1] - o[i]);
+  const int incl = wave_inclusive_scan(cnt);
+  const int excl = incl - cnt;
+  const bool own = (q >= excl) && (q < incl);
+  const unsigned long long b = __ballot(own);
+  if (b == 0ull) {
+    e_out = -1;
+    u_out = 0;
+    beg_out = end_out = 0;
+    return;
+  }
+  const int owner = __ffsll((long long)b) - 1;
+  int ef = -1, uf = 0, bf = 0, nf = 0;
+  if (own) {
+    int acc = excl;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (e0 + i < E) {
+        const int u = units(o[i + 1] - o[i]);
+        if (ef < 0 && q < acc + u) {
+          ef = e0 + i;
+          uf = q - acc;
+          bf = o[i];
+          nf = o[i + 1];
+        }
+        acc += u;
+      }
+    }
+  }
+  e_out = __shfl(ef, owner, kWave);
+  u_out = __shfl(uf, owner, kWave);
+  beg_out = __shfl(bf, owner, kWave);
+  end_out = __shfl(nf, owner, kWave);
+}
+template <typename Units>
+__device__ __forceinline__ void locate_item(const int32_t* __restrict__ offsets, int E, int q,
+                                            Units units, int& e_out, int& u_out) {
+  int beg, end;
+  locate_item(offsets, E, q, units, e_out, u_out, beg, end);
 }
 
 // Work item of workgroup b in a grouped GEMM whose experts are cut into BM-row

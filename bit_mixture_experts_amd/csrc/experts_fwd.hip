@@ -13,15 +13,16 @@
 //
 // Two kernel families:
 //  * skinny (decode-sized row counts): one workgroup streams 32 weight rows of
-//    one expert over all of K, split across its waves; each wave dequantises
-//    its nibbles through an LDS byte table and runs 16x16x32 bf16 MFMA, one
-//    k-step per 32 weights; waves are reduced through LDS. NF4 weights get
-//    their absmax before the MFMA; MXFP4 blocks get their power-of-two scale
-//    on the fp32 partial product of the block (exact either way).
-//  * tiled (prefill-sized row counts): a 128-row tile of one expert's permuted
-//    activations is staged in LDS (double-buffered); each wave owns 64 weight
-//    rows, loads their nibbles straight into registers with 128-bit loads,
-//    dequantises with the scale folded in, and runs 32x32x16 bf16 MFMA.
+//    one expert over all of K, split across its waves, with the scales of its
+//    rows staged once in LDS; each wave loads 16-byte pieces of nibbles into
+//    registers, transposes them across lanes into MFMA order, dequantises them
+//    (NF4 through an LDS table of fp32 level pairs, MXFP4 in the hardware
+//    conversion) and runs 16x16x32 bf16 MFMA; waves are reduced through LDS.
+//  * tiled (prefill-sized row counts): one workgroup of eight waves per work
+//    item of up to 320 activation rows x 256 weight rows; activation tiles and
+//    packed weights arrive in a three-stage LDS ring by direct loads, every
+//    weight is dequantised once per workgroup, and each wave owns one 32-wide
+//    column tile on 32x32x16 bf16 MFMA against every row of the item.
 #include <type_traits>
 
 #include "common.hpp"
@@ -92,19 +93,57 @@ __device__ __forceinline__ float scale_operand(uint32_t raw) {
 
 // ------------------------------------------------------------ skinny kernel
 
-// Per-wave operands of one 128-k iteration of the skinny kernel.
+// 4x4 transpose of dwords across the four 16-lane rows of a wave: on entry
+// row g holds D[g][0..3] in v[0..3]; on exit row g holds D[0..3][g]. The
+// 32-lane swap trades the upper half of its first operand for the lower half
+// of its second; the 16-lane swap trades the odd rows of its first operand for
+// the even rows of its second.
+__device__ __forceinline__ void transpose4x4_rows(u32x4& v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  v[0] = c[0];
+  v[1] = c[1];
+  v[2] = d[0];
+  v[3] = d[1];
+}
+
+// Scale layout of the skinny kernel. The scales of the workgroup's 32 weight
+// rows are copied once into LDS by direct loads, a chunk of at most kKc k at a
+// time (one chunk for every K up to kKc): row r of the chunk starts in dword
+// r * pitch, shifted by the byte offset of the row's first scale within its
+// dword. The pitch is odd in dwords, so the 16 rows of a column tile sit in 16
+// different banks.
+template <int FMT>
+struct SkinnyScales {
+  static constexpr int kBytes = FMT == MOE4_FMT_NF4 ? 4 : 1;   // per block
+  static constexpr int kKb = Format<FMT>::kBlock;
+  static constexpr int kKc = FMT == MOE4_FMT_NF4 ? 8192 : 16384;
+  // dword pitch of one row for a chunk of kc k: the chunk's bytes, up to
+  // three bytes of lead, rounded up, and made odd
+  __host__ __device__ static constexpr int pitch(int kc) {
+    return (((kc / kKb) * kBytes + 3 + 3) / 4) | 1;
+  }
+  // the stage, rounded up to whole 64-dword loads
+  __host__ __device__ static constexpr int lds_bytes(int K) {
+    return (32 * pitch(K < kKc ? K : kKc) * 4 + 255) / 256 * 256;
+  }
+};
+
+// Per-wave operands of one 128-k iteration of the skinny kernel: the nibbles
+// of the two column tiles and the activation operands of the four MFMA steps.
 template <int NRT>
 struct SkinnyBatch {
   u32x4 wraw[2];
-  uint32_t sraw[2];    // scale word (fp32 absmax, e8m0 byte, or 8-bit absmax code)
   u32x4 av[NRT][4];
 };
 
 // Buffer resources and lane offsets of one wave of the skinny kernel.
 struct SkinnyLane {
-  rsrc_t rq, rs, ra;    // this expert's nibbles and scales; this row chunk's activations
+  rsrc_t rq, ra;        // this expert's nibbles; this row chunk's activations
   int qoff[2];          // byte offset of the lane's 16-byte column in weight row c, k = 0
-  int srow[2];          // weight row index of column tile c (inside the expert)
+  int sb[2];            // LDS byte address of the first staged scale of weight row c
   int a2bnd;            // double-quantised NF4: per c (16 bits each), the first block
                         // of weight row c that lies in the row's second absmax group
 };
@@ -118,61 +157,67 @@ struct SkinnyDq {
   float off;           // the stack's absmax offset
 };
 
-// Each k-iteration covers 128 k: lane (n = l%16, g = l/16) loads 16 bytes
+// Each k-iteration covers 128 k. Lane (n = l%16, g = l/16) loads 16 bytes
 // (32 k) of its weight row with one 128-bit load, so the four lanes of a row
-// read 64 contiguous bytes. Lane g's 32 k lie in one scale block (64 for NF4,
-// 32 for MXFP4); MFMA step s uses k = kb + 32g + 8s.
+// read 64 contiguous bytes; a 4x4 dword transpose across g then gives lane g,
+// for MFMA step s, the 8 k at kb + 32s + 8g. The activation operand of step s
+// is loaded in the same order (the four lanes of a row read 64 contiguous
+// bytes), and every step lies inside one scale block (64 for NF4, 32 for
+// MXFP4).
 template <int FMT, int NRT>
 __device__ __forceinline__ void skinny_load(SkinnyBatch<NRT>& bt, const SkinnyLane& sl, int K,
-                                            int it, int it1) {
-  constexpr int KB = Format<FMT>::kBlock;
-  constexpr int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
+                                            int kb, bool live) {
   const int l = lane_id(), nl = l & 15, g = l >> 4;
-  const int kb = it * 128;
-  const bool live = it < it1;
   const bool ink = live && kb + 32 * g < K;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    bt.wraw[c] = buf_load_b128(sl.rq, ink ? sl.qoff[c] + kb / 2 : kOob);
-    const int so = ink ? (sl.srow[c] * (K / KB) + (kb + 32 * g) / KB) * sbytes : kOob;
-    bt.sraw[c] = sbytes == 4 ? buf_load_b32(sl.rs, so) : buf_load_u8(sl.rs, so);
-  }
+  for (int c = 0; c < 2; ++c) bt.wraw[c] = buf_load_b128(sl.rq, ink ? sl.qoff[c] + kb / 2 : kOob);
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int m = rt * 16 + nl;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const int k = kb + 32 * g + 8 * st;
+      const int k = kb + 32 * st + 8 * g;
       bt.av[rt][st] = buf_load_b128(sl.ra, (live && k < K) ? (m * K + k) * 2 : kOob);
     }
   }
 }
 
+// Multiply one batch: iteration `it` of the chunk (its first block is
+// it * 128 / block of the staged row, nblk blocks staged). Blocks past the
+// staged ones (an iteration beyond K, whose activations are zero) take the
+// last staged scale, so every operand stays finite. Each weight becomes the
+// bf16 operand of dequant8 (NF4: bf16(fp32(level * absmax)); MXFP4: the exact
+// hardware conversion with the block's power of two).
 template <int FMT, int NRT>
 __device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const float2* lutf,
-                                               const SkinnyLane& sl, const SkinnyDq& dq, int K,
-                                               int it, f32x4 (&acc)[2][2]) {
-  float scs[2];
+                                               const uint8_t* stage, const SkinnyLane& sl,
+                                               const SkinnyDq& dq, int it, int nblk, int gblk0,
+                                               f32x4 (&acc)[2][2]) {
+  constexpr int KB = Format<FMT>::kBlock;
+  constexpr int NSC = 128 / KB;   // scale blocks per iteration: 2 (NF4) or 4 (MXFP4)
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    if constexpr (FMT == MOE4_FMT_NF4_DQ) {
-      // absmax = fp32(fp32(book[code] * absmax2) + offset); absmax2 is the
-      // row's first or second group scale
-      const int l = lane_id();
-      const int blk = 2 * it + (l >> 5);   // (128 it + 32 g) / 64
-      const int bnd = (sl.a2bnd >> (16 * c)) & 0xFFFF;
-      const float a2 = dq.a2tab[2 * (16 * c + (l & 15)) + (blk < bnd ? 0 : 1)];
-      scs[c] = mul_then_add(dq.book[bt.sraw[c] & 255u], a2, dq.off);
-    } else {
-      scs[c] = scale_operand<FMT>(bt.sraw[c]);
+    float sc[NSC];
+#pragma unroll
+    for (int j = 0; j < NSC; ++j) {
+      const int b = min(it * NSC + j, nblk - 1);
+      if constexpr (FMT == MOE4_FMT_NF4) {
+        sc[j] = *reinterpret_cast<const float*>(stage + sl.sb[c] + 4 * b);
+      } else if constexpr (FMT == MOE4_FMT_MXFP4) {
+        sc[j] = scale_operand<FMT>(stage[sl.sb[c] + b]);
+      } else {
+        // absmax = fp32(fp32(book[code] * absmax2) + offset); absmax2 is the
+        // row's first or second group scale
+        const int bnd = (sl.a2bnd >> (16 * c)) & 0xFFFF;
+        const float a2 = dq.a2tab[2 * (16 * c + (lane_id() & 15)) + (gblk0 + b < bnd ? 0 : 1)];
+        sc[j] = mul_then_add(dq.book[stage[sl.sb[c] + b]], a2, dq.off);
+      }
     }
-  }
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const float sc = scs[c];
+    u32x4 wq = bt.wraw[c];
+    transpose4x4_rows(wq);
     u32x4 bq[4];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) bq[st] = dequant8<FMT>(bt.wraw[c][st], sc, lutf);
+    for (int st = 0; st < 4; ++st) bq[st] = dequant8<FMT>(wq[st], sc[st * NSC / 4], lutf);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
@@ -183,110 +228,212 @@ __device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const
   }
 }
 
-// K loop of one wave over iterations [it0, it1) for NRT 16-row tiles; the
-// next iteration's loads are in flight while the current one is dequantised
-// and multiplied.
+// K loop of one wave over the iterations [it0, it1) of a chunk starting at k0,
+// for NRT 16-row tiles, with NB batches in a register ring: while one batch is
+// dequantised and multiplied, the loads of the next NB - 1 are in flight.
+// Loads are never skipped: an iteration past it1 reads out of bounds (zero
+// activations, no memory traffic), which keeps the count of loads in flight
+// the same on every path, so the compiler waits for exactly the batch it
+// needs. The prologue (the first NB - 1 batches) is a separate call so that
+// the first row chunk can issue it before the workgroup's set-up barrier.
+#ifndef SK_NB
+#define SK_NB 2
+#endif
+constexpr int kSkNb = SK_NB;
+
 template <int FMT, int NRT>
-__device__ __forceinline__ void skinny_kloop(const SkinnyLane& sl, int K, int it0, int it1,
-                                             const float2* lutf, const SkinnyDq& dq,
-                                             f32x4 (&acc)[2][2]) {
-  SkinnyBatch<NRT> b0, b1;
-  skinny_load<FMT>(b0, sl, K, it0, it1);
-  for (int it = it0; it < it1; it += 2) {
-    if (it + 1 < it1) skinny_load<FMT>(b1, sl, K, it + 1, it1);
-    skinny_compute<FMT>(b0, lutf, sl, dq, K, it, acc);
-    if (it + 1 >= it1) break;
-    if (it + 2 < it1) skinny_load<FMT>(b0, sl, K, it + 2, it1);
-    skinny_compute<FMT>(b1, lutf, sl, dq, K, it + 1, acc);
+__device__ __forceinline__ void skinny_prologue(SkinnyBatch<NRT> (&b)[kSkNb],
+                                                const SkinnyLane& sl, int K, int k0, int it0,
+                                                int it1) {
+#pragma unroll
+  for (int j = 0; j < kSkNb - 1; ++j)
+    skinny_load<FMT>(b[j], sl, K, k0 + 128 * (it0 + j), it0 + j < it1);
+}
+
+template <int FMT, int NRT>
+__device__ __forceinline__ void skinny_body(SkinnyBatch<NRT> (&b)[kSkNb], const SkinnyLane& sl,
+                                            int K, int k0, int it0, int it1, int nblk,
+                                            const float2* lutf, const uint8_t* stage,
+                                            const SkinnyDq& dq, f32x4 (&acc)[2][2]) {
+  constexpr int NB = kSkNb;
+  constexpr int KB = Format<FMT>::kBlock;
+  const int gblk0 = k0 / KB;
+  for (int it = it0; it < it1; it += NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int itn = it + j + NB - 1;
+      skinny_load<FMT>(b[(j + NB - 1) % NB], sl, K, k0 + 128 * itn, itn < it1);
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the arithmetic
+      if (NB == 2 || it + j < it1)
+        skinny_compute<FMT>(b[j], lutf, stage, sl, dq, it + j, nblk, gblk0, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
 // Skinny grouped GEMM: one workgroup = one expert x 32 weight rows (gate_up:
 // 16 (gate, up) pairs; down: 32 output columns); its S waves split K and are
-// reduced through LDS; the expert's rows are taken 32 at a time.
+// reduced through LDS; the expert's rows are taken 16 * MAXR at a time.
+//
+// Set-up is arranged so that its memory latencies overlap: the expert and its
+// row range come from one pass over the offsets; then the scales of the 32
+// weight rows (direct loads into LDS), the NF4 level table and the first
+// batch of weights and activations are all issued before a single wait and
+// the workgroup barrier.
+#ifndef SK_WPE
+#define SK_WPE 3
+#endif
+#ifndef SK_MAXR
+#define SK_MAXR 1
+#endif
 template <int FMT, bool GATEUP>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SK_WPE)))
 void k_skinny(const GemmArgs a) {
   using F = Format<FMT>;
+  using SS = SkinnyScales<FMT>;
   constexpr bool NF4 = FMT != MOE4_FMT_MXFP4;
   constexpr bool DQ = FMT == MOE4_FMT_NF4_DQ;
-  constexpr int MAXR = 2;
+  constexpr int MAXR = SK_MAXR;
   constexpr int KB = F::kBlock;
   // NF4 byte -> two fp32 levels; the absmax code book of a double-quantised stack
   __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
   __shared__ float dqbook[DQ ? 256 : 1];
   __shared__ float a2tab[DQ ? 64 : 1];
-  extern __shared__ __attribute__((aligned(16))) float red[];   // [S][MAXR][2][256]
-  const int S = blockDim.x >> 6, w = wave_id(), l = lane_id();
-  if (NF4)
-    for (int i = threadIdx.x; i < 256; i += blockDim.x)
-      lutf[i] = make_float2(F::level(i & 15), F::level(i >> 4));
-  if (DQ)
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) dqbook[i] = a.dqbook[i];
-  SkinnyDq dq{dqbook, a2tab, DQ ? a.dqoff[0] : 0.0f};
-  const int item = blockIdx.x / a.ncg, cg = blockIdx.x - item * a.ncg;
-  int e, unused;
-  locate_item(a.offsets, a.E, item, [](int n) { return n > 0 ? 1 : 0; }, e, unused);
-  e = __builtin_amdgcn_readfirstlane(e);
-  const int Nw0 = GATEUP ? 2 * a.I : a.N_out;
-  if (DQ && e >= 0 && threadIdx.x < 32) {
-    // group scales of the workgroup's 32 weight rows (row (c, n) = thread 16 c + n)
-    const int c = threadIdx.x >> 4, n = threadIdx.x & 15;
-    const int row = GATEUP ? (c == 0 ? gate_row(a.layout, a.I, cg * 16 + n)
-                                     : up_row(a.layout, a.I, cg * 16 + n))
-                           : cg * 32 + 16 * c + n;
-    const int64_t ng = ((int64_t)a.E * Nw0 * (a.K / KB) + 255) / 256;
-    const int64_t g0 = (((int64_t)e * Nw0 + row) * (a.K / KB)) >> 8;
-    a2tab[2 * threadIdx.x] = a.ws2[g0];
-    a2tab[2 * threadIdx.x + 1] = g0 + 1 < ng ? a.ws2[g0 + 1] : 0.0f;
-  }
-  __syncthreads();
-  if (e < 0) return;
+  // [32 rows][pitch] staged scales (rounded up to 256 bytes), then
+  // [S][MAXR][2][256] partial sums
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int K = a.K;
-  const int rbeg = min(a.offsets[e], a.rows);
-  const int n_e = min(a.offsets[e + 1], a.rows) - rbeg;
-  const int nl = l & 15, g = l >> 4;
+  const int pdw = SS::pitch(min(K, SS::kKc));
+  uint8_t* stage = dyn;
+  float* red = reinterpret_cast<float*>(dyn + SS::lds_bytes(K));
+  const int S = blockDim.x >> 6, w = wave_id(), l = lane_id();
+  const int item = blockIdx.x / a.ncg, cg = blockIdx.x - item * a.ncg;
+  int e, unused, rbeg, rend;
+  auto nonempty = [](int n) { return n > 0 ? 1 : 0; };
+  if (a.E <= 128) locate_item_batched<2>(a.offsets, a.E, item, nonempty, e, unused, rbeg, rend);
+  else locate_item(a.offsets, a.E, item, nonempty, e, unused, rbeg, rend);
+  e = __builtin_amdgcn_readfirstlane(e);
+  if (e < 0) return;   // the whole workgroup: e is uniform
+  rbeg = __builtin_amdgcn_readfirstlane(min(rbeg, a.rows));
+  const int n_e = __builtin_amdgcn_readfirstlane(min(rend, a.rows)) - rbeg;
   const int Nw = GATEUP ? 2 * a.I : a.N_out;
-  SkinnyLane sl;
-  if (GATEUP) {
-    const int j = cg * 16 + nl;
-    sl.srow[0] = gate_row(a.layout, a.I, j);
-    sl.srow[1] = up_row(a.layout, a.I, j);
-  } else {
-    sl.srow[0] = cg * 32 + nl;
-    sl.srow[1] = cg * 32 + 16 + nl;
+  // weight row (inside the expert) of the workgroup's row r = 16 c + n
+  auto wrow = [&](int r) {
+    const int c = r >> 4, n = r & 15;
+    return GATEUP ? (c == 0 ? gate_row(a.layout, a.I, cg * 16 + n)
+                            : up_row(a.layout, a.I, cg * 16 + n))
+                  : cg * 32 + r;
+  };
+  const int rowbytes = (K / KB) * SS::kBytes;
+  const rsrc_t rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Nw * rowbytes,
+                              (uint32_t)Nw * rowbytes);
+  // direct loads of the scales of chunk [k0, k0 + kc) of the 32 rows: dword j
+  // of the stage is dword j % pdw of row j / pdw's covering span; the waves
+  // take the 64-dword pieces in turn (a piece may cross rows)
+  const float inv_pdw = 1.0f / (float)pdw;
+  auto stage_issue = [&](int k0) {
+    const int c0 = (k0 / KB) * SS::kBytes;
+    const int npiece = (32 * pdw + 63) / 64;
+    for (int q = w; q < npiece; q += S) {
+      const int j = 64 * q + l;
+      // j / pdw for j < 2^16: the rounded quotient of the float product is exact
+      const int r = (int)(((float)j + 0.5f) * inv_pdw), d = j - r * pdw;
+      const int off = r < 32 ? ((wrow(r) * rowbytes + c0) & ~3) + 4 * d : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE4_LDS(stage + 256 * q), 4, off, 0, 0, 0);
+    }
+  };
+  // the NF4 level pairs (2 KiB), by direct loads into LDS as well
+  auto lut_issue = [&]() {
+    if constexpr (NF4) {
+      const rsrc_t rl = make_rsrc(kNf4Pairs.v, sizeof(kNf4Pairs.v));
+      for (int q = w; q < 8; q += S)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rl, MOE4_LDS(reinterpret_cast<uint8_t*>(lutf) + 256 * q), 4, 256 * q + 4 * l, 0, 0,
+            0);
+    }
+  };
+  if constexpr (DQ) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) dqbook[i] = a.dqbook[i];
+    if (threadIdx.x < 32) {
+      // group scales of the workgroup's 32 weight rows (row (c, n) = thread 16 c + n)
+      const int64_t ng = ((int64_t)a.E * Nw * (K / KB) + 255) / 256;
+      const int64_t g0 = (((int64_t)e * Nw + wrow(threadIdx.x)) * (K / KB)) >> 8;
+      a2tab[2 * threadIdx.x] = a.ws2[g0];
+      a2tab[2 * threadIdx.x + 1] = g0 + 1 < ng ? a.ws2[g0 + 1] : 0.0f;
+    }
   }
+  SkinnyDq dq{dqbook, a2tab, DQ ? a.dqoff[0] : 0.0f};
+  const int nl = l & 15, g = l >> 4;
+  SkinnyLane sl;
+  int srow[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) srow[c] = wrow(16 * c + nl);
   sl.rq = make_rsrc(a.wq + (int64_t)e * Nw * (K / 2), (uint32_t)Nw * (K / 2));
-  constexpr int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
-  sl.rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Nw * (K / KB) * sbytes,
-                    (uint32_t)Nw * (K / KB) * sbytes);
   if (DQ) {
     sl.a2bnd = 0;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      sl.a2bnd |= (256 - (int)((((int64_t)e * Nw + sl.srow[c]) * (K / KB)) & 255)) << (16 * c);
+      sl.a2bnd |= (256 - (int)((((int64_t)e * Nw + srow[c]) * (K / KB)) & 255)) << (16 * c);
   }
 #pragma unroll
-  for (int c = 0; c < 2; ++c) sl.qoff[c] = sl.srow[c] * (K / 2) + 16 * g;
-  const int nit = (K + 127) / 128;
-  const int it0 = (int)((int64_t)w * nit / S), it1 = (int)((int64_t)(w + 1) * nit / S);
+  for (int c = 0; c < 2; ++c) sl.qoff[c] = srow[c] * (K / 2) + 16 * g;
+  const int nchunk = (K + SS::kKc - 1) / SS::kKc;
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int rc = 0; rc < n_e; rc += 16 * MAXR) {
+  // rows [rc, rc + 16 MAXR) of the expert; FIRST: the first chunk of rows,
+  // whose first chunk of K finishes the set-up
+  auto run_rows = [&](auto nrt_c, auto first_c, int rc) {
+    constexpr int NRT = decltype(nrt_c)::value;
+    constexpr bool FIRST = decltype(first_c)::value;
     const int nrows = min(16 * MAXR, n_e - rc);
-    const int nrt = (nrows + 15) >> 4;
     f32x4 acc[2][2] = {{zero4, zero4}, {zero4, zero4}};
-    sl.ra = make_rsrc(a.A + (int64_t)(rbeg + rc) * K, (uint32_t)nrows * K * 2);
-    if (nrt == 1) skinny_kloop<FMT, 1>(sl, K, it0, it1, lutf, dq, acc);
-    else skinny_kloop<FMT, 2>(sl, K, it0, it1, lutf, dq, acc);
+    sl.ra = make_rsrc(a.A + (int64_t)(rbeg + rc) * K, (uint32_t)max(nrows, 0) * K * 2);
+    SkinnyBatch<NRT> b[kSkNb];
+    // chunk ch of K: its scales in the stage, then the wave's iterations
+    auto chunk = [&](int ch, bool setup) {
+      const int k0 = ch * SS::kKc, kc = min(SS::kKc, K - k0);
+      const int c0 = (k0 / KB) * SS::kBytes;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        sl.sb[c] = (16 * c + nl) * pdw * 4 + ((srow[c] * rowbytes + c0) & 3);
+      const int nit = (kc + 127) / 128;
+      const int it0 = (int)((int64_t)w * nit / S), it1 = (int)((int64_t)(w + 1) * nit / S);
+      skinny_prologue<FMT>(b, sl, K, k0, it0, it1);
+      if (setup) {
+        // the scales and level pairs travel together with the first batch
+        __builtin_amdgcn_sched_barrier(0);
+        stage_issue(0);
+        lut_issue();
+        wait_vmcnt<0>();
+        lds_barrier();
+      }
+      skinny_body<FMT>(b, sl, K, k0, it0, it1, kc / KB, lutf, stage, dq, acc);
+    };
+    auto restage = [&](int ch) {
+      __syncthreads();   // every wave is done with the staged scales
+      stage_issue(ch * SS::kKc);
+      wait_vmcnt<0>();
+      __syncthreads();
+    };
+    // the first chunk of the first row chunk is straight-line code after the
+    // set-up (no merge with a loop's back edge before its prologue)
+    if (FIRST) {
+      chunk(0, true);
+    } else {
+      if (nchunk > 1) restage(0);
+      chunk(0, false);
+    }
+    for (int ch = 1; ch < nchunk; ++ch) {
+      restage(ch);
+      chunk(ch, false);
+    }
     // reduce the S partial sums through LDS: red[w][rt][c][lane*4 + i]
 #pragma unroll
-    for (int rt = 0; rt < MAXR; ++rt)
-      if (rt < nrt)
+    for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          *reinterpret_cast<f32x4*>(red + (((size_t)w * MAXR + rt) * 2 + c) * 256 + l * 4) =
-              acc[rt][c];
+      for (int c = 0; c < 2; ++c)
+        *reinterpret_cast<f32x4*>(red + (((size_t)w * MAXR + rt) * 2 + c) * 256 + l * 4) =
+            acc[rt][c];
     __syncthreads();
     if (GATEUP) {
       for (int el = threadIdx.x; el < nrows * 16; el += blockDim.x) {
@@ -312,6 +459,16 @@ void k_skinny(const GemmArgs a) {
       }
     }
     __syncthreads();
+  };
+  using One = std::integral_constant<int, 1>;
+  using Max = std::integral_constant<int, MAXR>;
+  using Yes = std::true_type;
+  using No = std::false_type;
+  if (MAXR == 1 || n_e <= 16) run_rows(One{}, Yes{}, 0);
+  else run_rows(Max{}, Yes{}, 0);
+  for (int rc = 16 * MAXR; rc < n_e; rc += 16 * MAXR) {
+    if (MAXR == 1 || n_e - rc <= 16) run_rows(One{}, No{}, rc);
+    else run_rows(Max{}, No{}, rc);
   }
 }
 
@@ -320,10 +477,9 @@ void k_skinny(const GemmArgs a) {
 // One workgroup per CU: eight waves, an expert tile of up to kBM rows and 256
 // weight rows (gate_up: 128 (gate, up) pairs; down: 256 output columns).
 // Wave w owns 32 of the weight rows -- one 32-wide MFMA column tile -- against
-// every row of the tile, so each weight is dequantised once per workgroup and
-// each wave's dequantisation work per MFMA is a quarter of a 128-row tile's
-// with two column tiles per wave. An expert whose rows fit in kBM takes one
-// tile; larger experts are cut into equal tiles (multiples of 32 rows).
+// every row of the tile, so each weight is dequantised once per workgroup. An
+// expert whose rows fit in kBM takes one tile; larger experts are cut into
+// equal tiles (multiples of 32 rows).
 constexpr int kBM = 320, kBN = 256, kBK = 64, kStages = 3, kTiledWaves = 8;
 constexpr int kMaxRowTiles = kBM / 32;
 // One LDS stage holds a k-tile of 64: the A tile [kBM rows][128 B] with the
@@ -672,11 +828,14 @@ hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
   const int nit = (a.K + 127) / 128;
   int S = (6144 + nwg - 1) / nwg;
   S = max(1, min(S, min(8, nit / 2)));
-  constexpr int MAXR = 2;
-  const size_t lds = (size_t)S * MAXR * 2 * 256 * sizeof(float);
+  constexpr int MAXR = SK_MAXR;
+  using SS = SkinnyScales<FMT>;
+  // staged scales, then the partial sums of the S waves
+  const size_t lds = SS::lds_bytes(a.K) + (size_t)S * MAXR * 2 * 256 * sizeof(float);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_skinny<FMT, GATEUP>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(8 * MAXR * 2 * 256 * sizeof(float)));
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)(SS::lds_bytes(SS::kKc) + 8 * MAXR * 2 * 256 * sizeof(float)));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((k_skinny<FMT, GATEUP>), dim3(nwg), dim3(64 * S), lds, s, a);
   return hipGetLastError();

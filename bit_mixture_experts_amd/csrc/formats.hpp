@@ -63,6 +63,21 @@ struct Format<MOE4_FMT_NF4_DQ> {
   __device__ static float level(int c) { return kNf4Levels[c]; }
 };
 
+// byte -> the fp32 NF4 levels of its two nibbles (low nibble first): a
+// 2 KiB table in device memory that kernels copy into LDS
+struct Nf4Pairs {
+  float v[512];
+};
+constexpr Nf4Pairs make_nf4_pairs() {
+  Nf4Pairs p{};
+  for (int i = 0; i < 256; ++i) {
+    p.v[2 * i] = kNf4Levels[i & 15];
+    p.v[2 * i + 1] = kNf4Levels[i >> 4];
+  }
+  return p;
+}
+__device__ constexpr Nf4Pairs kNf4Pairs = make_nf4_pairs();
+
 // byte -> two bf16 levels (low nibble in the low half)
 template <int FMT>
 __device__ __forceinline__ uint32_t lut_bf16x2(int byte) {
