@@ -109,7 +109,7 @@ __device__ __forceinline__ void transpose4x4_rows(u32x4& v) {
   v[3] = d[1];
 }
 
-// Scale layout of the skinny kernel. The scales of the workgroup's 32 weight
+// Scale layout of the skinny kernel. The scales of the workgroup's weight
 // rows are copied once into LDS by direct loads, a chunk of at most kKc k at a
 // time (one chunk for every K up to kKc): row r of the chunk starts in dword
 // r * pitch, shifted by the byte offset of the row's first scale within its
@@ -125,35 +125,43 @@ struct SkinnyScales {
   __host__ __device__ static constexpr int pitch(int kc) {
     return (((kc / kKb) * kBytes + 3 + 3) / 4) | 1;
   }
-  // the stage, rounded up to whole 64-dword loads
-  __host__ __device__ static constexpr int lds_bytes(int K) {
-    return (32 * pitch(K < kKc ? K : kKc) * 4 + 255) / 256 * 256;
+  // the stage of nrow rows, rounded up to whole 64-dword loads
+  __host__ __device__ static constexpr int lds_bytes(int K, int nrow) {
+    return (nrow * pitch(K < kKc ? K : kKc) * 4 + 255) / 256 * 256;
   }
 };
 
+// Column tiles of 16 weight rows per wave of the skinny kernel: every
+// activation operand feeds kSkNc MFMAs.
+#ifndef SK_NC
+#define SK_NC 2
+#endif
+constexpr int kSkNc = SK_NC;
+static_assert(kSkNc == 2 || kSkNc == 4, "8 kSkNc gate/up pairs must divide I (a multiple of 32)");
+
 // Per-wave operands of one 128-k iteration of the skinny kernel: the nibbles
-// of the two column tiles and the activation operands of the four MFMA steps.
+// of the column tiles and the activation operands of the four MFMA steps.
 template <int NRT>
 struct SkinnyBatch {
-  u32x4 wraw[2];
+  u32x4 wraw[kSkNc];
   u32x4 av[NRT][4];
 };
 
 // Buffer resources and lane offsets of one wave of the skinny kernel.
 struct SkinnyLane {
   rsrc_t rq, ra;        // this expert's nibbles; this row chunk's activations
-  int qoff[2];          // byte offset of the lane's 16-byte column in weight row c, k = 0
-  int sb[2];            // LDS byte address of the first staged scale of weight row c
-  int a2bnd;            // double-quantised NF4: per c (16 bits each), the first block
-                        // of weight row c that lies in the row's second absmax group
+  int qoff[kSkNc];      // byte offset of the lane's 16-byte column in weight row c, k = 0
+  int sb[kSkNc];        // LDS byte address of the first staged scale of weight row c
+  int a2bnd[kSkNc];     // double-quantised NF4: the first block of weight row c that
+                        // lies in the row's second absmax group
 };
 
-// Double-quantised NF4 in the skinny kernel: the workgroup's 32 weight rows
+// Double-quantised NF4 in the skinny kernel: the workgroup's weight rows
 // each span at most two groups of 256 absmax (rows of at most 256 blocks);
 // a2tab[2 * (16 c + n) + h] holds the group scale of half h of row (c, n).
 struct SkinnyDq {
   const float* book;   // LDS: the 256-entry code book
-  const float* a2tab;  // LDS: [32 rows][2]
+  const float* a2tab;  // LDS: [16 kSkNc rows][2]
   float off;           // the stack's absmax offset
 };
 
@@ -170,7 +178,8 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<NRT>& bt, const SkinnyLa
   const int l = lane_id(), nl = l & 15, g = l >> 4;
   const bool ink = live && kb + 32 * g < K;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) bt.wraw[c] = buf_load_b128(sl.rq, ink ? sl.qoff[c] + kb / 2 : kOob);
+  for (int c = 0; c < kSkNc; ++c)
+    bt.wraw[c] = buf_load_b128(sl.rq, ink ? sl.qoff[c] + kb / 2 : kOob);
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int m = rt * 16 + nl;
@@ -192,11 +201,11 @@ template <int FMT, int NRT>
 __device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const float2* lutf,
                                                const uint8_t* stage, const SkinnyLane& sl,
                                                const SkinnyDq& dq, int it, int nblk, int gblk0,
-                                               f32x4 (&acc)[2][2]) {
+                                               f32x4 (&acc)[2][kSkNc]) {
   constexpr int KB = Format<FMT>::kBlock;
   constexpr int NSC = 128 / KB;   // scale blocks per iteration: 2 (NF4) or 4 (MXFP4)
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < kSkNc; ++c) {
     float sc[NSC];
 #pragma unroll
     for (int j = 0; j < NSC; ++j) {
@@ -208,8 +217,8 @@ __device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const
       } else {
         // absmax = fp32(fp32(book[code] * absmax2) + offset); absmax2 is the
         // row's first or second group scale
-        const int bnd = (sl.a2bnd >> (16 * c)) & 0xFFFF;
-        const float a2 = dq.a2tab[2 * (16 * c + (lane_id() & 15)) + (gblk0 + b < bnd ? 0 : 1)];
+        const float a2 =
+            dq.a2tab[2 * (16 * c + (lane_id() & 15)) + (gblk0 + b < sl.a2bnd[c] ? 0 : 1)];
         sc[j] = mul_then_add(dq.book[stage[sl.sb[c] + b]], a2, dq.off);
       }
     }
@@ -254,7 +263,7 @@ template <int FMT, int NRT>
 __device__ __forceinline__ void skinny_body(SkinnyBatch<NRT> (&b)[kSkNb], const SkinnyLane& sl,
                                             int K, int k0, int it0, int it1, int nblk,
                                             const float2* lutf, const uint8_t* stage,
-                                            const SkinnyDq& dq, f32x4 (&acc)[2][2]) {
+                                            const SkinnyDq& dq, f32x4 (&acc)[2][kSkNc]) {
   constexpr int NB = kSkNb;
   constexpr int KB = Format<FMT>::kBlock;
   const int gblk0 = k0 / KB;
@@ -271,13 +280,15 @@ __device__ __forceinline__ void skinny_body(SkinnyBatch<NRT> (&b)[kSkNb], const 
   }
 }
 
-// Skinny grouped GEMM: one workgroup = one expert x 32 weight rows (gate_up:
-// 16 (gate, up) pairs; down: 32 output columns); its S waves split K and are
-// reduced through LDS; the expert's rows are taken 16 * MAXR at a time.
+// Skinny grouped GEMM: one workgroup = one expert x 16 kSkNc weight rows
+// (gate_up: 8 kSkNc (gate, up) pairs, the first half of the column tiles gate
+// rows and the second half the matching up rows; down: 16 kSkNc output
+// columns); its S waves split K and are reduced through LDS; the expert's rows
+// are taken 16 * MAXR at a time.
 //
 // Set-up is arranged so that its memory latencies overlap: the expert and its
-// row range come from one pass over the offsets; then the scales of the 32
-// weight rows (direct loads into LDS), the NF4 level table and the first
+// row range come from one pass over the offsets; then the scales of the
+// workgroup's weight rows (direct loads into LDS), the NF4 level table and the first
 // batch of weights and activations are all issued before a single wait and
 // the workgroup barrier.
 #ifndef SK_WPE
@@ -298,14 +309,15 @@ void k_skinny(const GemmArgs a) {
   // NF4 byte -> two fp32 levels; the absmax code book of a double-quantised stack
   __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
   __shared__ float dqbook[DQ ? 256 : 1];
-  __shared__ float a2tab[DQ ? 64 : 1];
-  // [32 rows][pitch] staged scales (rounded up to 256 bytes), then
-  // [S][MAXR][2][256] partial sums
+  __shared__ float a2tab[DQ ? 32 * kSkNc : 1];
+  constexpr int NROW = 16 * kSkNc;   // weight rows of the workgroup
+  // [NROW rows][pitch] staged scales (rounded up to 256 bytes), then
+  // [S][MAXR][kSkNc][256] partial sums
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int K = a.K;
   const int pdw = SS::pitch(min(K, SS::kKc));
   uint8_t* stage = dyn;
-  float* red = reinterpret_cast<float*>(dyn + SS::lds_bytes(K));
+  float* red = reinterpret_cast<float*>(dyn + SS::lds_bytes(K, NROW));
   const int S = blockDim.x >> 6, w = wave_id(), l = lane_id();
   const int item = blockIdx.x / a.ncg, cg = blockIdx.x - item * a.ncg;
   int e, unused, rbeg, rend;
@@ -319,26 +331,27 @@ void k_skinny(const GemmArgs a) {
   const int Nw = GATEUP ? 2 * a.I : a.N_out;
   // weight row (inside the expert) of the workgroup's row r = 16 c + n
   auto wrow = [&](int r) {
+    constexpr int H2 = kSkNc / 2;
     const int c = r >> 4, n = r & 15;
-    return GATEUP ? (c == 0 ? gate_row(a.layout, a.I, cg * 16 + n)
-                            : up_row(a.layout, a.I, cg * 16 + n))
-                  : cg * 32 + r;
+    return GATEUP ? (c < H2 ? gate_row(a.layout, a.I, cg * 8 * kSkNc + 16 * c + n)
+                            : up_row(a.layout, a.I, cg * 8 * kSkNc + 16 * (c - H2) + n))
+                  : cg * NROW + r;
   };
   const int rowbytes = (K / KB) * SS::kBytes;
   const rsrc_t rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Nw * rowbytes,
                               (uint32_t)Nw * rowbytes);
-  // direct loads of the scales of chunk [k0, k0 + kc) of the 32 rows: dword j
+  // direct loads of the scales of chunk [k0, k0 + kc) of the rows: dword j
   // of the stage is dword j % pdw of row j / pdw's covering span; the waves
   // take the 64-dword pieces in turn (a piece may cross rows)
   const float inv_pdw = 1.0f / (float)pdw;
   auto stage_issue = [&](int k0) {
     const int c0 = (k0 / KB) * SS::kBytes;
-    const int npiece = (32 * pdw + 63) / 64;
+    const int npiece = (NROW * pdw + 63) / 64;
     for (int q = w; q < npiece; q += S) {
       const int j = 64 * q + l;
       // j / pdw for j < 2^16: the rounded quotient of the float product is exact
       const int r = (int)(((float)j + 0.5f) * inv_pdw), d = j - r * pdw;
-      const int off = r < 32 ? ((wrow(r) * rowbytes + c0) & ~3) + 4 * d : kOob;
+      const int off = r < NROW ? ((wrow(r) * rowbytes + c0) & ~3) + 4 * d : kOob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE4_LDS(stage + 256 * q), 4, off, 0, 0, 0);
     }
   };
@@ -354,29 +367,28 @@ void k_skinny(const GemmArgs a) {
   };
   if constexpr (DQ) {
     for (int i = threadIdx.x; i < 256; i += blockDim.x) dqbook[i] = a.dqbook[i];
-    if (threadIdx.x < 32) {
-      // group scales of the workgroup's 32 weight rows (row (c, n) = thread 16 c + n)
+    for (int t = threadIdx.x; t < NROW; t += blockDim.x) {
+      // group scales of the workgroup's weight rows (row (c, n) = t = 16 c + n)
       const int64_t ng = ((int64_t)a.E * Nw * (K / KB) + 255) / 256;
-      const int64_t g0 = (((int64_t)e * Nw + wrow(threadIdx.x)) * (K / KB)) >> 8;
-      a2tab[2 * threadIdx.x] = a.ws2[g0];
-      a2tab[2 * threadIdx.x + 1] = g0 + 1 < ng ? a.ws2[g0 + 1] : 0.0f;
+      const int64_t g0 = (((int64_t)e * Nw + wrow(t)) * (K / KB)) >> 8;
+      a2tab[2 * t] = g0 < ng ? a.ws2[g0] : 0.0f;   // rows past Nw: unused
+      a2tab[2 * t + 1] = g0 + 1 < ng ? a.ws2[g0 + 1] : 0.0f;
     }
   }
   SkinnyDq dq{dqbook, a2tab, DQ ? a.dqoff[0] : 0.0f};
   const int nl = l & 15, g = l >> 4;
   SkinnyLane sl;
-  int srow[2];
+  int srow[kSkNc];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) srow[c] = wrow(16 * c + nl);
+  for (int c = 0; c < kSkNc; ++c) srow[c] = wrow(16 * c + nl);
   sl.rq = make_rsrc(a.wq + (int64_t)e * Nw * (K / 2), (uint32_t)Nw * (K / 2));
   if (DQ) {
-    sl.a2bnd = 0;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-      sl.a2bnd |= (256 - (int)((((int64_t)e * Nw + srow[c]) * (K / KB)) & 255)) << (16 * c);
+    for (int c = 0; c < kSkNc; ++c)
+      sl.a2bnd[c] = 256 - (int)((((int64_t)e * Nw + srow[c]) * (K / KB)) & 255);
   }
 #pragma unroll
-  for (int c = 0; c < 2; ++c) sl.qoff[c] = srow[c] * (K / 2) + 16 * g;
+  for (int c = 0; c < kSkNc; ++c) sl.qoff[c] = srow[c] * (K / 2) + 16 * g;
   const int nchunk = (K + SS::kKc - 1) / SS::kKc;
   const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -386,7 +398,11 @@ void k_skinny(const GemmArgs a) {
     constexpr int NRT = decltype(nrt_c)::value;
     constexpr bool FIRST = decltype(first_c)::value;
     const int nrows = min(16 * MAXR, n_e - rc);
-    f32x4 acc[2][2] = {{zero4, zero4}, {zero4, zero4}};
+    f32x4 acc[2][kSkNc];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int c = 0; c < kSkNc; ++c) acc[rt][c] = zero4;
     sl.ra = make_rsrc(a.A + (int64_t)(rbeg + rc) * K, (uint32_t)max(nrows, 0) * K * 2);
     SkinnyBatch<NRT> b[kSkNb];
     // chunk ch of K: its scales in the stage, then the wave's iterations
@@ -394,7 +410,7 @@ void k_skinny(const GemmArgs a) {
       const int k0 = ch * SS::kKc, kc = min(SS::kKc, K - k0);
       const int c0 = (k0 / KB) * SS::kBytes;
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < kSkNc; ++c)
         sl.sb[c] = (16 * c + nl) * pdw * 4 + ((srow[c] * rowbytes + c0) & 3);
       const int nit = (kc + 127) / 128;
       const int it0 = (int)((int64_t)w * nit / S), it1 = (int)((int64_t)(w + 1) * nit / S);
@@ -431,31 +447,34 @@ void k_skinny(const GemmArgs a) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        *reinterpret_cast<f32x4*>(red + (((size_t)w * MAXR + rt) * 2 + c) * 256 + l * 4) =
+      for (int c = 0; c < kSkNc; ++c)
+        *reinterpret_cast<f32x4*>(red + (((size_t)w * MAXR + rt) * kSkNc + c) * 256 + l * 4) =
             acc[rt][c];
     __syncthreads();
     if (GATEUP) {
-      for (int el = threadIdx.x; el < nrows * 16; el += blockDim.x) {
-        const int m = el >> 4, jj = el & 15;
-        const int rt = m >> 4, mr = m & 15;
-        const int off = (16 * (mr >> 2) + jj) * 4 + (mr & 3);
+      // pair jj of the workgroup: gate in column tile jj / 16, up in tile
+      // jj / 16 + kSkNc / 2
+      for (int el = threadIdx.x; el < nrows * 8 * kSkNc; el += blockDim.x) {
+        const int m = el / (8 * kSkNc), jj = el - m * 8 * kSkNc;
+        const int rt = m >> 4, mr = m & 15, ct = jj >> 4, n = jj & 15;
+        const int off = (16 * (mr >> 2) + n) * 4 + (mr & 3);
         float gs = 0.0f, us = 0.0f;
         for (int ww = 0; ww < S; ++ww) {
-          const float* p = red + ((size_t)ww * MAXR + rt) * 2 * 256;
-          gs += p[off];
-          us += p[256 + off];
+          const float* p = red + ((size_t)ww * MAXR + rt) * kSkNc * 256;
+          gs += p[ct * 256 + off];
+          us += p[(ct + kSkNc / 2) * 256 + off];
         }
-        gate_up_epilogue(a, e, rbeg + rc + m, cg * 16 + jj, gs, us);
+        gate_up_epilogue(a, e, rbeg + rc + m, cg * 8 * kSkNc + jj, gs, us);
       }
     } else {
-      for (int el = threadIdx.x; el < nrows * 32; el += blockDim.x) {
-        const int m = el >> 5, cc = el & 31;
-        const int rt = m >> 4, mr = m & 15, ct = cc >> 4, jj = cc & 15;
-        const int off = (16 * (mr >> 2) + jj) * 4 + (mr & 3);
+      for (int el = threadIdx.x; el < nrows * NROW; el += blockDim.x) {
+        const int m = el / NROW, cc = el - m * NROW;
+        const int rt = m >> 4, mr = m & 15, ct = cc >> 4, n = cc & 15;
+        const int off = (16 * (mr >> 2) + n) * 4 + (mr & 3);
         float ys = 0.0f;
-        for (int ww = 0; ww < S; ++ww) ys += red[(((size_t)ww * MAXR + rt) * 2 + ct) * 256 + off];
-        down_epilogue(a, e, rbeg + rc + m, cg * 32 + cc, ys);
+        for (int ww = 0; ww < S; ++ww)
+          ys += red[(((size_t)ww * MAXR + rt) * kSkNc + ct) * 256 + off];
+        if (cg * NROW + cc < a.N_out) down_epilogue(a, e, rbeg + rc + m, cg * NROW + cc, ys);
       }
     }
     __syncthreads();
@@ -826,16 +845,20 @@ hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
   // split K over S waves so that ~6K waves stream the weights (about six per
   // SIMD), each wave keeping at least two 128-k iterations
   const int nit = (a.K + 127) / 128;
-  int S = (6144 + nwg - 1) / nwg;
+#ifndef SK_TGT
+#define SK_TGT 6144
+#endif
+  int S = (SK_TGT + nwg - 1) / nwg;
   S = max(1, min(S, min(8, nit / 2)));
   constexpr int MAXR = SK_MAXR;
   using SS = SkinnyScales<FMT>;
   // staged scales, then the partial sums of the S waves
-  const size_t lds = SS::lds_bytes(a.K) + (size_t)S * MAXR * 2 * 256 * sizeof(float);
+  const size_t lds =
+      SS::lds_bytes(a.K, 16 * kSkNc) + (size_t)S * MAXR * kSkNc * 256 * sizeof(float);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_skinny<FMT, GATEUP>),
       hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)(SS::lds_bytes(SS::kKc) + 8 * MAXR * 2 * 256 * sizeof(float)));
+      (int)(SS::lds_bytes(SS::kKc, 16 * kSkNc) + 8 * MAXR * kSkNc * 256 * sizeof(float)));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((k_skinny<FMT, GATEUP>), dim3(nwg), dim3(64 * S), lds, s, a);
   return hipGetLastError();
@@ -908,8 +931,10 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
   const int touched = min(E, rows);
   hipError_t err;
   if (variant == MOE4_VARIANT_SKINNY) {
-    g.ncg = I / 16;
-    d.ncg = H / 32;
+    // I is a multiple of 32 (the pairs of a column group); H may end in a
+    // partial column group, whose rows past H read as zeros and are not stored
+    g.ncg = I / (8 * kSkNc);
+    d.ncg = (H + 16 * kSkNc - 1) / (16 * kSkNc);
     le.before(0, s);
     err = run_skinny<FMT, true>(g, touched, s);
     le.after(0, s);

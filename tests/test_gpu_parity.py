@@ -28,6 +28,12 @@ LORA_SMALL = inp.QWEN3_30B_NF4_LORA.scaled(name="lora_small", seed_id=104, E=8, 
 MXFP4_LORA_SMALL = inp.GPT_OSS_20B_MXFP4.scaled(name="mxfp4_lora_small", seed_id=105, E=8, k=2,
                                                 H=320, I=192, tokens=(40,), lora_r=4,
                                                 lora_alpha=8.0)
+# rows longer than one staged chunk of scales in the decode kernel (8192 k for
+# NF4, 16384 k for MXFP4): the gate_up GEMM's K runs over two chunks
+LONGK_NF4 = inp.QWEN3_30B_NF4.scaled(name="long_k_nf4", seed_id=107, E=4, k=2, H=8256, I=64,
+                                     tokens=(6,))
+LONGK_MXFP4 = inp.GPT_OSS_20B_MXFP4.scaled(name="long_k_mxfp4", seed_id=108, E=4, k=2,
+                                           H=16416, I=32, tokens=(5,))
 _LAYERS = {}
 
 
@@ -447,7 +453,8 @@ def test_combine_against_oracle():
 # ------------------------------------------------------------ layer forward
 
 FWD_CASES = [(inp.TINY_NF4, 64), (QWEN_SMALL, 5), (QWEN_SMALL, 100), (GPTOSS_SMALL, 3),
-             (GPTOSS_SMALL, 200), (LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40)]
+             (GPTOSS_SMALL, 200), (LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (LONGK_NF4, 6),
+             (LONGK_MXFP4, 5)]
 
 
 @pytest.mark.parametrize("variant", [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED])
