@@ -132,11 +132,9 @@ struct SkinnyScales {
 };
 
 // Column tiles of 16 weight rows per wave of the skinny kernel: every
-// activation operand feeds kSkNc MFMAs.
-#ifndef SK_NC
-#define SK_NC 2
-#endif
-constexpr int kSkNc = SK_NC;
+// activation operand feeds kSkNc MFMAs (four measured slower than two: fewer,
+// fatter workgroups and more registers).
+constexpr int kSkNc = 2;
 static_assert(kSkNc == 2 || kSkNc == 4, "8 kSkNc gate/up pairs must divide I (a multiple of 32)");
 
 // Per-wave operands of one 128-k iteration of the skinny kernel: the nibbles
@@ -245,10 +243,9 @@ __device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const
 // the same on every path, so the compiler waits for exactly the batch it
 // needs. The prologue (the first NB - 1 batches) is a separate call so that
 // the first row chunk can issue it before the workgroup's set-up barrier.
-#ifndef SK_NB
-#define SK_NB 2
-#endif
-constexpr int kSkNb = SK_NB;
+// Batches in the register ring (three or four measured slower: spills at three
+// waves per SIMD, or fewer waves).
+constexpr int kSkNb = 2;
 
 template <int FMT, int NRT>
 __device__ __forceinline__ void skinny_prologue(SkinnyBatch<NRT> (&b)[kSkNb],
@@ -291,20 +288,19 @@ __device__ __forceinline__ void skinny_body(SkinnyBatch<NRT> (&b)[kSkNb], const 
 // workgroup's weight rows (direct loads into LDS), the NF4 level table and the first
 // batch of weights and activations are all issued before a single wait and
 // the workgroup barrier.
-#ifndef SK_WPE
-#define SK_WPE 3
-#endif
-#ifndef SK_MAXR
-#define SK_MAXR 1
-#endif
+// Three waves per SIMD (168 registers), and the expert's rows taken 16 at a
+// time (one 16-row MFMA tile: decode-sized experts rarely have more rows, and
+// a second accumulator tile would cost the third wave).
+constexpr int kSkWavesPerEu = 3;
+constexpr int kSkMaxRowTiles = 1;
 template <int FMT, bool GATEUP>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SK_WPE)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSkWavesPerEu)))
 void k_skinny(const GemmArgs a) {
   using F = Format<FMT>;
   using SS = SkinnyScales<FMT>;
   constexpr bool NF4 = FMT != MOE4_FMT_MXFP4;
   constexpr bool DQ = FMT == MOE4_FMT_NF4_DQ;
-  constexpr int MAXR = SK_MAXR;
+  constexpr int MAXR = kSkMaxRowTiles;
   constexpr int KB = F::kBlock;
   // NF4 byte -> two fp32 levels; the absmax code book of a double-quantised stack
   __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
@@ -843,14 +839,12 @@ hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
   const int nwg = nitems * a.ncg;
   if (nwg == 0) return hipSuccess;
   // split K over S waves so that ~6K waves stream the weights (about six per
-  // SIMD), each wave keeping at least two 128-k iterations
+  // SIMD), each wave keeping at least two 128-k iterations (targets of 3K and
+  // 4K waves measured no different)
   const int nit = (a.K + 127) / 128;
-#ifndef SK_TGT
-#define SK_TGT 6144
-#endif
-  int S = (SK_TGT + nwg - 1) / nwg;
+  int S = (6144 + nwg - 1) / nwg;
   S = max(1, min(S, min(8, nit / 2)));
-  constexpr int MAXR = SK_MAXR;
+  constexpr int MAXR = kSkMaxRowTiles;
   using SS = SkinnyScales<FMT>;
   // staged scales, then the partial sums of the S waves
   const size_t lds =
