@@ -149,6 +149,7 @@ struct SkinnyBatch {
 struct SkinnyLane {
   rsrc_t rq, ra;        // this expert's nibbles; this row chunk's activations
   int qoff[kSkNc];      // byte offset of the lane's 16-byte column in weight row c, k = 0
+  int aoff;             // byte offset of the lane's activation operand in its row, k = 0
   int sb[kSkNc];        // LDS byte address of the first staged scale of weight row c
   int a2bnd[kSkNc];     // double-quantised NF4: the first block of weight row c that
                         // lies in the row's second absmax group
@@ -170,21 +171,31 @@ struct SkinnyDq {
 // is loaded in the same order (the four lanes of a row read 64 contiguous
 // bytes), and every step lies inside one scale block (64 for NF4, 32 for
 // MXFP4).
-template <int FMT, int NRT>
+// FULL: the iteration lies inside K (kb + 128 <= K), so only `live` (an
+// iteration of this wave) decides, once per operand set; the four activation
+// loads then differ only in their immediate offsets. Otherwise every 32-k piece
+// is checked against K.
+template <int FMT, int NRT, bool FULL>
 __device__ __forceinline__ void skinny_load(SkinnyBatch<NRT>& bt, const SkinnyLane& sl, int K,
                                             int kb, bool live) {
   const int l = lane_id(), nl = l & 15, g = l >> 4;
-  const bool ink = live && kb + 32 * g < K;
+  const bool ink = live && (FULL || kb + 32 * g < K);
 #pragma unroll
   for (int c = 0; c < kSkNc; ++c)
     bt.wraw[c] = buf_load_b128(sl.rq, ink ? sl.qoff[c] + kb / 2 : kOob);
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    const int m = rt * 16 + nl;
+    if constexpr (FULL) {
+      const int base = live ? sl.aoff + (rt * 16 * K + kb) * 2 : kOob;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int k = kb + 32 * st + 8 * g;
-      bt.av[rt][st] = buf_load_b128(sl.ra, (live && k < K) ? (m * K + k) * 2 : kOob);
+      for (int st = 0; st < 4; ++st) bt.av[rt][st] = buf_load_b128(sl.ra, base + 64 * st);
+    } else {
+      const int m = rt * 16 + nl;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int k = kb + 32 * st + 8 * g;
+        bt.av[rt][st] = buf_load_b128(sl.ra, (live && k < K) ? (m * K + k) * 2 : kOob);
+      }
     }
   }
 }
@@ -236,8 +247,8 @@ __device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const
 }
 
 // K loop of one wave over the iterations [it0, it1) of a chunk starting at k0,
-// for NRT 16-row tiles, with NB batches in a register ring: while one batch is
-// dequantised and multiplied, the loads of the next NB - 1 are in flight.
+// for NRT 16-row tiles, with two batches in a register ring: while one batch
+// is dequantised and multiplied, the loads of the next are in flight.
 // Loads are never skipped: an iteration past it1 reads out of bounds (zero
 // activations, no memory traffic), which keeps the count of loads in flight
 // the same on every path, so the compiler waits for exactly the batch it
@@ -247,33 +258,38 @@ __device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const
 // waves per SIMD, or fewer waves).
 constexpr int kSkNb = 2;
 
+// Iterations [it0, itf) of the wave lie inside K; iteration itf < it1, if the
+// wave has it, is the chunk's partial last one.
 template <int FMT, int NRT>
 __device__ __forceinline__ void skinny_prologue(SkinnyBatch<NRT> (&b)[kSkNb],
                                                 const SkinnyLane& sl, int K, int k0, int it0,
-                                                int it1) {
-#pragma unroll
-  for (int j = 0; j < kSkNb - 1; ++j)
-    skinny_load<FMT>(b[j], sl, K, k0 + 128 * (it0 + j), it0 + j < it1);
+                                                int itf, int it1) {
+  static_assert(kSkNb == 2, "one batch of prologue");
+  if (it0 < itf) skinny_load<FMT, NRT, true>(b[0], sl, K, k0 + 128 * it0, true);
+  else skinny_load<FMT, NRT, false>(b[0], sl, K, k0 + 128 * it0, it0 < it1);
 }
 
 template <int FMT, int NRT>
 __device__ __forceinline__ void skinny_body(SkinnyBatch<NRT> (&b)[kSkNb], const SkinnyLane& sl,
-                                            int K, int k0, int it0, int it1, int nblk,
+                                            int K, int k0, int it0, int itf, int it1, int nblk,
                                             const float2* lutf, const uint8_t* stage,
                                             const SkinnyDq& dq, f32x4 (&acc)[2][kSkNc]) {
-  constexpr int NB = kSkNb;
   constexpr int KB = Format<FMT>::kBlock;
   const int gblk0 = k0 / KB;
-  for (int it = it0; it < it1; it += NB) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int itn = it + j + NB - 1;
-      skinny_load<FMT>(b[(j + NB - 1) % NB], sl, K, k0 + 128 * itn, itn < it1);
-      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the arithmetic
-      if (NB == 2 || it + j < it1)
-        skinny_compute<FMT>(b[j], lutf, stage, sl, dq, it + j, nblk, gblk0, acc);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int it = it0; it < itf; it += 2) {
+    skinny_load<FMT, NRT, true>(b[1], sl, K, k0 + 128 * (it + 1), it + 1 < itf);
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the arithmetic
+    skinny_compute<FMT>(b[0], lutf, stage, sl, dq, it, nblk, gblk0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    skinny_load<FMT, NRT, true>(b[0], sl, K, k0 + 128 * (it + 2), it + 2 < itf);
+    __builtin_amdgcn_sched_barrier(0);
+    skinny_compute<FMT>(b[1], lutf, stage, sl, dq, it + 1, nblk, gblk0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (itf < it1) {
+    // the partial last iteration (the prologue loaded it if it is the wave's only one)
+    if (it0 < itf) skinny_load<FMT, NRT, false>(b[0], sl, K, k0 + 128 * itf, true);
+    skinny_compute<FMT>(b[0], lutf, stage, sl, dq, itf, nblk, gblk0, acc);
   }
 }
 
@@ -288,7 +304,8 @@ __device__ __forceinline__ void skinny_body(SkinnyBatch<NRT> (&b)[kSkNb], const 
 // workgroup's weight rows (direct loads into LDS), the NF4 level table and the first
 // batch of weights and activations are all issued before a single wait and
 // the workgroup barrier.
-// Three waves per SIMD (168 registers), and the expert's rows taken 16 at a
+//
+// Three waves per SIMD (four measured the same), and the expert's rows taken 16 at a
 // time (one 16-row MFMA tile: decode-sized experts rarely have more rows, and
 // a second accumulator tile would cost the third wave).
 constexpr int kSkWavesPerEu = 3;
@@ -400,6 +417,7 @@ void k_skinny(const GemmArgs a) {
 #pragma unroll
       for (int c = 0; c < kSkNc; ++c) acc[rt][c] = zero4;
     sl.ra = make_rsrc(a.A + (int64_t)(rbeg + rc) * K, (uint32_t)max(nrows, 0) * K * 2);
+    sl.aoff = (nl * K + 8 * g) * 2;
     SkinnyBatch<NRT> b[kSkNb];
     // chunk ch of K: its scales in the stage, then the wave's iterations
     auto chunk = [&](int ch, bool setup) {
@@ -410,7 +428,8 @@ void k_skinny(const GemmArgs a) {
         sl.sb[c] = (16 * c + nl) * pdw * 4 + ((srow[c] * rowbytes + c0) & 3);
       const int nit = (kc + 127) / 128;
       const int it0 = (int)((int64_t)w * nit / S), it1 = (int)((int64_t)(w + 1) * nit / S);
-      skinny_prologue<FMT>(b, sl, K, k0, it0, it1);
+      const int itf = min(it1, kc / 128);   // end of the wave's whole iterations
+      skinny_prologue<FMT>(b, sl, K, k0, it0, itf, it1);
       if (setup) {
         // the scales and level pairs travel together with the first batch
         __builtin_amdgcn_sched_barrier(0);
@@ -419,7 +438,7 @@ void k_skinny(const GemmArgs a) {
         wait_vmcnt<0>();
         lds_barrier();
       }
-      skinny_body<FMT>(b, sl, K, k0, it0, it1, kc / KB, lutf, stage, dq, acc);
+      skinny_body<FMT>(b, sl, K, k0, it0, itf, it1, kc / KB, lutf, stage, dq, acc);
     };
     auto restage = [&](int ch) {
       __syncthreads();   // every wave is done with the staged scales
