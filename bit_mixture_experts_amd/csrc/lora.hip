@@ -12,57 +12,81 @@ namespace moe4 {
 namespace {
 
 // out[row][q] = sum_k M[row][k] P[e(row)][q][k] in fp32, M bf16 [rows, K], P bf16
-// [E, r, K]. One wave per 32-row tile of one expert: MFMA operand A = 32 rows
-// of M, operand B = 32 rank rows of P (zero past r), both read straight from
-// memory as 16-byte pieces (rows past the tile and ranks past r read zeros).
+// [E, r, K]. One workgroup per 32-row tile of one expert; its four waves split
+// K into four ranges of 16-k MFMA steps and their 32x32 partial products meet
+// in LDS. MFMA operand A = 32 rows of M, operand B = 32 rank rows of P (zero
+// past r), both read straight from memory as 16-byte pieces (rows past the
+// tile, ranks past r and steps past the wave's range read zeros), eight steps
+// per batch with the next batch in flight.
 __global__ __launch_bounds__(256) void k_rank_proj(const uint16_t* __restrict__ M,
                                                    const int32_t* __restrict__ offsets, int E,
                                                    int rows, int K, const uint16_t* __restrict__ P,
                                                    int r, float* __restrict__ out) {
+  __shared__ float red[4][16][kWave];
   const int w = wave_id(), l = lane_id(), n32 = l & 31, h = l >> 5;
   int e, u, unused;
-  locate_tile_eq<32>(offsets, E, 1, blockIdx.x * 4 + w, e, u, unused);
+  locate_tile_eq<32>(offsets, E, 1, blockIdx.x, e, u, unused);
   e = __builtin_amdgcn_readfirstlane(e);
   u = __builtin_amdgcn_readfirstlane(u);
-  if (e < 0) return;
+  if (e < 0) return;   // the whole workgroup: e is uniform
   const int ebeg = min(offsets[e], rows);
   const int row0 = ebeg + 32 * u;
   const int nrows = min(32, min(offsets[e + 1], rows) - row0);
   const rsrc_t rm = make_rsrc(M + (int64_t)row0 * K, (uint32_t)nrows * K * 2);
   const int moff = (n32 * K + 8 * h) * 2;
+  const int nsteps = (K + 15) / 16;
+  const int s0 = w * nsteps / 4, s1 = (w + 1) * nsteps / 4;
   for (int q0 = 0; q0 < r; q0 += 32) {
     const rsrc_t rp = make_rsrc(P + ((int64_t)e * r + q0) * K, (uint32_t)(r - q0) * K * 2);
     f32x16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    int k0 = 0;
-    for (; k0 + 128 <= K; k0 += 128) {
-      u32x4 av[8], bv[8];
+    u32x4 av[2][8], bv[2][8];
+    // steps st .. st + 7 into batch slot b (never skipped: out-of-range steps
+    // read zeros, so the count of loads in flight is the same on every path)
+    auto load = [&](int b, int st) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        av[j] = buf_load_b128(rm, moff + 2 * (k0 + 16 * j));
-        bv[j] = buf_load_b128(rp, moff + 2 * (k0 + 16 * j));
+        const int step = st + j;
+        const int off = (step < s1 && 16 * step + 8 * h < K) ? moff + 32 * step : kOob;
+        av[b][j] = buf_load_b128(rm, off);
+        bv[b][j] = buf_load_b128(rp, off);
       }
+    };
+    auto mul = [&](int b) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]),
-                                                      __builtin_bit_cast(bf16x8, bv[j]), acc, 0,
-                                                      0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[b][j]),
+                                                      __builtin_bit_cast(bf16x8, bv[b][j]), acc,
+                                                      0, 0, 0);
+    };
+    load(0, s0);
+    for (int st = s0; st < s1; st += 16) {
+      load(1, st + 8);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(0, st + 16);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    for (; k0 < K; k0 += 16) {
-      const u32x4 av = buf_load_b128(rm, k0 + 8 * h < K ? moff + 2 * k0 : kOob);
-      const u32x4 bv = buf_load_b128(rp, k0 + 8 * h < K ? moff + 2 * k0 : kOob);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                    __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
-    }
-    // lane holds rank column q0 + n32 of rows 8 (i / 4) + 4 h + i % 4
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[w][i][l] = acc[i];
+    __syncthreads();
+    // lane holds rank column q0 + n32 of rows 8 (i / 4) + 4 h + i % 4; wave
+    // w sums and stores entries i = 4 w .. 4 w + 3
     if (q0 + n32 < r) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 4 * w + ii;
         const int rr = 8 * (i >> 2) + 4 * h + (i & 3);
-        if (rr < nrows) out[(int64_t)(row0 + rr) * r + q0 + n32] = acc[i];
+        if (rr < nrows)
+          out[(int64_t)(row0 + rr) * r + q0 + n32] =
+              red[0][i][l] + red[1][i][l] + red[2][i][l] + red[3][i][l];
       }
     }
+    __syncthreads();   // red is reused by the next rank tile
   }
 }
 
@@ -82,7 +106,9 @@ __global__ __launch_bounds__(256) void k_transpose_rank(const uint16_t* __restri
 //   lscale * sum over the rows of e of bf16(vec[row][q]) * mat[row][col]
 // vec fp32 [rows, r], mat bf16 [rows, ncols]. Block = (256 columns, expert);
 // wave w takes rows w, w + 4, ..., lane l columns 4 l .. 4 l + 3, up to kQ
-// ranks per pass; the four waves' partial sums meet in LDS.
+// ranks per pass; the four waves' partial sums meet in LDS. A rank entry past
+// r (read from the next row, or as zero past the last) is multiplied by zero:
+// the mask makes it 0 before the product, so it never reaches a sum.
 constexpr int kQ = 8;
 template <bool TRANSPOSED>
 __global__ __launch_bounds__(256) void k_rank_reduce(const uint16_t* __restrict__ mat, int ncols,
@@ -103,27 +129,37 @@ __global__ __launch_bounds__(256) void k_rank_reduce(const uint16_t* __restrict_
     for (int q = 0; q < kQ; ++q)
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[q][c] = 0.0f;
-    for (int row = r0 + w; row < r1; row += 16) {
-      uint2 mv[4];
-      float vv[4][kQ];
+    // 32-row windows of the expert through buffer resources: rows past r1
+    // read zeros, so every load is issued (eight rows per wave and window,
+    // the four waves interleaved by row)
+    for (int rb = r0; rb < r1; rb += 32) {
+      const int nw = min(32, r1 - rb);
+      const rsrc_t rmat = make_rsrc(mat + (int64_t)rb * ncols, (uint32_t)nw * ncols * 2);
+      const rsrc_t rvec = make_rsrc(vec + (int64_t)rb * r, (uint32_t)nw * r * 4);
+      u32x2 mv[8];
+      f32x4 vlo[8], vhi[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rw = row + 4 * j;
-        const bool ok = on && rw < r1;
-        mv[j] = ok ? *reinterpret_cast<const uint2*>(mat + (int64_t)rw * ncols + col) : make_uint2(0u, 0u);
-#pragma unroll
-        for (int q = 0; q < kQ; ++q)
-          vv[j][q] = (rw < r1 && q0 + q < r) ? round_bf16(vec[(int64_t)rw * r + q0 + q]) : 0.0f;
+      for (int j = 0; j < 8; ++j) {
+        const int rw = w + 4 * j;
+        mv[j] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rmat, on ? (rw * ncols + col) * 2 : kOob,
+                                                        0, 0));
+        // ranks q0 .. q0 + 7 of the row (entries past r are masked below)
+        vlo[j] = __builtin_bit_cast(f32x4, buf_load_b128(rvec, (rw * r + q0) * 4));
+        vhi[j] = __builtin_bit_cast(f32x4, buf_load_b128(rvec, (rw * r + q0 + 4) * 4));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float m0 = bf16lo(mv[j].x), m1 = bf16hi(mv[j].x), m2 = bf16lo(mv[j].y), m3 = bf16hi(mv[j].y);
+      for (int j = 0; j < 8; ++j) {
+        const float m0 = bf16lo(mv[j][0]), m1 = bf16hi(mv[j][0]), m2 = bf16lo(mv[j][1]),
+                    m3 = bf16hi(mv[j][1]);
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
-          acc[q][0] += vv[j][q] * m0;
-          acc[q][1] += vv[j][q] * m1;
-          acc[q][2] += vv[j][q] * m2;
-          acc[q][3] += vv[j][q] * m3;
+          const float raw = q < 4 ? vlo[j][q] : vhi[j][q - 4];
+          const float v = q0 + q < r ? round_bf16(raw) : 0.0f;
+          acc[q][0] += v * m0;
+          acc[q][1] += v * m1;
+          acc[q][2] += v * m2;
+          acc[q][3] += v * m3;
         }
       }
     }
@@ -154,10 +190,10 @@ __global__ __launch_bounds__(256) void k_rank_reduce(const uint16_t* __restrict_
 hipError_t launch_rank_proj(const uint16_t* M, const int32_t* offsets, int E, int rows, int K,
                             const uint16_t* P, int r, float* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  // tiles of 32 rows: at most rows / 32 + (one per expert), plus 8 spare ids
-  const int ntiles = rows / 32 + min(E, rows) + 8;
-  hipLaunchKernelGGL(k_rank_proj, dim3((ntiles + 3) / 4), dim3(256), 0, s, M, offsets, E, rows,
-                     K, P, r, out);
+  // tiles of 32 rows: at most rows / 32 + (one per expert); one workgroup each
+  const int ntiles = rows / 32 + min(E, rows);
+  hipLaunchKernelGGL(k_rank_proj, dim3(ntiles), dim3(256), 0, s, M, offsets, E, rows, K, P, r,
+                     out);
   return hipGetLastError();
 }
 
