@@ -34,6 +34,15 @@ LONGK_NF4 = inp.QWEN3_30B_NF4.scaled(name="long_k_nf4", seed_id=107, E=4, k=2, H
                                      tokens=(6,))
 LONGK_MXFP4 = inp.GPT_OSS_20B_MXFP4.scaled(name="long_k_mxfp4", seed_id=108, E=4, k=2,
                                            H=16416, I=32, tokens=(5,))
+# degenerate shapes of the method: one expert at top-1 (a dense 4-bit MLP),
+# every expert chosen (k = E), and the smallest MXFP4 rows (H = I = 32: one
+# partial iteration / k-tile everywhere)
+DENSE_NF4 = inp.TINY_NF4.scaled(name="dense_nf4_E1_k1", seed_id=109, E=1, k=1, H=256, I=128,
+                                tokens=(40,))
+ALLEXP_NF4 = inp.TINY_NF4.scaled(name="all_experts_nf4_E4_k4", seed_id=110, E=4, k=4, H=128,
+                                 I=64, tokens=(33,))
+MIN_MXFP4 = inp.GPT_OSS_20B_MXFP4.scaled(name="min_mxfp4_H32_I32", seed_id=111, E=4, k=2, H=32,
+                                         I=32, tokens=(9,))
 _LAYERS = {}
 
 
@@ -454,7 +463,7 @@ def test_combine_against_oracle():
 
 FWD_CASES = [(inp.TINY_NF4, 64), (QWEN_SMALL, 5), (QWEN_SMALL, 100), (GPTOSS_SMALL, 3),
              (GPTOSS_SMALL, 200), (LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (LONGK_NF4, 6),
-             (LONGK_MXFP4, 5)]
+             (LONGK_MXFP4, 5), (DENSE_NF4, 40), (ALLEXP_NF4, 33), (MIN_MXFP4, 9)]
 
 
 @pytest.mark.parametrize("variant", [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED])
