@@ -190,10 +190,12 @@ __global__ __launch_bounds__(256) void k_rank_reduce(const uint16_t* __restrict_
 hipError_t launch_rank_proj(const uint16_t* M, const int32_t* offsets, int E, int rows, int K,
                             const uint16_t* P, int r, float* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  // tiles of 32 rows: at most rows / 32 + (one per expert); one workgroup each
+  // tiles of 32 rows: at most rows / 32 + (one per expert), one workgroup
+  // each; the XCD-contiguous deal of locate_tile_eq needs 8 ids beyond the
+  // tile count (an XCD's share may start past the last id otherwise)
   const int ntiles = rows / 32 + min(E, rows);
-  hipLaunchKernelGGL(k_rank_proj, dim3(ntiles), dim3(256), 0, s, M, offsets, E, rows, K, P, r,
-                     out);
+  hipLaunchKernelGGL(k_rank_proj, dim3(ntiles + 8), dim3(256), 0, s, M, offsets, E, rows, K, P,
+                     r, out);
   return hipGetLastError();
 }
 

@@ -567,7 +567,11 @@ def test_empty_inputs():
 
 # ----------------------------------------------------------------- backward
 
-BWD_CASES = [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40)]
+# one expert at top-1 with an adapter: the backward of a dense 4-bit QLoRA MLP
+DENSE_LORA = inp.QWEN3_30B_NF4_LORA.scaled(name="dense_lora_E1_k1", seed_id=112, E=1, k=1,
+                                           H=128, I=64, tokens=(50,), lora_r=4,
+                                           lora_alpha=8.0)
+BWD_CASES = [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (DENSE_LORA, 50)]
 
 
 def test_layer_backward_skewed():
