@@ -222,7 +222,8 @@ class DQLayer:
                             gu_soff=goff, dn_soff=doff, dq_book=to_dev(self.book))
 
 
-DQ_CASES = [(QWEN_SMALL, 5, "dynamic"), (QWEN_SMALL, 100, "linear"), (LORA_SMALL, 150, "dynamic")]
+DQ_CASES = [(QWEN_SMALL, 5, "dynamic"), (QWEN_SMALL, 100, "linear"), (LORA_SMALL, 150, "dynamic"),
+            (DENSE_NF4, 40, "dynamic")]
 
 
 @pytest.mark.parametrize("variant", [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED])
@@ -463,7 +464,8 @@ def test_combine_against_oracle():
 
 FWD_CASES = [(inp.TINY_NF4, 64), (QWEN_SMALL, 5), (QWEN_SMALL, 100), (GPTOSS_SMALL, 3),
              (GPTOSS_SMALL, 200), (LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (LONGK_NF4, 6),
-             (LONGK_MXFP4, 5), (DENSE_NF4, 40), (ALLEXP_NF4, 33), (MIN_MXFP4, 9)]
+             (LONGK_MXFP4, 5), (DENSE_NF4, 40), (ALLEXP_NF4, 33), (MIN_MXFP4, 9), (QWEN_SMALL, 1),
+             (GPTOSS_SMALL, 1)]
 
 
 @pytest.mark.parametrize("variant", [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED])
@@ -571,7 +573,16 @@ def test_empty_inputs():
 DENSE_LORA = inp.QWEN3_30B_NF4_LORA.scaled(name="dense_lora_E1_k1", seed_id=112, E=1, k=1,
                                            H=128, I=64, tokens=(50,), lora_r=4,
                                            lora_alpha=8.0)
-BWD_CASES = [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (DENSE_LORA, 50)]
+# and its MXFP4 counterpart (biases, interleaved rows, clamped GLU), and every
+# expert chosen with an adapter (k = E = 2)
+DENSE_MXFP4_LORA = inp.GPT_OSS_20B_MXFP4.scaled(name="dense_mxfp4_lora_E1_k1", seed_id=113, E=1,
+                                                k=1, H=96, I=64, tokens=(30,), lora_r=4,
+                                                lora_alpha=8.0)
+ALLEXP_LORA = inp.QWEN3_30B_NF4_LORA.scaled(name="all_experts_lora_E2_k2", seed_id=114, E=2,
+                                            k=2, H=128, I=64, tokens=(45,), lora_r=8,
+                                            lora_alpha=16.0)
+BWD_CASES = [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (DENSE_LORA, 50), (DENSE_MXFP4_LORA, 30),
+             (ALLEXP_LORA, 45)]
 
 
 def test_layer_backward_skewed():
