@@ -513,12 +513,12 @@ def test_auto_variant_choice():
         assert res["variant"] == want
 
 
-@pytest.mark.parametrize("T", [300, 700])
+@pytest.mark.parametrize("T", [300, 320, 321, 700])
 def test_forward_single_expert_overflow_rows(T):
-    """All tokens on two experts: the skinny kernel loops over row chunks; at
-    T=700 the tiled kernel cuts each expert into three equal tiles (of up to
-    320 rows), which the largest-first order deals with the other experts'
-    empty ones."""
+    """All tokens on two experts: the skinny kernel loops over row chunks; the
+    tiled kernel takes 320 rows in one tile and cuts 321 rows into two (161 +
+    160), and at T=700 each expert into three equal tiles (of up to 320 rows),
+    which the largest-first order deals with the other experts' empty ones."""
     spec = inp.TINY_NF4
     L = layer_of(spec)
     x, _ = inp.host_tokens(spec, T)
