@@ -585,12 +585,12 @@ BWD_CASES = [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (DENSE_LORA, 50), (DENSE
              (ALLEXP_LORA, 45)]
 
 
-def test_layer_backward_skewed():
-    """All tokens on two experts (300 rows each): the dgrad kernels cut each
-    expert into two 160-row tiles, and the adapter reductions run over long
-    row ranges."""
+@pytest.mark.parametrize("T", [256, 257, 300])
+def test_layer_backward_skewed(T):
+    """All tokens on two experts (T rows each): the dgrad kernels take 256 rows
+    in one tile and cut 257 or 300 rows into two, and the adapter reductions
+    run over long row ranges."""
     spec = LORA_SMALL
-    T = 300
     say(f"backward skewed {spec.name} T={T}")
     L = layer_of(spec)
     ex = L.device()
