@@ -43,6 +43,12 @@ ALLEXP_NF4 = inp.TINY_NF4.scaled(name="all_experts_nf4_E4_k4", seed_id=110, E=4,
                                  I=64, tokens=(33,))
 MIN_MXFP4 = inp.GPT_OSS_20B_MXFP4.scaled(name="min_mxfp4_H32_I32", seed_id=111, E=4, k=2, H=32,
                                          I=32, tokens=(9,))
+# more experts than one 64-lane pass over the offsets covers twice (E > 128),
+# up to the largest E the interface takes
+WIDE_NF4 = inp.TINY_NF4.scaled(name="wide_nf4_E160_k2", seed_id=115, E=160, k=2, H=128, I=64,
+                               tokens=(40,))
+WIDEST_MXFP4 = inp.GPT_OSS_20B_MXFP4.scaled(name="widest_mxfp4_E1024_k4", seed_id=116, E=1024,
+                                            k=4, H=64, I=64, tokens=(20,))
 _LAYERS = {}
 
 
@@ -465,7 +471,7 @@ def test_combine_against_oracle():
 FWD_CASES = [(inp.TINY_NF4, 64), (QWEN_SMALL, 5), (QWEN_SMALL, 100), (GPTOSS_SMALL, 3),
              (GPTOSS_SMALL, 200), (LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (LONGK_NF4, 6),
              (LONGK_MXFP4, 5), (DENSE_NF4, 40), (ALLEXP_NF4, 33), (MIN_MXFP4, 9), (QWEN_SMALL, 1),
-             (GPTOSS_SMALL, 1)]
+             (GPTOSS_SMALL, 1), (WIDE_NF4, 40), (WIDEST_MXFP4, 20)]
 
 
 @pytest.mark.parametrize("variant", [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED])
