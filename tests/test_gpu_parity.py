@@ -587,8 +587,10 @@ DENSE_MXFP4_LORA = inp.GPT_OSS_20B_MXFP4.scaled(name="dense_mxfp4_lora_E1_k1", s
 ALLEXP_LORA = inp.QWEN3_30B_NF4_LORA.scaled(name="all_experts_lora_E2_k2", seed_id=114, E=2,
                                             k=2, H=128, I=64, tokens=(45,), lora_r=8,
                                             lora_alpha=16.0)
+WIDE_LORA = inp.QWEN3_30B_NF4_LORA.scaled(name="wide_lora_E160_k2", seed_id=117, E=160, k=2,
+                                          H=128, I=64, tokens=(40,), lora_r=4, lora_alpha=8.0)
 BWD_CASES = [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (DENSE_LORA, 50), (DENSE_MXFP4_LORA, 30),
-             (ALLEXP_LORA, 45)]
+             (ALLEXP_LORA, 45), (WIDE_LORA, 40)]
 
 
 @pytest.mark.parametrize("T", [256, 257, 300])
