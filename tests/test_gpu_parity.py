@@ -49,6 +49,9 @@ WIDE_NF4 = inp.TINY_NF4.scaled(name="wide_nf4_E160_k2", seed_id=115, E=160, k=2,
                                tokens=(40,))
 WIDEST_MXFP4 = inp.GPT_OSS_20B_MXFP4.scaled(name="widest_mxfp4_E1024_k4", seed_id=116, E=1024,
                                             k=4, H=64, I=64, tokens=(20,))
+# top-16 routing: the combine's rows past the eighth and permute's k > 8
+TOPK16_NF4 = inp.TINY_NF4.scaled(name="top16_nf4_E64_k16", seed_id=118, E=64, k=16, H=128,
+                                 I=64, tokens=(30,))
 _LAYERS = {}
 
 
@@ -419,7 +422,8 @@ def _permute(idx, E, x=None, scale=None):
 
 
 @pytest.mark.parametrize("T,E,k", [(64, 8, 2), (1, 128, 8), (128, 128, 8), (200, 32, 4),
-                                   (3000, 128, 8), (300, 1024, 7), (1500, 4, 4)])
+                                   (3000, 128, 8), (300, 1024, 7), (1500, 4, 4), (100, 64, 16),
+                                   (700, 32, 16), (40, 1024, 32), (50, 64, 16)])
 def test_permute_bit_exact(T, E, k):
     say(f"permute T={T} E={E} k={k}")
     rng = np.random.default_rng(T + E + k)
@@ -445,10 +449,16 @@ def test_permute_skewed_one_expert():
     assert np.array_equal(off.cpu().numpy(), ro) and np.array_equal(sor.cpu().numpy(), rs)
 
 
-def test_combine_against_oracle():
-    say("combine")
-    rng = np.random.default_rng(21)
-    T, k, H = 70, 4, 264
+# k = 8 is the last count whose rows are all loaded together; k > 8 takes the
+# one-row-at-a-time tail; H = 8 leaves most lanes of the wave idle
+COMBINE_CASES = [(70, 4, 264), (33, 1, 64), (50, 8, 136), (19, 9, 72), (23, 16, 2056),
+                 (5, 32, 8)]
+
+
+@pytest.mark.parametrize("T,k,H", COMBINE_CASES)
+def test_combine_against_oracle(T, k, H):
+    say(f"combine T={T} k={k} H={H}")
+    rng = np.random.default_rng(21 + T * k + H)
     y = rng.standard_normal((T * k, H)).astype(np.float32)
     ros = rng.permutation(T * k).astype(np.int32)
     w = rng.random((T, k)).astype(np.float32)
@@ -471,7 +481,7 @@ def test_combine_against_oracle():
 FWD_CASES = [(inp.TINY_NF4, 64), (QWEN_SMALL, 5), (QWEN_SMALL, 100), (GPTOSS_SMALL, 3),
              (GPTOSS_SMALL, 200), (LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (LONGK_NF4, 6),
              (LONGK_MXFP4, 5), (DENSE_NF4, 40), (ALLEXP_NF4, 33), (MIN_MXFP4, 9), (QWEN_SMALL, 1),
-             (GPTOSS_SMALL, 1), (WIDE_NF4, 40), (WIDEST_MXFP4, 20)]
+             (GPTOSS_SMALL, 1), (WIDE_NF4, 40), (WIDEST_MXFP4, 20), (TOPK16_NF4, 30)]
 
 
 @pytest.mark.parametrize("variant", [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED])
