@@ -36,7 +36,8 @@ brute force on tiny inputs, float64 finite differences, torch CPU autograd, the
 published NF4 construction). No function is "parity unpinned".
 """
 
-from .numerics import bf16_bits_from_f32, bf16_bits_to_f64, bf16_bits_to_f32, bf16_round_f64
+from .numerics import (bf16_bits_from_f32, bf16_bits_to_f64, bf16_bits_to_f32, bf16_round_f64,
+                       bf16_other_neighbour_f64)
 from .formats import (NF4_LEVELS, nf4_midpoints, quantize_nf4, dequantize_nf4,
                       dequantize_nf4_bf16, E2M1_MAGNITUDES, mxfp4_values, decode_mxfp4_bf16,
                       convert_mxfp4_to_nf4, dq_midpoints, compress_absmax, expand_absmax)
@@ -48,6 +49,7 @@ from .layer import (ExpertWeights, gate_up, activation, down, combine,
 
 __all__ = [
     "bf16_bits_from_f32", "bf16_bits_to_f64", "bf16_bits_to_f32", "bf16_round_f64",
+    "bf16_other_neighbour_f64",
     "NF4_LEVELS", "nf4_midpoints", "quantize_nf4", "dequantize_nf4", "dequantize_nf4_bf16",
     "E2M1_MAGNITUDES", "mxfp4_values", "decode_mxfp4_bf16", "convert_mxfp4_to_nf4",
     "dq_midpoints", "compress_absmax", "expand_absmax",

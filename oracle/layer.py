@@ -28,6 +28,17 @@ Readings (the pages are silent):
 * Backward covers the expert path only (router logits are given inputs):
   dX, dA, dB; the frozen base and biases get no gradient. Clamp derivatives
   pass where the clamp is inactive, boundaries included.
+* The clamped GLU is continuous but its derivative jumps at g = limit and at
+  u = +-limit. A value computed in fp32 that lies within its rounding error of
+  such a point may fall on either side of it, and either side's derivative is
+  then a valid result; ``clamp_flip`` names entries whose side is taken
+  opposite to the side their oracle value falls on (for comparisons against
+  an fp32 computation; the default takes every side as the value says).
+* Likewise, the bf16 rounding of dGU (a GEMM operand) is decided on a value
+  that an fp32 computation carries with an error of its own: where the exact
+  value lies close to a rounding midpoint, either neighbouring bf16 value is
+  a valid operand. ``round_flip`` names dGU entries that take the other
+  neighbour (the default rounds every entry to the nearest).
 * Precision: bf16 model tensors with fp32 accumulation (solutions index,
   grouped-nf4-gemm entries; experts4bit-qlora page, the adapter runs in the
   model dtype, bf16). The oracle rounds to bf16 exactly where a value becomes
@@ -45,7 +56,8 @@ from typing import Callable, Optional
 import numpy as np
 
 from .formats import dequantize_nf4, dequantize_nf4_bf16, mxfp4_values
-from .numerics import bf16_bits_from_f32, bf16_bits_to_f64, bf16_round_f64
+from .numerics import (bf16_bits_from_f32, bf16_bits_to_f64, bf16_other_neighbour_f64,
+                       bf16_round_f64)
 from .routing import permute
 
 HALVES = "halves"
@@ -192,8 +204,13 @@ def activation(gu, W):
     raise ValueError("unknown activation")
 
 
-def activation_backward(gu, dh, W):
-    """d(loss)/d(gu) given d(loss)/d(h), in the stack's gate/up layout."""
+def activation_backward(gu, dh, W, flip=None):
+    """d(loss)/d(gu) given d(loss)/d(h), in the stack's gate/up layout.
+
+    flip (clamped GLU only): bool array shaped like gu; where True, the clamp
+    of that entry is taken as the other side of its boundary decides (active
+    for a value inside [-limit, limit] (up) or <= limit (gate), inactive
+    otherwise)."""
     g, u = split_gate_up(gu, W.layout, W.I)
     if W.act == SWIGLU:
         s = _sigmoid(g)
@@ -203,8 +220,13 @@ def activation_backward(gu, dh, W):
         gc = np.minimum(g, W.limit)
         uc = np.clip(u, -W.limit, W.limit)
         sa = _sigmoid(W.alpha * gc)
-        du = dh * gc * sa * ((u >= -W.limit) & (u <= W.limit))
-        dg = dh * (uc + 1.0) * (sa + W.alpha * gc * sa * (1.0 - sa)) * (g <= W.limit)
+        pass_u = (u >= -W.limit) & (u <= W.limit)
+        pass_g = g <= W.limit
+        if flip is not None:
+            fg, fu = split_gate_up(np.asarray(flip, dtype=bool), W.layout, W.I)
+            pass_g, pass_u = pass_g ^ fg, pass_u ^ fu
+        du = dh * gc * sa * pass_u
+        dg = dh * (uc + 1.0) * (sa + W.alpha * gc * sa * (1.0 - sa)) * pass_g
     else:
         raise ValueError("unknown activation")
     return join_gate_up(dg, du, W.layout)
@@ -272,13 +294,19 @@ def token_forward(x_row_bits, experts, weights, W, exact=False):
     return out
 
 
-def layer_backward(x_bits, topk_idx, topk_w, dout_bits, W, exact=False):
+def layer_backward(x_bits, topk_idx, topk_w, dout_bits, W, exact=False, clamp_flip=None,
+                   round_flip=None):
     """Gradient of sum_t <dOut[t], out[t]> with respect to x, A and B.
 
     Returns dict with ``dx`` [T,H], ``dA`` [E,r,H], ``dB`` [E,2I,r] (zero for
     experts that receive no rows), plus the per-row ``dgu`` and ``dx_perm``.
     Unless exact, the routing weights enter as fp32 (the interface's dtype) and
-    the scaled upstream gradient is bf16(fp32(w * dOut)).
+    the scaled upstream gradient is bf16(fp32(w * dOut)). clamp_flip: None, or
+    a bool array [T*k, 2I] in permuted-row order and the stack's gate/up
+    layout, passed row by row to ``activation_backward``. round_flip: None, or
+    a bool array of the same shape; where True, that dGU entry is rounded to
+    the other bf16 neighbour of its exact value (``bf16_other_neighbour_f64``).
+    Also returned: ``dgu_exact`` (dGU before its rounding) and ``dh``.
     """
     x = _as_f64(x_bits)
     dout = _as_f64(dout_bits)
@@ -288,6 +316,8 @@ def layer_backward(x_bits, topk_idx, topk_w, dout_bits, W, exact=False):
     rows = T * k
     dx_perm = np.zeros((rows, W.H))
     dgu_all = np.zeros((rows, 2 * W.I))
+    dgu_exact_all = np.zeros((rows, 2 * W.I))
+    dh_all = np.zeros((rows, W.I))
     lora = W.lora_A is not None
     r = W.lora_A(0).shape[0] if lora else 0
     dA = np.zeros((W.E, r, W.H))
@@ -307,7 +337,11 @@ def layer_backward(x_bits, topk_idx, topk_w, dout_bits, W, exact=False):
         gu, xa = gate_up(X, W, e, exact)
         Wgu, Wd = W.expert(e)
         dH = dY @ Wd
-        dGU = _op(activation_backward(gu, dH, W), exact)
+        flip = None if clamp_flip is None else np.asarray(clamp_flip)[a:b]
+        dGU_exact = activation_backward(gu, dH, W, flip)
+        dGU = _op(dGU_exact, exact)
+        if round_flip is not None and not exact:
+            dGU = np.where(np.asarray(round_flip)[a:b], bf16_other_neighbour_f64(dGU_exact), dGU)
         dX = dGU @ Wgu
         if lora:
             A, B = W.lora_A(e), W.lora_B(e)
@@ -317,6 +351,9 @@ def layer_backward(x_bits, topk_idx, topk_w, dout_bits, W, exact=False):
             dA[e] = W.lora_scale * (t.T @ X)
         dx_perm[a:b] = dX
         dgu_all[a:b] = dGU
+        dgu_exact_all[a:b] = dGU_exact
+        dh_all[a:b] = dH
     dx = combine(dx_perm, row_of_slot, None, T, k)
     return {"dx": dx, "dA": dA, "dB": dB, "dx_perm": dx_perm, "dgu": dgu_all,
+            "dgu_exact": dgu_exact_all, "dh": dh_all,
             "offsets": offsets, "slot_of_row": slot_of_row, "row_of_slot": row_of_slot}

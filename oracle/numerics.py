@@ -58,3 +58,24 @@ def bf16_round_f64(x):
     r[big] = np.copysign(np.inf, r[big])
     out[fin] = r
     return out
+
+
+def bf16_other_neighbour_f64(x):
+    """The bf16 value next to bf16_round_f64(x) on the other side of x
+    (float64). The two bracket x: they are the two roundings of x that a
+    computation carrying x with a small error of its own can pick where x lies
+    close to their midpoint. Equal to the rounding when x is a bf16 value."""
+    x = np.asarray(x, dtype=np.float64)
+    r = bf16_round_f64(x)
+    bits = r.astype(np.float32).view(np.uint32).astype(np.int64)
+    mag, neg = bits & 0x7FFFFFFF, (bits >> 31) & 1
+    above = x > r                       # the other neighbour lies above r
+    grow = np.where(neg == 0, above, ~above)   # its magnitude is larger than r's
+    new_mag = np.where(grow, mag + 0x10000, mag - 0x10000)
+    new_neg = neg
+    zero = mag == 0                     # r = +-0: the neighbour is +-2^-133 on x's side
+    new_mag = np.where(zero, 0x10000, new_mag)
+    new_neg = np.where(zero, (x < 0).astype(np.int64), new_neg)
+    out_bits = ((new_neg << 31) | new_mag).astype(np.uint32)
+    other = out_bits.view(np.float32).astype(np.float64)
+    return np.where(x == r, r, other)

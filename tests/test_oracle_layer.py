@@ -18,7 +18,7 @@ import torch
 
 from oracle import (ExpertWeights, layer_forward, layer_backward, token_forward,
                     route, quantize_nf4, activation, combine, bf16_round_f64)
-from oracle.layer import HALVES, INTERLEAVED, SWIGLU, SWIGLU_CLAMPED
+from oracle.layer import HALVES, INTERLEAVED, SWIGLU, SWIGLU_CLAMPED, activation_backward
 from tests.conftest import read_golden
 
 NF4_GOLD = [float(r[0]) for r in read_golden("nf4_levels.txt")]
@@ -294,6 +294,68 @@ def test_backward_matches_finite_differences(layout, act, limit):
     for pos in list(np.ndindex(B.shape))[::3]:
         assert abs(fd(B, pos) - gr["dB"][pos]) < 1e-6 * (1 + abs(gr["dB"][pos]))
     assert np.all(gr["dA"][3] == 0) and np.all(gr["dB"][3] == 0)
+
+
+def test_clamp_flip_takes_the_neighbouring_side():
+    """A flipped clamp entry sitting exactly on a boundary gets the derivative
+    of the point one float64 ulp across that boundary (the clamped function
+    is continuous there, so only the indicator changes); unflipped entries,
+    and every entry of the plain SwiGLU, are untouched."""
+    a, L = 1.702, 7.0
+    W = ExpertWeights(E=1, H=1, I=4, layout=INTERLEAVED, act=SWIGLU_CLAMPED, gu=None, dn=None,
+                      alpha=a, limit=L)
+    # pairs (g, u): g on its boundary, u on +limit, u on -limit, an interior point
+    g = np.array([[L, 0.5, -2.0, 1.0]])
+    u = np.array([[3.0, L, -L, 2.0]])
+    gu = np.empty((1, 8))
+    gu[:, 0::2], gu[:, 1::2] = g, u
+    dh = np.array([[1.5, -0.75, 2.0, 1.25]])
+    base = activation_backward(gu, dh, W)
+    flip = np.zeros_like(gu, dtype=bool)
+    flip[0, 0] = flip[0, 3] = flip[0, 5] = True   # g of pair 0, u of pairs 1 and 2
+    got = activation_backward(gu, dh, W, flip)
+    across = gu.copy()
+    across[0, 0] = np.nextafter(L, np.inf)
+    across[0, 3] = np.nextafter(L, np.inf)
+    across[0, 5] = np.nextafter(-L, -np.inf)
+    want = activation_backward(across, dh, W)
+    assert np.allclose(got, want, rtol=1e-13, atol=0)
+    assert got[0, 0] == 0 and got[0, 3] == 0 and got[0, 5] == 0 and base[0, 0] != 0
+    keep = ~flip
+    assert np.array_equal(got[keep], base[keep])
+    assert np.array_equal(activation_backward(gu, dh, W, np.zeros_like(flip)), base)
+    # and the other direction: a value just outside, flipped, passes like the boundary
+    out = across.copy()
+    assert np.allclose(activation_backward(out, dh, W, flip), base, rtol=1e-13, atol=0)
+    Ws = ExpertWeights(E=1, H=1, I=4, layout=INTERLEAVED, act=SWIGLU, gu=None, dn=None)
+    assert np.array_equal(activation_backward(gu, dh, Ws, flip), activation_backward(gu, dh, Ws))
+
+
+def test_round_flip_takes_the_other_neighbour_of_dgu():
+    """round_flip changes exactly the flagged dGU operands, each to the other
+    bf16 neighbour of its exact value, and the rest of the backward follows
+    from the changed operand: dx_perm moves by the change times the gate_up
+    weight row (plus the adapter path)."""
+    from oracle import bf16_other_neighbour_f64
+    rng = np.random.default_rng(19)
+    E, H, I, r, T, k = 2, 64, 32, 4, 6, 2
+    W, Wg, *_ = _dense_layer(rng, E, H, I, r, HALVES, SWIGLU)
+    W.lora_A = W.lora_B = None
+    x = _bf16(rng.standard_normal((T, H)))
+    dout = _bf16(rng.standard_normal((T, H)))
+    idx, w = route(rng.standard_normal((T, E)).astype(np.float32), k)
+    base = layer_backward(x, idx, w, dout, W)
+    flip = np.zeros_like(base["dgu"], dtype=bool)
+    flip[1, 3] = flip[4, 40] = True
+    got = layer_backward(x, idx, w, dout, W, round_flip=flip)
+    assert np.array_equal(got["dgu"][~flip], base["dgu"][~flip])
+    want = bf16_other_neighbour_f64(base["dgu_exact"][flip])
+    assert np.array_equal(got["dgu"][flip], want) and np.all(want != base["dgu"][flip])
+    e_of = np.searchsorted(base["offsets"], np.arange(T * k), side="right") - 1
+    for (row, col) in ((1, 3), (4, 40)):
+        delta = got["dgu"][row, col] - base["dgu"][row, col]
+        pred = base["dx_perm"][row] + delta * Wg[e_of[row]][col]
+        assert np.allclose(got["dx_perm"][row], pred, rtol=1e-12, atol=1e-12)
 
 
 def test_backward_matches_torch_autograd():
