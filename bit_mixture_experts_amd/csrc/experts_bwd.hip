@@ -228,6 +228,44 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
 #pragma unroll
     for (int j = 0; j < kGStages - 1; ++j)
       if (j < nk) issue(j);
+    // LoRA delta of dx (gate_up dgrad) while the first batches land: MFMA steps
+    // over the rank, A = bf16(t[row][q]), B = A_e[q][n] (bf16 already). They
+    // start from zero accumulators, which then hold the fp32 sum scaled once
+    // by lora_scale, as dx = dGU W + lora_scale * (bf16(t) A) defines it; the
+    // k-tiles accumulate on top.
+    if (MODE == DGRAD_GATEUP && a.r) {
+      const uint16_t* ar = a.loraA + ((int64_t)e * a.r) * Nw + n;
+      for (int q0 = 0; q0 < a.r; q0 += 16) {
+        u32x4 pb;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int q = q0 + 8 * h + 2 * jj;
+          const uint32_t x0 = (n < Nw && q < a.r) ? ar[(int64_t)q * Nw] : 0u;
+          const uint32_t x1 = (n < Nw && q + 1 < a.r) ? ar[(int64_t)(q + 1) * Nw] : 0u;
+          pb[jj] = x0 | (x1 << 16);
+        }
+#pragma unroll
+        for (int i = 0; i < NRT; ++i) {
+          const int rr = i * 32 + n32;
+          const float* tr = a.t + (int64_t)(row0 + rr) * a.r;
+          u32x4 pk;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int q = q0 + 8 * h + 2 * jj;
+            const float x0 = (rr < nrows && q < a.r) ? tr[q] : 0.0f;
+            const float x1 = (rr < nrows && q + 1 < a.r) ? tr[q + 1] : 0.0f;
+            pk[jj] = pack_bf16x2(x0, x1);
+          }
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
+                                                           __builtin_bit_cast(bf16x8, pb), acc[i],
+                                                           0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NRT; ++i)
+#pragma unroll
+        for (int z = 0; z < 16; ++z) acc[i][z] *= a.lscale;
+    }
     if (nk >= 3) wait_vmcnt<3 * kGLoads>();
     else if (nk == 2) wait_vmcnt<2 * kGLoads>();
     else wait_vmcnt<kGLoads>();
@@ -258,39 +296,6 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
       // next k-tile's weights into the other Bt buffer (after the last k-tile
       // the stage holds zeros or stale bytes: decoded and never read)
       dequant_to_bt((kt + 1) % kGStages, (kt + 1) & 1);
-    }
-
-    // LoRA delta of dx (gate_up dgrad) as extra reduction steps over the rank:
-    // A = bf16(t[row][q]), B = bf16(lora_scale * A_e[q][n])
-    if (MODE == DGRAD_GATEUP && a.r) {
-      for (int q0 = 0; q0 < a.r; q0 += 16) {
-        u32x4 pb;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int q = q0 + 8 * h + 2 * jj;
-          const uint16_t* ar = a.loraA + ((int64_t)e * a.r) * Nw + n;
-          const float x0 = (n < Nw && q < a.r) ? a.lscale * bf16_to_f32(ar[(int64_t)q * Nw]) : 0.0f;
-          const float x1 =
-              (n < Nw && q + 1 < a.r) ? a.lscale * bf16_to_f32(ar[(int64_t)(q + 1) * Nw]) : 0.0f;
-          pb[jj] = pack_bf16x2(x0, x1);
-        }
-#pragma unroll
-        for (int i = 0; i < NRT; ++i) {
-          const int rr = i * 32 + n32;
-          const float* tr = a.t + (int64_t)(row0 + rr) * a.r;
-          u32x4 pk;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int q = q0 + 8 * h + 2 * jj;
-            const float x0 = (rr < nrows && q < a.r) ? tr[q] : 0.0f;
-            const float x1 = (rr < nrows && q + 1 < a.r) ? tr[q + 1] : 0.0f;
-            pk[jj] = pack_bf16x2(x0, x1);
-          }
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
-                                                           __builtin_bit_cast(bf16x8, pb), acc[i],
-                                                           0, 0, 0);
-        }
-      }
     }
 
     // ---- epilogue: lane holds column n of each 32 x 32 row tile, rows

@@ -678,6 +678,48 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
     issue_b(0, 0);
     issue(0);
     if (nk > 1) issue(1);
+    // LoRA delta while the first batches land: MFMA steps over the rank (the
+    // rank index q is their k), operand A = bf16(xa[row][q]), operand B =
+    // B[e][n][q] (bf16 already; zero past r and for idle columns). They start
+    // from zero accumulators, which then hold the fp32 sum scaled once by
+    // lora_scale, as gu = x W^T + lora_scale * (bf16(xa) B^T) defines it; the
+    // k-tiles accumulate on top.
+    if constexpr (GATEUP) {
+      if (a.r) {
+        bool on;
+        const int wr = wrow_of(n32, on);
+        const uint16_t* brow = a.loraB + ((int64_t)e * 2 * a.I + wr) * a.r;
+        for (int q0 = 0; q0 < a.r; q0 += 16) {
+          u32x4 bl;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int q = q0 + 8 * h + 2 * jj;
+            const uint32_t v0 = (on && q < a.r) ? brow[q] : 0u;
+            const uint32_t v1 = (on && q + 1 < a.r) ? brow[q + 1] : 0u;
+            bl[jj] = v0 | (v1 << 16);
+          }
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            const int row = rt * 32 + n32;
+            const float* xr = a.xa + (int64_t)(row0 + row) * a.r;
+            u32x4 al;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int q = q0 + 8 * h + 2 * jj;
+              const float v0 = (row < nrows && q < a.r) ? xr[q] : 0.0f;
+              const float v1 = (row < nrows && q + 1 < a.r) ? xr[q + 1] : 0.0f;
+              al[jj] = pack_bf16x2(v0, v1);
+            }
+            acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, bl), acc[rt], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[rt][i] *= a.lscale;
+      }
+    }
     if (nk > 1) wait_vmcnt<2 * kLoadsPerTile>();
     else wait_vmcnt<kLoadsPerTile>();
     read_b(0, braw, sc);   // the wave's own loads: no barrier needed
@@ -724,41 +766,6 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
         for (int j = 0; j < kParts; ++j)
           if (f == j * kN / kParts && more) issue_part(kt + 2, j);
         __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // LoRA delta as a last stretch of the reduction: the rank index q is the
-    // k of extra MFMA steps, operand A = bf16(xa[row][q]) and operand B =
-    // bf16(lora_scale * B[e][n][q]) (zero past r and for idle columns).
-    if constexpr (GATEUP) {
-      if (a.r) {
-        bool on;
-        const int wr = wrow_of(n32, on);
-        const uint16_t* brow = a.loraB + ((int64_t)e * 2 * a.I + wr) * a.r;
-        for (int q0 = 0; q0 < a.r; q0 += 16) {
-          u32x4 bl;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int q = q0 + 8 * h + 2 * jj;
-            const float v0 = (on && q < a.r) ? a.lscale * bf16_to_f32(brow[q]) : 0.0f;
-            const float v1 = (on && q + 1 < a.r) ? a.lscale * bf16_to_f32(brow[q + 1]) : 0.0f;
-            bl[jj] = pack_bf16x2(v0, v1);
-          }
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            const int row = rt * 32 + n32;
-            const float* xr = a.xa + (int64_t)(row0 + row) * a.r;
-            u32x4 al;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int q = q0 + 8 * h + 2 * jj;
-              const float v0 = (row < nrows && q < a.r) ? xr[q] : 0.0f;
-              const float v1 = (row < nrows && q + 1 < a.r) ? xr[q + 1] : 0.0f;
-              al[jj] = pack_bf16x2(v0, v1);
-            }
-            acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, bl), acc[rt], 0, 0, 0);
-          }
-        }
       }
     }
     // ---- epilogue. Lane holds column n32 of each 32x32 tile, rows

@@ -109,8 +109,12 @@ __global__ __launch_bounds__(256) void k_transpose_rank(const uint16_t* __restri
 // ranks per pass; the four waves' partial sums meet in LDS. A rank entry past
 // r (read from the next row, or as zero past the last) is multiplied by zero:
 // the mask makes it 0 before the product, so it never reaches a sum.
+// R4: r % 4 == 0, so every 16-byte piece of a row's ranks lies wholly inside
+// the window's resource or wholly past its end (then it reads zeros); other
+// ranks are read one dword at a time, each checked against the resource on its
+// own (a multi-dword load that straddles the end is not relied on).
 constexpr int kQ = 8;
-template <bool TRANSPOSED>
+template <bool TRANSPOSED, bool R4>
 __global__ __launch_bounds__(256) void k_rank_reduce(const uint16_t* __restrict__ mat, int ncols,
                                                      const float* __restrict__ vec, int r,
                                                      const int32_t* __restrict__ offsets,
@@ -145,8 +149,16 @@ __global__ __launch_bounds__(256) void k_rank_reduce(const uint16_t* __restrict_
             u32x2, __builtin_amdgcn_raw_buffer_load_b64(rmat, on ? (rw * ncols + col) * 2 : kOob,
                                                         0, 0));
         // ranks q0 .. q0 + 7 of the row (entries past r are masked below)
-        vlo[j] = __builtin_bit_cast(f32x4, buf_load_b128(rvec, (rw * r + q0) * 4));
-        vhi[j] = __builtin_bit_cast(f32x4, buf_load_b128(rvec, (rw * r + q0 + 4) * 4));
+        if constexpr (R4) {
+          vlo[j] = __builtin_bit_cast(f32x4, buf_load_b128(rvec, (rw * r + q0) * 4));
+          vhi[j] = __builtin_bit_cast(f32x4, buf_load_b128(rvec, (rw * r + q0 + 4) * 4));
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            vlo[j][q] = __uint_as_float(buf_load_b32(rvec, (rw * r + q0 + q) * 4));
+            vhi[j][q] = __uint_as_float(buf_load_b32(rvec, (rw * r + q0 + 4 + q) * 4));
+          }
+        }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -212,12 +224,19 @@ hipError_t launch_rank_reduce(const uint16_t* mat, int ncols, const float* vec, 
                               const int32_t* offsets, int rows, int E, float lscale, float* out,
                               bool transposed, hipStream_t s) {
   const dim3 grid((unsigned)((ncols + 255) / 256), (unsigned)E);
-  if (transposed)
-    hipLaunchKernelGGL(k_rank_reduce<true>, grid, dim3(256), 0, s, mat, ncols, vec, r, offsets,
-                       rows, lscale, out);
+  const bool r4 = r % 4 == 0;
+  if (transposed && r4)
+    hipLaunchKernelGGL((k_rank_reduce<true, true>), grid, dim3(256), 0, s, mat, ncols, vec, r,
+                       offsets, rows, lscale, out);
+  else if (transposed)
+    hipLaunchKernelGGL((k_rank_reduce<true, false>), grid, dim3(256), 0, s, mat, ncols, vec, r,
+                       offsets, rows, lscale, out);
+  else if (r4)
+    hipLaunchKernelGGL((k_rank_reduce<false, true>), grid, dim3(256), 0, s, mat, ncols, vec, r,
+                       offsets, rows, lscale, out);
   else
-    hipLaunchKernelGGL(k_rank_reduce<false>, grid, dim3(256), 0, s, mat, ncols, vec, r, offsets,
-                       rows, lscale, out);
+    hipLaunchKernelGGL((k_rank_reduce<false, false>), grid, dim3(256), 0, s, mat, ncols, vec, r,
+                       offsets, rows, lscale, out);
   return hipGetLastError();
 }
 

@@ -143,6 +143,19 @@ def test_descriptor_refusals(field, value, code, msg):
     assert moe4.moe4_last_variant() == 0
 
 
+def test_activation_tile_offsets_refused():
+    # one expert's packed matrix fits (I * H < 2^31) but a 320-row activation
+    # tile of K = H bf16 values does not fit 32-bit byte offsets
+    d = _desc(H=1 << 22, I=64)
+    assert _fwd(d) == moe4.MOE4_ESHAPE
+    assert "320-row activation tile" in moe4.moe4_last_error()
+    d = _desc(H=64, I=1 << 21)   # K = 2I of the gate_up dgrad
+    assert _fwd(d) == moe4.MOE4_ESHAPE
+    d = _desc(H=3 << 20, I=64)   # the largest H below the limit passes validation
+    assert 640 * d.H < 1 << 31
+    assert lib.moe4_workspace_size(ctypes.byref(d), 4, 2) > 0
+
+
 def test_mxfp4_alignment_and_clamp_parameters():
     d = _desc(format=moe4.MOE4_FMT_MXFP4, H=2880, I=2880, act=moe4.MOE4_ACT_SWIGLU_CLAMPED,
               act_limit=0.0)
