@@ -11,8 +11,8 @@ import torch
 
 import oracle
 from bit_mixture_experts_amd import inputs as inp
-from tests.gpu_helpers import (DEV, HostLayer, assert_close, bits, check_bf16_output, f64,
-                               run_layer, say, to_dev)
+from tests.gpu_helpers import (DEV, HostLayer, assert_close, backward_reference, bits,
+                               check_bf16_output, f64, run_layer, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +52,18 @@ WIDEST_MXFP4 = inp.GPT_OSS_20B_MXFP4.scaled(name="widest_mxfp4_E1024_k4", seed_i
 # top-16 routing: the combine's rows past the eighth and permute's k > 8
 TOPK16_NF4 = inp.TINY_NF4.scaled(name="top16_nf4_E64_k16", seed_id=118, E=64, k=16, H=128,
                                  I=64, tokens=(30,))
+# adapter ranks other than the workloads' 8, with lora_scale = alpha / r not
+# always a power of two: ranks that are not a multiple of four (the adapter
+# gradient reductions then read the ranks a dword at a time), ranks past one
+# 16-wide MFMA rank step (r > 16) and past one 32-wide tile of the rank
+# projection (r > 32), up to the largest rank the interface takes
+RANKS = [(1, 2.0), (3, 5.0), (6, 12.0), (12, 16.0), (33, 66.0), (64, 16.0), (4, 3.0)]
+RANK_NF4 = [LORA_SMALL.scaled(name=f"lora_nf4_r{r}_a{a:g}", seed_id=120 + i, lora_r=r,
+                              lora_alpha=a, tokens=(60,)) for i, (r, a) in enumerate(RANKS)]
+RANK_MXFP4 = [MXFP4_LORA_SMALL.scaled(name="lora_mxfp4_r3_a5", seed_id=130, lora_r=3,
+                                      lora_alpha=5.0, tokens=(36,)),
+              MXFP4_LORA_SMALL.scaled(name="lora_mxfp4_r33_a40", seed_id=131, lora_r=33,
+                                      lora_alpha=40.0, tokens=(36,))]
 _LAYERS = {}
 
 
@@ -512,6 +524,33 @@ def test_layer_forward(spec, T, variant):
         assert rel < 0.05
 
 
+RANK_FWD = [(s, s.tokens[0]) for s in RANK_NF4 + RANK_MXFP4]
+
+
+@pytest.mark.parametrize("variant", [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED])
+@pytest.mark.parametrize("spec,T", RANK_FWD, ids=[s.name for s, _ in RANK_FWD])
+def test_layer_forward_lora_ranks(spec, T, variant):
+    """Both kernel families apply lora_scale in fp32 to the rank sum, for any
+    rank the interface takes."""
+    say(f"forward {spec.name} (scale {spec.lora_scale:g}) T={T} variant={variant}")
+    L = layer_of(spec)
+    x, lg = inp.host_tokens(spec, T)
+    res = run_layer(L.device(variant), to_dev(x), to_dev(lg), spec.k, save=True)
+    assert res["variant"] == variant
+    ri, rw = oracle.route(lg, spec.k)
+    ref = oracle.layer_forward(x, ri, rw, L.W, keep=True)
+    assert_close(res["save_xa"].cpu().numpy(), ref["xa"], "xa")
+    assert_close(res["save_gu"].cpu().numpy(), ref["gu"], "gu")
+    assert_close(res["y_perm"].cpu().numpy(), ref["y"], "y_perm")
+    assert_close(res["out32"].cpu().numpy(), ref["out"], "out")
+    base = oracle.layer_forward(x, ri, rw, _without_lora(L), keep=True)
+    got = res["save_gu"].cpu().numpy() - base["gu"]
+    want = ref["gu"] - base["gu"]
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    say(f"  lora delta relative L2 error {rel:.2e}")
+    assert rel < 0.05
+
+
 def _without_lora(L):
     import copy
     W = copy.copy(L.W)
@@ -641,13 +680,10 @@ def test_layer_backward_skewed(T):
     assert_close(dB_h, ref["dB"], "dB")
 
 
-@pytest.mark.parametrize("spec,T", BWD_CASES, ids=[s.name for s, _ in BWD_CASES])
-def test_layer_backward(spec, T):
-    say(f"backward {spec.name} T={T}")
-    L = layer_of(spec)
-    ex = L.device()
-    x, lg = inp.host_tokens(spec, T)
-    dout = inp.host_upstream_grad(spec, T)
+def gpu_backward(spec, ex, x, lg, dout):
+    """Forward (saving gu and xa), the row-scaled gather of dOut, the expert
+    backward and the dX combine, on the GPU."""
+    T = x.shape[0]
     res = run_layer(ex, to_dev(x), to_dev(lg), spec.k, save=True)
     S = T * spec.k
     dy = torch.empty((S, spec.H), dtype=torch.bfloat16, device=DEV)
@@ -663,18 +699,81 @@ def test_layer_backward(spec, T):
     dx = torch.empty((T, spec.H), dtype=torch.float32, device=DEV)
     moe4.moe4_combine(dx_perm, res["row_of_slot"], None, dx, spec.k)
     torch.cuda.synchronize()
+    return dict(res=res, dy=dy, dx_perm=dx_perm, dA=dA, dB=dB, dx=dx)
+
+
+def check_backward(spec, L, T):
+    ex = L.device()
+    x, lg = inp.host_tokens(spec, T)
+    dout = inp.host_upstream_grad(spec, T)
+    g = gpu_backward(spec, ex, x, lg, dout)
     ri, rw = oracle.route(lg, spec.k)
     # the row-scaled gather is bit-exact with the oracle's definition
     _, rs, _ = oracle.permute(ri, spec.E)
-    assert np.array_equal(bits(dy), oracle.gather_rows(dout, rs, spec.k,
-                                                       row_scale=res["w"].cpu().numpy().reshape(-1)))
-    ref = oracle.layer_backward(x, ri, rw, dout, L.W)
-    assert_close(dx_perm.cpu().numpy(), ref["dx_perm"], "dx_perm")
-    assert_close(dx.cpu().numpy(), ref["dx"], "dx")
-    dA_h, dB_h = dA.cpu().numpy(), dB.cpu().numpy()
+    assert np.array_equal(bits(g["dy"]), oracle.gather_rows(
+        dout, rs, spec.k, row_scale=g["res"]["w"].cpu().numpy().reshape(-1)))
+    ref = backward_reference(x, ri, rw, dout, L.W, g["res"]["save_gu"].cpu().numpy(),
+                             g["dx_perm"].cpu().numpy())
+    assert_close(g["dx_perm"].cpu().numpy(), ref["dx_perm"], "dx_perm")
+    assert_close(g["dx"].cpu().numpy(), ref["dx"], "dx")
+    dA_h, dB_h = g["dA"].cpu().numpy(), g["dB"].cpu().numpy()
     counts = np.bincount(ri.reshape(-1), minlength=spec.E)
     for e in range(spec.E):
         if counts[e] == 0:
             assert np.all(dA_h[e] == 0) and np.all(dB_h[e] == 0)
     assert_close(dA_h, ref["dA"], "dA")
     assert_close(dB_h, ref["dB"], "dB")
+
+
+@pytest.mark.parametrize("spec,T", BWD_CASES, ids=[s.name for s, _ in BWD_CASES])
+def test_layer_backward(spec, T):
+    say(f"backward {spec.name} T={T}")
+    check_backward(spec, layer_of(spec), T)
+
+
+@pytest.mark.parametrize("spec", RANK_NF4 + RANK_MXFP4, ids=[s.name for s in RANK_NF4 + RANK_MXFP4])
+def test_layer_backward_lora_ranks(spec):
+    say(f"backward {spec.name} (r={spec.lora_r}, scale {spec.lora_scale:g}) T={spec.tokens[0]}")
+    check_backward(spec, layer_of(spec), spec.tokens[0])
+
+
+@pytest.mark.parametrize("spec,T", [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40)],
+                         ids=["nf4", "mxfp4"])
+def test_backward_deterministic(spec, T):
+    """Two backward passes of one batch agree bit for bit: the dgrad kernels,
+    the rank projection and the adapter-gradient reductions sum in a fixed
+    order (no atomics)."""
+    say(f"backward run twice, bitwise: {spec.name} T={T}")
+    L = layer_of(spec)
+    ex = L.device()
+    x, lg = inp.host_tokens(spec, T)
+    dout = inp.host_upstream_grad(spec, T)
+    a = gpu_backward(spec, ex, x, lg, dout)
+    b = gpu_backward(spec, ex, x, lg, dout)
+    for key in ("dy", "dx_perm", "dA", "dB", "dx"):
+        ta, tb = a[key], b[key]
+        if ta.dtype == torch.bfloat16:
+            ta, tb = ta.view(torch.int16), tb.view(torch.int16)
+        assert torch.equal(ta, tb), key
+    for key in ("save_gu", "save_xa", "y_perm"):
+        assert torch.equal(a["res"][key], b["res"][key]), key
+
+
+def test_route_backward_deterministic():
+    say("route_backward run twice, bitwise")
+    T, E, k, H = 300, 128, 8, 2048
+    spec = inp.QWEN3_30B_NF4.scaled(name="route_bwd_det", seed_id=119, E=E, k=k, H=H)
+    _, lg = inp.host_tokens(spec, T)
+    ri, rw = oracle.route(lg, k)
+    _, _, row_of_slot = oracle.permute(ri, E)
+    args = [to_dev(ri.astype(np.int32)), to_dev(rw.astype(np.float32)),
+            to_dev(inp.host_upstream_grad(spec, T)), to_dev(inp.host_slot_outputs(spec, T)),
+            to_dev(row_of_slot)]
+    outs = []
+    for _ in range(2):
+        dw = torch.empty((T, k), dtype=torch.float32, device=DEV)
+        dl = torch.empty((T, E), dtype=torch.float32, device=DEV)
+        moe4.moe4_route_backward(*args, dw, dl)
+        torch.cuda.synchronize()
+        outs.append((dw, dl))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
