@@ -7,9 +7,22 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace {
+
+// Scratch of moe4_expert_forward_noalloc: file-scope device memory, one copy
+// on every GPU the library runs on, held until the process ends. In host code
+// `scratch` names a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, once per device (scratch_of_current_device).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static_assert(MOE4_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "moe4.h states the size");
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
 
 thread_local char g_err[512] = "";
 thread_local int g_variant = 0;
@@ -128,6 +141,40 @@ int check_experts(const moe4_experts* ex) {
     REQUIRE_ALIGN(ex->lora_B, 2, "moe4_experts.lora_B");
     if (ex->H % 8) return fail(MOE4_ESHAPE, "LoRA needs H %% 8 == 0 (H = %d)", ex->H);
   }
+  return MOE4_OK;
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call per device (with that device current) and kept.
+int scratch_of_current_device(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(MOE4_EDEVICE, "moe4_expert_forward_noalloc: hipGetDevice failed: %s",
+                hipGetErrorString(e));
+  if (stream != nullptr) {
+    int sdev = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess)
+      return fail(MOE4_EINVAL, "moe4_expert_forward_noalloc: stream: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(MOE4_EINVAL,
+                  "moe4_expert_forward_noalloc: stream is on device %d, the current device is %d",
+                  sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE4_EDEVICE, "moe4_expert_forward_noalloc: device %d beyond the %d supported",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MOE4_EDEVICE, "moe4_expert_forward_noalloc: device %d: scratch address: %s",
+                  dev, hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
   return MOE4_OK;
 }
 
@@ -338,10 +385,13 @@ int moe4_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32
                   "moe4_permute");
 }
 
-int moe4_expert_forward(const moe4_experts* ex, const uint16_t* x_perm, const int32_t* offsets,
-                        int32_t rows, float* y_perm, float* save_gu, float* save_xa,
-                        void* ws, size_t ws_bytes, void* stream) {
-  g_variant = 0;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the expert forward (both entry points).
+int check_forward(const moe4_experts* ex, const uint16_t* x_perm, const int32_t* offsets,
+                  int32_t rows, float* y_perm, float* save_gu, float* save_xa) {
   int rc = check_experts(ex);
   if (rc) return rc;
   if (rows < 0) return fail(MOE4_ESHAPE, "rows = %d is negative", rows);
@@ -356,6 +406,43 @@ int moe4_expert_forward(const moe4_experts* ex, const uint16_t* x_perm, const in
   REQUIRE_ALIGN(y_perm, 16, "y_perm");
   REQUIRE_ALIGN(save_gu, 4, "save_gu");
   REQUIRE_ALIGN(save_xa, 4, "save_xa");
+  return MOE4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe4_expert_forward_noalloc(const moe4_experts* ex, const uint16_t* x_perm,
+                                const int32_t* offsets, int32_t rows, float* y_perm,
+                                float* save_gu, float* save_xa, void* stream) {
+  g_variant = 0;
+  int rc = check_forward(ex, x_perm, offsets, rows, y_perm, save_gu, save_xa);
+  if (rc) return rc;
+  const size_t need = moe4::forward_ws_bytes(*ex, rows);
+  if (need > kNoAllocScratchBytes)
+    return fail(MOE4_EWORKSPACE,
+                "moe4_expert_forward_noalloc: this call needs %zu bytes of scratch, beyond the "
+                "%zu the library holds per device (moe4_expert_forward takes a workspace)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  rc = scratch_of_current_device(stream, &ws);
+  if (rc) return rc;
+  int variant = 0;
+  hipError_t e = moe4::launch_expert_forward(*ex, x_perm, offsets, rows, y_perm, save_gu,
+                                             save_xa, ws, &variant, moe4::LaunchEvents{g_events},
+                                             (hipStream_t)stream);
+  rc = launched(e, "moe4_expert_forward_noalloc");
+  if (rc == MOE4_OK) g_variant = variant;
+  return rc;
+}
+
+int moe4_expert_forward(const moe4_experts* ex, const uint16_t* x_perm, const int32_t* offsets,
+                        int32_t rows, float* y_perm, float* save_gu, float* save_xa,
+                        void* ws, size_t ws_bytes, void* stream) {
+  g_variant = 0;
+  int rc = check_forward(ex, x_perm, offsets, rows, y_perm, save_gu, save_xa);
+  if (rc) return rc;
   rc = check_ws(ws, ws_bytes, moe4::forward_ws_bytes(*ex, rows), "moe4_expert_forward");
   if (rc) return rc;
   int variant = 0;

@@ -28,12 +28,14 @@ MOE4_GU_HALVES, MOE4_GU_INTERLEAVED = 1, 2
 MOE4_ACT_SWIGLU, MOE4_ACT_SWIGLU_CLAMPED = 1, 2
 MOE4_VARIANT_AUTO, MOE4_VARIANT_SKINNY, MOE4_VARIANT_TILED = 0, 1, 2
 MOE4_DTYPE_BF16, MOE4_DTYPE_F32 = 1, 2
+MOE4_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # every symbol declared in include/moe4.h
 EXPORTS = ("moe4_quantize_nf4", "moe4_compress_absmax", "moe4_expand_absmax",
            "moe4_decode_mxfp4", "moe4_convert_mxfp4_nf4",
            "moe4_router_logits", "moe4_route", "moe4_route_backward", "moe4_permute",
-           "moe4_expert_forward", "moe4_combine", "moe4_expert_backward",
+           "moe4_expert_forward", "moe4_expert_forward_noalloc", "moe4_combine",
+           "moe4_expert_backward",
            "moe4_workspace_size", "moe4_set_timing_events", "moe4_last_error",
            "moe4_last_variant")
 
@@ -71,6 +73,7 @@ _SIGS = {
     "moe4_permute": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
                      ctypes.c_int),
     "moe4_expert_forward": ([_P, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "moe4_expert_forward_noalloc": ([_P, _vp, _vp, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe4_combine": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp], ctypes.c_int),
     "moe4_expert_backward": ([_P, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                              ctypes.c_int),
@@ -268,6 +271,16 @@ def moe4_expert_forward(ex, x_perm, offsets, y_perm, save_gu=None, save_xa=None,
                                     _ptr(save_xa, _F32, "save_xa"), _ptr(ws, None, "ws"),
                                     0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(stream)))
+
+
+def moe4_expert_forward_noalloc(ex, x_perm, offsets, y_perm, save_gu=None, save_xa=None,
+                                stream=None):
+    """moe4_expert_forward with the library's per-device scratch in place of a
+    workspace (allocates nothing)."""
+    _check(_lib.moe4_expert_forward_noalloc(
+        ctypes.byref(ex.desc), _ptr(x_perm, _BF16, "x_perm"), _ptr(offsets, _I32, "offsets"),
+        x_perm.shape[0], _ptr(y_perm, _F32, "y_perm"), _ptr(save_gu, _F32, "save_gu"),
+        _ptr(save_xa, _F32, "save_xa"), _stream(stream)))
 
 
 def moe4_combine(y_perm, row_of_slot, topk_w, out, k, stream=None):

@@ -25,8 +25,9 @@
  *
  * Conventions for every entry point:
  *  - Pointers marked "device" are device (HBM) pointers owned by the caller.
- *    The library allocates nothing and keeps no device state; scratch memory is
- *    the caller's workspace (see moe4_workspace_size).
+ *    The library allocates nothing; scratch memory is the caller's workspace
+ *    (see moe4_workspace_size), except for moe4_expert_forward_noalloc, whose
+ *    scratch is a fixed buffer in the library's device code (one per GPU).
  *  - bf16 values are passed as uint16_t bit patterns.
  *  - `stream` is a hipStream_t (NULL = the null stream). Every call only
  *    enqueues work on it and returns; argument validation is synchronous and
@@ -291,6 +292,27 @@ int moe4_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
 int moe4_expert_forward(const moe4_experts* ex, const uint16_t* x_perm, const int32_t* offsets,
                         int32_t rows, float* y_perm, float* save_gu, float* save_xa,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe4_expert_forward without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same computation and kernels, with the scratch
+ * memory (the bf16 activations h, the adapter projection xa, the expanded
+ * absmax of a double-quantised stack) in a buffer of
+ * MOE4_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends. Allocates nothing.
+ *   A call that needs more scratch than that (moe4_workspace_size's forward
+ *   part: rows * I * 2 bytes, + rows * r * 4 with LoRA, + the two fp32 absmax
+ *   arrays of an NF4_DQ stack on the prefill-sized path) returns
+ *   MOE4_EWORKSPACE. `stream` must belong to the current device (else
+ *   MOE4_EINVAL). Nothing in the scratch is assumed to start at any value.
+ *   All calls on one GPU share its buffer: calls that overlap on a GPU (two
+ *   streams, two threads) race; order them on one stream.
+ */
+enum { MOE4_NOALLOC_SCRATCH_BYTES = 16 << 20 };
+int moe4_expert_forward_noalloc(const moe4_experts* ex, const uint16_t* x_perm,
+                                const int32_t* offsets, int32_t rows, float* y_perm,
+                                float* save_gu, float* save_xa, void* stream);
 
 /*
  * Weighted un-permute: out[t] = sum_{j=0..k-1} w[t,j] * y_perm[row_of_slot[t*k+j]],
