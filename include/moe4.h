@@ -211,10 +211,16 @@ int moe4_convert_mxfp4_nf4(const uint8_t* blocks, const uint8_t* scales, int64_t
                            uint8_t* packed, float* absmax, void* stream);
 
 /*
- * Top-k routing on given fp32 router logits. Per token: the k largest logits
- * (equal logits -> lower expert index; +0 == -0), output in that order;
- * weights = softmax over all E restricted to the k and, if renormalize != 0,
- * divided by their sum. NaN logits give unspecified output.
+ * Top-k routing on given fp32 router logits [Offload page, "Why it happens":
+ * top-k routing sends each token to a small subset of the experts; project
+ * page "experts4bit-qlora", "Current measured position": the top-k choice
+ * itself flips under rounding of the logits, so the logits are taken as given
+ * fp32 inputs and the choice is exact on them]. Per token: the k largest
+ * logits, output in that order; weights = softmax over all E restricted to
+ * the k and, if renormalize != 0, divided by their sum (softmax, then top-k,
+ * then renormalise). Readings where the pages are silent: the choice is made
+ * on the logits (not on the rounded probabilities); equal logits -> lower
+ * expert index; +0 == -0. NaN logits give unspecified output.
  *   logits f32 [T, E]; 1 <= k <= E <= 1024; T >= 0
  *   topk_idx i32 [T, k] out; topk_w f32 [T, k] out
  */
@@ -258,8 +264,13 @@ int moe4_route_backward(const int32_t* topk_idx, const float* topk_w, const floa
 
 /*
  * Stable permutation of the T*k routed slots (s = t*k + j) by expert, plus the
- * row gather. Rows of expert e are offsets[e] .. offsets[e+1]-1, in ascending
- * slot order. x_perm[r] = x[slot_of_row[r] / k], or with row_scale,
+ * row gather [Solutions index, grouped-nf4-gemm entry: the routed expert GEMM
+ * runs over every expert in one launch, so its input rows are grouped by
+ * expert; project page "experts4bit-qlora", "What it does": the experts of a
+ * layer are one fused [E, ...] stack indexed by expert]. Rows of expert e are
+ * offsets[e] .. offsets[e+1]-1. Reading where the pages are silent: inside an
+ * expert, rows keep ascending slot order (a stable counting sort), which
+ * makes every index deterministic; any order gives the same layer output. x_perm[r] = x[slot_of_row[r] / k], or with row_scale,
  * bf16(fp32(row_scale[s] * x[s / k])) (IEEE product, one rounding), which
  * scales an upstream gradient by its routing weight for the backward.
  *   topk_idx i32 [T, k] with values in [0, E) (else unspecified output)
@@ -317,7 +328,13 @@ int moe4_expert_forward_noalloc(const moe4_experts* ex, const uint16_t* x_perm,
 /*
  * Weighted un-permute: out[t] = sum_{j=0..k-1} w[t,j] * y_perm[row_of_slot[t*k+j]],
  * summed in fp32 in ascending j; topk_w == NULL gives the plain sum (used to
- * sum dx_perm into dX after the backward). out_dtype MOE4_DTYPE_BF16 stores
+ * sum dx_perm into dX after the backward). The pages do not spell the combine
+ * out: this is the reading of the standard routed-MoE output, the routing
+ * weights of a token's k experts applied to their outputs [project page
+ * "experts4bit-qlora", "What it does": fused MoE layers served and trained as
+ * the model defines them; Offload page, "Why it happens": each token uses its
+ * top-k experts]. Reading: the down bias is inside y_perm, so it is weighted
+ * too; the fixed ascending-j order makes the sum deterministic. out_dtype MOE4_DTYPE_BF16 stores
  * the fp32 sum rounded once to bf16 (the model dtype); MOE4_DTYPE_F32 stores
  * the fp32 sum itself (the same bits before rounding).
  *   y_perm f32 [T*k, H] (16-byte aligned); out [T, H] of out_dtype (16-byte
