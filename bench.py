@@ -217,70 +217,91 @@ def touched(torch, moe4, step, ex, x, logits):
 
 # --------------------------------------------------------------------- timing
 
+def pct(vals, q):
+    v = sorted(vals)
+    if not v:
+        return None
+    i = min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))
+    return v[i]
+
+
+def spread(vals, nd=4):
+    """median, p10 and p90 of a list of per-step figures."""
+    return {"median": round(pct(vals, 0.5), nd), "p10": round(pct(vals, 0.1), nd),
+            "p90": round(pct(vals, 0.9), nd)}
+
+
 def time_steps(torch, hip, moe4, steps, warmup, run, nkern=2):
-    """Run `run(i)` warmup + steps times; time the steps with events around the
-    whole timed region and, through the library hook, around each of the
-    (up to two) GEMM launches of every step. Returns (ms_per_step, [avg kernel
-    ms for each GEMM])."""
+    """Run `run(i)` warmup + steps times. The timed region (steps warmup ..
+    warmup + steps - 1) is bracketed by a synchronisation and events on both
+    sides; an event also marks every step boundary, and the library records
+    events around each of the (up to two) GEMM launches of every step.
+    Returns (region ms / steps, per-step ms, [per-step ms of GEMM j])."""
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
     kev = hip.events(4 * steps)
-    region = hip.events(2)
+    bounds = hip.events(steps + 1)
     per_step = [(ctypes.c_void_p * 4)(*kev[4 * i:4 * i + 4]) for i in range(steps)]
-    hip.record(region[0], stream)
     for i in range(steps):
+        hip.record(bounds[i], stream)
         moe4.moe4_set_timing_events(per_step[i])
         run(warmup + i)
     moe4.moe4_set_timing_events(None)
-    hip.record(region[1], stream)
+    hip.record(bounds[steps], stream)
     torch.cuda.synchronize()
-    total = hip.ms(region[0], region[1])
-    kms = []
-    for j in range(nkern):
-        kms.append(sum(hip.ms(kev[4 * i + 2 * j], kev[4 * i + 2 * j + 1]) for i in range(steps))
-                   / steps)
-    return total / steps, kms
+    total = hip.ms(bounds[0], bounds[steps])
+    step_ms = [hip.ms(bounds[i], bounds[i + 1]) for i in range(steps)]
+    kms = [[hip.ms(kev[4 * i + 2 * j], kev[4 * i + 2 * j + 1]) for i in range(steps)]
+           for j in range(nkern)]
+    return total / steps, step_ms, kms
 
 
 # ----------------------------------------------------------------- workloads
 
-def bench_layer(torch, hip, moe4, inputs, spec, T, exs, steps, warmup, seed, nlogits=16):
-    """Forward steps of one workload at T tokens, rotating layer replicas and
-    routing draws so that decode-sized steps read cold weights."""
+def bench_layer(torch, hip, moe4, inputs, spec, T, exs, steps, warmup, seed):
+    """Forward steps of one workload at T tokens. Every repetition (warm-up
+    included) has its own routing draw (fresh tokens and logits), and the
+    layer replicas rotate, so decode-sized steps read cold weights."""
     step = Step(moe4, torch, spec, T, exs[0])
+    n = warmup + steps
     toks = [inputs.device_tokens(spec, T, layer=li % spec.layers if spec.layers > 1 else 0,
                                  seed=seed + 1000 + li)
-            for li in range(nlogits)]
+            for li in range(n)]
     nrep = len(exs)
-    counts = [touched(torch, moe4, step, exs[0], *toks[i]) for i in range(nlogits)]
+    counts = [touched(torch, moe4, step, exs[0], *toks[i]) for i in range(n)]
 
     def run(i):
-        x, lg = toks[i % nlogits]
+        x, lg = toks[i]
         step.forward(exs[i % nrep], x, lg)
 
-    ms, (k_gu, k_dn) = time_steps(torch, hip, moe4, steps, warmup, run)
+    ms, step_ms, (k_gu, k_dn) = time_steps(torch, hip, moe4, steps, warmup, run)
     gu_b, dn_b = expert_bytes(spec)
-    # steps i = warmup .. warmup+steps-1 used logits set i % nlogits
-    ntouch = sum(counts[(warmup + i) % nlogits] for i in range(steps)) / steps
+    ntouch = [counts[warmup + i] for i in range(steps)]
     S = T * spec.k
     flops_gu = 2.0 * S * 2 * spec.I * spec.H
     flops_dn = 2.0 * S * spec.H * spec.I
+    gemm = [a + b for a, b in zip(k_gu, k_dn)]
+    wbps = [nt * (gu_b + dn_b) / (g * 1e-3) / 1e9 for nt, g in zip(ntouch, gemm)]
+    gubps = [nt * gu_b / (g * 1e-3) / 1e9 for nt, g in zip(ntouch, k_gu)]
+    tfl = [(flops_gu + flops_dn) / (g * 1e-3) / 1e12 for g in gemm]
+    gutfl = [flops_gu / (g * 1e-3) / 1e12 for g in k_gu]
     res = {
-        "workload": spec.name, "T": T, "ms_per_step": round(ms, 5),
+        "workload": spec.name, "T": T, "steps": steps, "replicas": nrep,
+        "ms_per_step": round(ms, 5), "step_ms": spread(step_ms, 5),
         "routed_tokens_per_s": round(T / (ms / 1e3), 1),
         "kernel": moe4.moe4_last_variant() == moe4.MOE4_VARIANT_SKINNY and "skinny" or "tiled",
-        "gate_up_us": round(k_gu * 1e3, 2), "down_us": round(k_dn * 1e3, 2),
-        "touched_experts": round(ntouch, 2),
-        "weight_GBps": round(ntouch * (gu_b + dn_b) / ((k_gu + k_dn) * 1e-3) / 1e9, 1),
-        "gate_up_weight_GBps": round(ntouch * gu_b / (k_gu * 1e-3) / 1e9, 1),
-        "tflops": round((flops_gu + flops_dn) / ((k_gu + k_dn) * 1e-3) / 1e12, 2),
-        "gate_up_tflops": round(flops_gu / (k_gu * 1e-3) / 1e12, 2),
+        "gate_up_us": spread([v * 1e3 for v in k_gu], 2),
+        "down_us": spread([v * 1e3 for v in k_dn], 2),
+        "touched_experts": round(sum(ntouch) / steps, 2),
+        "weight_GBps": spread(wbps, 1), "gate_up_weight_GBps": spread(gubps, 1),
+        "tflops": spread(tfl, 2), "gate_up_tflops": spread(gutfl, 2),
     }
-    res["hbm_frac"] = round(res["weight_GBps"] / HBM_PEAK_GBS, 4)
-    res["mfma_frac"] = round(res["tflops"] / BF16_PEAK_TFLOPS, 4)
-    return res, (k_gu, flops_gu, ntouch * gu_b)
+    res["hbm_frac"] = round(res["weight_GBps"]["median"] / HBM_PEAK_GBS, 4)
+    res["mfma_frac"] = round(res["tflops"]["median"] / BF16_PEAK_TFLOPS, 4)
+    k_gu_mean = sum(k_gu) / steps
+    return res, (k_gu_mean, flops_gu, sum(ntouch) / steps * gu_b)
 
 
 def bench_backward(torch, hip, moe4, inputs, spec, T, ex, steps, warmup, seed):
@@ -294,8 +315,10 @@ def bench_backward(torch, hip, moe4, inputs, spec, T, ex, steps, warmup, seed):
     def run_b(i):
         step.backward_pass(ex, dout)
 
-    f_ms, (f_gu, f_dn) = time_steps(torch, hip, moe4, steps, warmup, run_f)
-    b_ms, (b_dn, b_gu) = time_steps(torch, hip, moe4, steps, warmup, run_b)
+    f_ms, f_steps, (f_gu, f_dn) = time_steps(torch, hip, moe4, steps, warmup, run_f)
+    b_ms, b_steps, (b_dn, b_gu) = time_steps(torch, hip, moe4, steps, warmup, run_b)
+    med = lambda v: pct(v, 0.5)
+    f_gu, f_dn, b_dn, b_gu = med(f_gu), med(f_dn), med(b_dn), med(b_gu)
     S = T * spec.k
     H, I, r = spec.H, spec.I, spec.lora_r
     f_flops = 2.0 * S * (2 * I * H + H * I)
@@ -305,6 +328,7 @@ def bench_backward(torch, hip, moe4, inputs, spec, T, ex, steps, warmup, seed):
     tot = f_flops + lora_f + b_flops + lora_b
     return {
         "workload": spec.name, "T": T, "forward_ms": round(f_ms, 4), "backward_ms": round(b_ms, 4),
+        "forward_step_ms": spread(f_steps, 4), "backward_step_ms": spread(b_steps, 4),
         "fwd_bwd_ms": round(f_ms + b_ms, 4),
         "fwd_bwd_tflops_step": round(tot / ((f_ms + b_ms) * 1e-3) / 1e12, 2),
         "fwd_gemm_tflops": round(f_flops / ((f_gu + f_dn) * 1e-3) / 1e12, 2),
@@ -328,7 +352,7 @@ def bench_stack(torch, hip, moe4, inputs, spec, T, exs, steps, warmup, seed):
             step.forward(exs[l], x, lg)
 
     # the hook times the last layer's kernels of each pass; the region is the stack
-    ms, _ = time_steps(torch, hip, moe4, steps, warmup, run)
+    ms, pass_ms, _ = time_steps(torch, hip, moe4, steps, warmup, run)
     # the same pass captured once in a HIP graph and replayed: the library
     # launches on the current stream and allocates or synchronises nothing, so
     # the 36 x 4 calls capture as they are and the host launch gaps disappear
@@ -339,19 +363,21 @@ def bench_stack(torch, hip, moe4, inputs, spec, T, exs, steps, warmup, seed):
     for _ in range(warmup):
         graph.replay()
     stream = torch.cuda.current_stream().cuda_stream
-    region = hip.events(2)
+    marks = hip.events(steps + 1)
     torch.cuda.synchronize()
-    hip.record(region[0], stream)
-    for _ in range(steps):
+    for i in range(steps):
+        hip.record(marks[i], stream)
         graph.replay()
-    hip.record(region[1], stream)
+    hip.record(marks[steps], stream)
     torch.cuda.synchronize()
-    ms_graph = hip.ms(region[0], region[1]) / steps
+    ms_graph = hip.ms(marks[0], marks[steps]) / steps
+    graph_ms = [hip.ms(marks[i], marks[i + 1]) for i in range(steps)]
     del graph
     gu_b, dn_b = expert_bytes(spec)
     total_bytes = sum(counts) * (gu_b + dn_b)
     return {"workload": spec.name, "T": T, "layers": L,
             "stack_ms": round(ms, 4), "stack_ms_graph": round(ms_graph, 4),
+            "stack_ms_spread": spread(pass_ms, 4), "stack_ms_graph_spread": spread(graph_ms, 4),
             "stack_weight_GBps_graph": round(total_bytes / (ms_graph * 1e-3) / 1e9, 1),
             "per_layer_us": round(ms * 1e3 / L, 2),
             "touched_experts_per_layer": round(sum(counts) / L, 2),
@@ -435,6 +461,7 @@ def bench_router(torch, hip, moe4, inputs, spec, T, steps, warmup, seed):
         return ms[len(ms) // 2]
 
     f_ms = timed(lambda: moe4.moe4_router_logits(x, wr, lg))
+    flips = flip_floor(torch, moe4, x, wr, rb if spec.zipf else None, k)
     b_ms = timed(lambda: moe4.moe4_route_backward(idx, w, dout, y, ros, dw, dl))
     f_bytes = T * H * 2 + E * H * 2 + T * E * 4
     b_bytes = T * k * H * 4 + T * H * 2 + T * k * 12 + T * E * 4
@@ -444,49 +471,205 @@ def bench_router(torch, hip, moe4, inputs, spec, T, steps, warmup, seed):
             "logits_GBps": round(f_bytes / (f_ms * 1e-3) / 1e9, 1),
             "route_backward_us": round(b_ms * 1e3, 2),
             "route_backward_GBps": round(b_bytes / (b_ms * 1e-3) / 1e9, 1),
-            "route_backward_hbm_frac": round(b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "route_backward_hbm_frac": round(b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "routing_flip_floor": flips}
+
+
+def flip_floor(torch, moe4, x, wr, bias, k):
+    """Share of tokens whose top-k expert set on the GPU's fp32 router logits
+    differs from the top-k set of the exact logits rounded to fp32 (the exact
+    sums by a float64 matrix product on the host)."""
+    T, E = x.shape[0], wr.shape[0]
+    lg = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    moe4.moe4_router_logits(x, wr, lg, bias=bias)
+    torch.cuda.synchronize()
+    exact = x.double().cpu() @ wr.double().cpu().T
+    if bias is not None:
+        exact += bias.double().cpu()[None, :]
+    got = lg.cpu()
+    a = torch.topk(got, k, dim=1).indices.sort(dim=1).values
+    b = torch.topk(exact.float(), k, dim=1).indices.sort(dim=1).values
+    n = int((a != b).any(dim=1).sum())
+    return {"tokens": T, "flipped": n, "fraction": round(n / T, 6),
+            "exact_logits": "float64 host matmul of the same bf16 x and W_r, rounded to fp32"}
+
+
+def ceilings(torch, hip):
+    """Practical HBM ceiling of this part: a plain copy (torch copy_ of 2 GiB
+    float32: every byte read once and written once), median of 10."""
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    a = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for name, fn, nbytes in (("copy", lambda: b.copy_(a), 2 * a.numel() * 4),):
+        for _ in range(3):
+            fn()
+        ev = hip.events(2 * 10)
+        torch.cuda.synchronize()
+        for i in range(10):
+            hip.record(ev[2 * i], stream)
+            fn()
+            hip.record(ev[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        ms = pct([hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(10)], 0.5)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBS, 4),
+                     "bytes": nbytes}
+    del a, b
+    torch.cuda.empty_cache()
+    out["what"] = "torch copy_ of 2 GiB fp32 (every byte read once and written once)"
+    return out
+
+
+def device_state(torch=None, busy=None):
+    """Clocks and power as rocm-smi reports them (None where unavailable). With
+    busy (a callable issuing GPU work), rocm-smi is sampled from a second thread
+    while the GPU runs it for about two seconds, so the clocks are the loaded
+    ones."""
+    import subprocess
+    import threading
+    got = {}
+
+    def sample():
+        time.sleep(0.8)
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--showmaxpower", "--showpower",
+                                "--json"], capture_output=True, text=True, timeout=30)
+            if r.returncode == 0 and r.stdout.strip():
+                got["rec"] = json.loads(r.stdout)
+        except Exception:
+            pass
+
+    th = threading.Thread(target=sample)
+    th.start()
+    if busy is not None:
+        t0 = time.time()
+        while time.time() - t0 < 2.5 and th.is_alive():
+            for _ in range(20):
+                busy()
+            torch.cuda.synchronize()
+    th.join()
+    rec = got.get("rec")
+    if not rec:
+        return None
+    card = rec.get("card0", next(iter(rec.values()), {}))
+    keep = {"sampled": "while the GPU ran the headline step" if busy else "idle"}
+    for key, val in card.items():
+        lk = key.lower()
+        if any(w in lk for w in ("sclk", "mclk", "fclk", "power", "socclk")):
+            keep[key] = val
+    return keep
 
 
 # -------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(spec, T_batch, n_tokens, seed=0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_layer_phases(oracle, spec, x, lg, W):
+    """The oracle's forward of one batch, step by step (the same calls its
+    layer_forward makes), timed per phase: route + permute, per-expert
+    dequantisation, per-expert matmuls and activation, combine."""
+    import numpy as np
+    t = {}
+    t0 = time.perf_counter()
+    ri, rw = oracle.route(lg, spec.k)
+    offsets, slot_of_row, row_of_slot = oracle.permute(ri, spec.E)
+    t["route_permute_s"] = time.perf_counter() - t0
+    xf = oracle.bf16_bits_to_f64(x)
+    y = np.zeros((x.shape[0] * spec.k, spec.H))
+    deq = mm = 0.0
+    for e in range(spec.E):
+        a, b = offsets[e], offsets[e + 1]
+        if a == b:
+            continue
+        t0 = time.perf_counter()
+        W.expert(e)
+        t1 = time.perf_counter()
+        gu, _ = oracle.gate_up(xf[slot_of_row[a:b] // spec.k], W, e)
+        h = oracle.bf16_round_f64(oracle.activation(gu, W))
+        y[a:b] = oracle.down(h, W, e)
+        t2 = time.perf_counter()
+        deq += t1 - t0
+        mm += t2 - t1
+    t["dequantise_s"], t["matmul_activation_s"] = deq, mm
+    t0 = time.perf_counter()
+    oracle.combine(y, row_of_slot, rw, x.shape[0], spec.k)
+    t["combine_s"] = time.perf_counter() - t0
+    return t
+
+
+def cpu_baseline(spec, T_batch, n_tokens, tiny, seed=0):
     """The CPU oracle, untuned, on a bounded sample of the headline workload:
     n_tokens tokens of a T_batch batch through route -> permute -> expert
-    forward (dequantise + matmul per touched expert) -> combine."""
+    forward (dequantise + matmul per touched expert) -> combine, timed per
+    phase, with numpy's BLAS threads set to the cores this process may use.
+    Also the whole tiny layer (median of 3) on those cores and on one."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
     from bit_mixture_experts_amd import inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    x, lg = inputs.host_tokens(spec, T_batch, seed=seed)
-    x, lg = x[:n_tokens], lg[:n_tokens]
-    idx, _ = oracle.route(lg, spec.k)
-    need = sorted(set(int(e) for e in idx.reshape(-1)))
-    E, H, I = spec.E, spec.H, spec.I
-    gq = np.zeros((E, 2 * I, H // 2), np.uint8)
-    ga = np.zeros((E, 2 * I, H // 64), np.float32)
-    dq = np.zeros((E, H, I // 2), np.uint8)
-    da = np.zeros((E, H, I // 64), np.float32)
-    for e in need:   # set-up, not timed: quantise the experts the sample touches
-        wg, wd = inputs.host_nf4_source(spec, e, 0, seed)
-        p, a = oracle.quantize_nf4(wg.reshape(-1))
-        gq[e], ga[e] = p.reshape(2 * I, H // 2), a.reshape(2 * I, H // 64)
-        p, a = oracle.quantize_nf4(wd.reshape(-1))
-        dq[e], da[e] = p.reshape(H, I // 2), a.reshape(H, I // 64)
-    W = oracle.ExpertWeights.from_nf4(gq, ga, dq, da, layout=spec.layout, act=spec.act)
-    t0 = time.perf_counter()
-    ri, rw = oracle.route(lg, spec.k)
-    oracle.layer_forward(x, ri, rw, W)
-    dt = time.perf_counter() - t0
-    return {"value": round(n_tokens / dt, 3), "unit": "routed tokens/s", "cores": int(threads),
+    cores = len(os.sched_getaffinity(0))
+
+    def nf4_weights(sp, experts, phases):
+        E, H, I = sp.E, sp.H, sp.I
+        gq = np.zeros((E, 2 * I, H // 2), np.uint8)
+        ga = np.zeros((E, 2 * I, H // 64), np.float32)
+        dq = np.zeros((E, H, I // 2), np.uint8)
+        da = np.zeros((E, H, I // 64), np.float32)
+        t0 = time.perf_counter()
+        for e in experts:
+            wg, wd = inputs.host_nf4_source(sp, e, 0, seed)
+            p, a = oracle.quantize_nf4(wg.reshape(-1))
+            gq[e], ga[e] = p.reshape(2 * I, H // 2), a.reshape(2 * I, H // 64)
+            p, a = oracle.quantize_nf4(wd.reshape(-1))
+            dq[e], da[e] = p.reshape(H, I // 2), a.reshape(H, I // 64)
+        phases["quantise_s"] = time.perf_counter() - t0
+        return oracle.ExpertWeights.from_nf4(gq, ga, dq, da, layout=sp.layout, act=sp.act)
+
+    with threadpool_limits(cores):
+        x, lg = inputs.host_tokens(spec, T_batch, seed=seed)
+        x, lg = x[:n_tokens], lg[:n_tokens]
+        idx, _ = oracle.route(lg, spec.k)
+        need = sorted(set(int(e) for e in idx.reshape(-1)))
+        ph = {}
+        W = nf4_weights(spec, need, ph)
+        ph.update(oracle_layer_phases(oracle, spec, x, lg, W))
+    layer_s = sum(v for k, v in ph.items() if k != "quantise_s")
+    tiny_res = {}
+    tx, tlg = inputs.host_tokens(tiny, tiny.tokens[0], seed=seed)
+    for threads in (cores, 1):
+        with threadpool_limits(threads):
+            runs = []
+            for _ in range(3):
+                p = {}
+                Wt = nf4_weights(tiny, range(tiny.E), p)
+                p.update(oracle_layer_phases(oracle, tiny, tx, tlg, Wt))
+                runs.append(p)
+            tot = sorted(sum(v for k, v in p.items() if k != "quantise_s") for p in runs)
+            tiny_res[f"{threads}_threads"] = {
+                "layer_s_median": round(tot[1], 4),
+                "routed_tokens_per_s": round(tiny.tokens[0] / tot[1], 1),
+                "phases_s": {k: round(sorted(p[k] for p in runs)[1], 4) for k in runs[0]}}
+    return {"value": round(n_tokens / layer_s, 3), "unit": "routed tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": (f"{n_tokens} tokens of the T={T_batch} {spec.name} batch "
                        f"({len(need)} experts touched): route, permute, per-expert NF4 "
-                       f"dequantise + float64 matmul, combine; {dt:.1f} s")}
+                       f"dequantise + float64 matmul, combine; {layer_s:.1f} s "
+                       f"(quantising the touched experts on the host, not counted: "
+                       f"{ph['quantise_s']:.1f} s)"),
+            "cpu_model": cpu_model(), "blas_threads": cores,
+            "phases_s": {k: round(v, 3) for k, v in ph.items()},
+            "tiny_layer": {"workload": f"{tiny.name} T={tiny.tokens[0]}", **tiny_res}}
 
 
 PMC_TAG = "gate_up_tiled_nf4_qwen3_T4096"
@@ -578,10 +761,15 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--replicas", type=int, default=8,
+                    help="independently seeded layer replicas resident for the decode rows")
+    ap.add_argument("--decode-reps", type=int, default=60,
+                    help="timed repetitions of each decode-sized row (each its own routing draw)")
+    ap.add_argument("--tokens", default="",
+                    help="comma list of token counts to keep in the per-layer sweeps")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--only", default="", help="comma list of sweep parts: qwen,gptoss,lora,dq,router,convert,stack")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run the copy kernel of known size (for PMC scaling)")
@@ -616,6 +804,11 @@ def main():
     head, (k_gu, flops_gu, _) = bench_layer(torch, hip, moe4, inputs, spec, HEADLINE_T, exs,
                                             args.steps, args.warmup, args.seed)
     log("headline:", json.dumps(head))
+    hx, hlg = inputs.device_tokens(spec, HEADLINE_T, seed=args.seed + 7)
+    hstep = Step(moe4, torch, spec, HEADLINE_T, exs[0])
+    state = device_state(torch, lambda: hstep.forward(exs[0], hx, hlg))
+    del hstep, hx, hlg
+    log("device state:", json.dumps(state))
     achieved = flops_gu / (k_gu * 1e-3) / 1e12
     traffic = traffic_from_profile()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
@@ -625,23 +818,28 @@ def main():
 
     sweep = []
     only = set(filter(None, args.only.split(",")))
+    keep_t = set(int(t) for t in args.tokens.split(",") if t)
+    want = lambda T: not keep_t or T in keep_t
+    dreps = max(50, args.decode_reps)
     if not args.no_sweep:
         reps = max(10, args.steps)
         if not only or "qwen" in only:
             for T in (1, 16, 128):
-                r, _ = bench_layer(torch, hip, moe4, inputs, spec, T, exs, reps * 2, args.warmup,
-                                   args.seed)
-                log("sweep:", json.dumps(r))
-                sweep.append(r)
+                if want(T):
+                    r, _ = bench_layer(torch, hip, moe4, inputs, spec, T, exs, dreps,
+                                       args.warmup, args.seed)
+                    log("sweep:", json.dumps(r))
+                    sweep.append(r)
             sweep.append(head)
         if not only or "gptoss" in only:
             g = inputs.GPT_OSS_20B_MXFP4
             gex = [mxfp4_layer(moe4, inputs, g, r, args.seed, torch) for r in range(args.replicas)]
             for T in g.tokens:
-                r, _ = bench_layer(torch, hip, moe4, inputs, g, T, gex, reps * 2, args.warmup,
-                                   args.seed)
-                log("sweep:", json.dumps(r))
-                sweep.append(r)
+                if want(T):
+                    r, _ = bench_layer(torch, hip, moe4, inputs, g, T, gex,
+                                       dreps if T < 1024 else reps, args.warmup, args.seed)
+                    log("sweep:", json.dumps(r))
+                    sweep.append(r)
             del gex
         if not only or "lora" in only:
             lspec = inputs.QWEN3_30B_NF4_LORA
@@ -663,10 +861,11 @@ def main():
             dex = [nf4_dq_layer(moe4, inputs, spec, r, args.seed, torch)
                    for r in range(args.replicas)]
             for T in (1, 16, 128, HEADLINE_T):
-                r, _ = bench_layer(torch, hip, moe4, inputs, dspec, T, dex,
-                                   reps * (2 if T < HEADLINE_T else 1), args.warmup, args.seed)
-                log("sweep:", json.dumps(r))
-                sweep.append(r)
+                if want(T):
+                    r, _ = bench_layer(torch, hip, moe4, inputs, dspec, T, dex,
+                                       dreps if T < HEADLINE_T else reps, args.warmup, args.seed)
+                    log("sweep:", json.dumps(r))
+                    sweep.append(r)
             del dex
         if not only or "router" in only:
             r = bench_router(torch, hip, moe4, inputs, spec, HEADLINE_T, reps, args.warmup,
@@ -685,17 +884,26 @@ def main():
             torch.cuda.synchronize()
             log(f"36-layer MXFP4 stack ready ({time.time() - t0:.1f} s)")
             for T in s5.tokens:
-                r = bench_stack(torch, hip, moe4, inputs, s5, T, sex, max(5, reps // 2),
-                                2, args.seed)
-                log("sweep:", json.dumps(r))
-                sweep.append(r)
+                if want(T):
+                    r = bench_stack(torch, hip, moe4, inputs, s5, T, sex, max(5, reps // 2),
+                                    2, args.seed)
+                    log("sweep:", json.dumps(r))
+                    sweep.append(r)
             del sex
+            xs, _ = inputs.device_tokens(s5, 32, seed=args.seed + 31)
+            wr5, rb5 = inputs.device_router(s5, seed=args.seed)
+            r = {"workload": f"{s5.name} router step", "T": 32,
+                 "routing_flip_floor": flip_floor(torch, moe4, xs, wr5, rb5, s5.k)}
+            log("sweep:", json.dumps(r))
+            sweep.append(r)
         torch.cuda.empty_cache()
+    ceil = ceilings(torch, hip)
+    log("ceilings:", json.dumps(ceil))
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(spec, HEADLINE_T, args.cpu_tokens, args.seed)
+        cpu = cpu_baseline(spec, HEADLINE_T, args.cpu_tokens, inputs.TINY_NF4, args.seed)
         log("cpu_baseline:", json.dumps(cpu))
 
     line = {
@@ -710,6 +918,8 @@ def main():
                    "device": f"{props.name or 'AMD GPU'} {getattr(props, 'gcnArchName', '')}".strip()},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "hbm_ceilings": ceil,
+        "device_state": state,
         "sweep": sweep,
     }
     print(json.dumps(line), flush=True)
