@@ -300,6 +300,29 @@ def bench_layer(torch, hip, moe4, inputs, spec, T, exs, steps, warmup, seed):
     }
     res["hbm_frac"] = round(res["weight_GBps"]["median"] / HBM_PEAK_GBS, 4)
     res["mfma_frac"] = round(res["tflops"]["median"] / BF16_PEAK_TFLOPS, 4)
+    if T < 1024:
+        # the same timed steps (each with its own routing draw and replica)
+        # captured back to back into one HIP graph and replayed: the step time
+        # a serving loop sees without host launch overhead
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                run(warmup + i)
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream().cuda_stream
+        ev = hip.events(6)
+        rep = []
+        for r in range(3):
+            hip.record(ev[2 * r], stream)
+            g.replay()
+            hip.record(ev[2 * r + 1], stream)
+        torch.cuda.synchronize()
+        rep = sorted(hip.ms(ev[2 * r], ev[2 * r + 1]) / steps for r in range(3))
+        del g
+        res["graph_ms_per_step"] = round(rep[1], 5)
+        res["graph_routed_tokens_per_s"] = round(T / (rep[1] / 1e3), 1)
     k_gu_mean = sum(k_gu) / steps
     return res, (k_gu_mean, flops_gu, sum(ntouch) / steps * gu_b)
 

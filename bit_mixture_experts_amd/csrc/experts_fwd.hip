@@ -866,10 +866,12 @@ hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
   if (nwg == 0) return hipSuccess;
   // split K over S waves so that ~6K waves stream the weights (about six per
   // SIMD), each wave keeping at least two 128-k iterations (targets of 3K and
-  // 4K waves measured no different)
+  // 4K waves measured no different); gate_up takes at most four (with one row
+  // per expert, four waves per workgroup measured 5-15% faster than eight, and
+  // no slower elsewhere)
   const int nit = (a.K + 127) / 128;
   int S = (6144 + nwg - 1) / nwg;
-  S = max(1, min(S, min(8, nit / 2)));
+  S = max(1, min(S, min(GATEUP ? 4 : 8, nit / 2)));
   constexpr int MAXR = kSkMaxRowTiles;
   using SS = SkinnyScales<FMT>;
   // staged scales, then the partial sums of the S waves
