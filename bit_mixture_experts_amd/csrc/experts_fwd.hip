@@ -234,8 +234,19 @@ __device__ __forceinline__ void skinny_compute(const SkinnyBatch<NRT>& bt, const
     u32x4 wq = bt.wraw[c];
     transpose4x4_rows(wq);
     u32x4 bq[4];
+    if constexpr (FMT == MOE4_FMT_NF4_DQ) {
+      // every table read of the column tile first, then the arithmetic (17%
+      // faster here; the plain NF4 loop measured no different)
+      f32x2 lv[4][4];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) bq[st] = dequant8<FMT>(wq[st], sc[st * NSC / 4], lutf);
+      for (int st = 0; st < 4; ++st) fetch8<FMT>(wq[st], lutf, lv[st]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) bq[st] = apply8<FMT>(wq[st], lv[st], sc[st * NSC / 4]);
+    } else {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) bq[st] = dequant8<FMT>(wq[st], sc[st * NSC / 4], lutf);
+    }
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
