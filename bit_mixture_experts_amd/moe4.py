@@ -11,7 +11,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe4.so")
+# MOE4_LIB_PATH names another build of the same library (the host-only ASan
+# build that tests/test_abi_asan.py loads); by default the in-tree libmoe4.so
+LIB_PATH = os.environ.get("MOE4_LIB_PATH") or os.path.join(_HERE, "libmoe4.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
