@@ -304,11 +304,14 @@ __device__ __forceinline__ void skinny_body(SkinnyBatch<NRT> (&b)[kSkNb], const 
   }
 }
 
-// Skinny grouped GEMM: one workgroup = one expert x 16 kSkNc weight rows
-// (gate_up: 8 kSkNc (gate, up) pairs, the first half of the column tiles gate
-// rows and the second half the matching up rows; down: 16 kSkNc output
-// columns); its S waves split K and are reduced through LDS; the expert's rows
-// are taken 16 * MAXR at a time.
+// Skinny grouped GEMM: one workgroup = 16 MAXR rows of one expert x 16 kSkNc
+// weight rows (gate_up: 8 kSkNc (gate, up) pairs, the first half of the column
+// tiles gate rows and the second half the matching up rows; down: 16 kSkNc
+// output columns); its S waves split K and are reduced through LDS. An expert
+// with more rows than one chunk gets one workgroup per chunk, so a hot expert
+// of a skewed batch spreads over as many workgroups (which read its weights
+// concurrently, the repeats mostly from the caches) instead of one workgroup
+// streaming them once per chunk.
 //
 // Set-up is arranged so that its memory latencies overlap: the expert and its
 // row range come from one pass over the offsets; then the scales of the
@@ -316,9 +319,9 @@ __device__ __forceinline__ void skinny_body(SkinnyBatch<NRT> (&b)[kSkNb], const 
 // batch of weights and activations are all issued before a single wait and
 // the workgroup barrier.
 //
-// Three waves per SIMD (four measured the same), and the expert's rows taken 16 at a
-// time (one 16-row MFMA tile: decode-sized experts rarely have more rows, and
-// a second accumulator tile would cost the third wave).
+// Three waves per SIMD (four measured the same), and chunks of 16 rows (one
+// 16-row MFMA tile: decode-sized experts rarely have more rows, and a second
+// accumulator tile would cost the third wave).
 constexpr int kSkWavesPerEu = 3;
 constexpr int kSkMaxRowTiles = 1;
 template <int FMT, bool GATEUP>
@@ -344,14 +347,16 @@ void k_skinny(const GemmArgs a) {
   float* red = reinterpret_cast<float*>(dyn + SS::lds_bytes(K, NROW));
   const int S = blockDim.x >> 6, w = wave_id(), l = lane_id();
   const int item = blockIdx.x / a.ncg, cg = blockIdx.x - item * a.ncg;
-  int e, unused, rbeg, rend;
-  auto nonempty = [](int n) { return n > 0 ? 1 : 0; };
-  if (a.E <= 128) locate_item_batched<2>(a.offsets, a.E, item, nonempty, e, unused, rbeg, rend);
-  else locate_item(a.offsets, a.E, item, nonempty, e, unused, rbeg, rend);
+  int e, u, rbeg, rend;
+  auto chunks = [](int n) { return (n + 16 * MAXR - 1) / (16 * MAXR); };
+  if (a.E <= 128) locate_item_batched<2>(a.offsets, a.E, item, chunks, e, u, rbeg, rend);
+  else locate_item(a.offsets, a.E, item, chunks, e, u, rbeg, rend);
   e = __builtin_amdgcn_readfirstlane(e);
   if (e < 0) return;   // the whole workgroup: e is uniform
   rbeg = __builtin_amdgcn_readfirstlane(min(rbeg, a.rows));
   const int n_e = __builtin_amdgcn_readfirstlane(min(rend, a.rows)) - rbeg;
+  const int rc0 = __builtin_amdgcn_readfirstlane(16 * MAXR * u);   // this workgroup's chunk
+  if (rc0 >= n_e) return;   // rows past `rows` (uniform)
   const int Nw = GATEUP ? 2 * a.I : a.N_out;
   // weight row (inside the expert) of the workgroup's row r = 16 c + n
   auto wrow = [&](int r) {
@@ -508,13 +513,8 @@ void k_skinny(const GemmArgs a) {
   using One = std::integral_constant<int, 1>;
   using Max = std::integral_constant<int, MAXR>;
   using Yes = std::true_type;
-  using No = std::false_type;
-  if (MAXR == 1 || n_e <= 16) run_rows(One{}, Yes{}, 0);
-  else run_rows(Max{}, Yes{}, 0);
-  for (int rc = 16 * MAXR; rc < n_e; rc += 16 * MAXR) {
-    if (MAXR == 1 || n_e - rc <= 16) run_rows(One{}, No{}, rc);
-    else run_rows(Max{}, No{}, rc);
-  }
+  if (MAXR == 1 || n_e - rc0 <= 16) run_rows(One{}, Yes{}, rc0);
+  else run_rows(Max{}, Yes{}, rc0);
 }
 
 // ------------------------------------------------------------- tiled kernel
@@ -871,8 +871,10 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   }
 }
 
+// nitems: touched experts (sets the K split); nchunks: a bound on the 16-row
+// chunks of all experts (sets the grid; the workgroups past the last chunk exit)
 template <int FMT, bool GATEUP>
-hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
+hipError_t run_skinny(const GemmArgs& a, int nitems, int nchunks, hipStream_t s) {
   const int nwg = nitems * a.ncg;
   if (nwg == 0) return hipSuccess;
   // split K over S waves so that ~6K waves stream the weights (about six per
@@ -893,7 +895,7 @@ hipError_t run_skinny(const GemmArgs& a, int nitems, hipStream_t s) {
       hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)(SS::lds_bytes(SS::kKc, 16 * kSkNc) + 8 * MAXR * kSkNc * 256 * sizeof(float)));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_skinny<FMT, GATEUP>), dim3(nwg), dim3(64 * S), lds, s, a);
+  hipLaunchKernelGGL((k_skinny<FMT, GATEUP>), dim3(nchunks * a.ncg), dim3(64 * S), lds, s, a);
   return hipGetLastError();
 }
 
@@ -968,12 +970,15 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
     // partial column group, whose rows past H read as zeros and are not stored
     g.ncg = I / (8 * kSkNc);
     d.ncg = (H + 16 * kSkNc - 1) / (16 * kSkNc);
+    // 16-row chunks: at most one per row, and at most rows / 16 plus one per
+    // touched expert
+    const int nchunks = min(rows, rows / (16 * kSkMaxRowTiles) + touched);
     le.before(0, s);
-    err = run_skinny<FMT, true>(g, touched, s);
+    err = run_skinny<FMT, true>(g, touched, nchunks, s);
     le.after(0, s);
     if (err != hipSuccess) return err;
     le.before(1, s);
-    err = run_skinny<FMT, false>(d, touched, s);
+    err = run_skinny<FMT, false>(d, touched, nchunks, s);
     le.after(1, s);
     return err;
   }
