@@ -23,7 +23,11 @@ enum { DGRAD_DOWN = 0, DGRAD_GATEUP = 1 };
 
 struct DgradArgs {
   const uint8_t* wq;   // stack [E, Kw, Nw] (rows = reduction dim), Nw/2 bytes per row
-  const void* ws;      // scales per row: Nw/64 f32 (NF4) or Nw/32 u8 (MXFP4)
+  const void* ws;      // scales per row: Nw/64 f32 (NF4), Nw/32 u8 (MXFP4) or
+                       // Nw/64 u8 absmax codes (double-quantised NF4)
+  const float* ws2;    // double-quantised NF4: absmax2, one per 256 absmax of the stack
+  const float* dqoff;  // double-quantised NF4: the stack's absmax offset
+  const float* dqbook; // double-quantised NF4: the 256-entry code book
   int Kw, Nw;
   const uint16_t* A;   // [rows, Kw] bf16
   const int32_t* offsets;
@@ -71,7 +75,8 @@ constexpr int kGM = 256, kGN = 256, kGK = 32, kGStages = 4;
 // [kGK rows][kGN / 2 B] (16-byte chunk c of row r stored at c ^ ((r >> 3) & 3),
 // so that the dequantising threads' byte reads spread over the banks), and
 // the scales in 4-byte slots 32 b + r (block b of weight row r: NF4 the fp32
-// absmax, MXFP4 the e8m0 byte).
+// absmax, MXFP4 the e8m0 byte; double-quantised NF4 the code byte, and in slot
+// 128 + 32 b + r the group's absmax2).
 constexpr int kGStageA = kGM * kGK * 2;
 constexpr int kGStageB = kGK * kGN / 2;
 constexpr int kGStageS = 1024;
@@ -87,12 +92,15 @@ static_assert(kGLds + 256 * 8 <= 160 * 1024, "dgrad LDS");
 template <int FMT, int MODE>
 __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
   using F = Format<FMT>;
-  constexpr bool NF4 = FMT == MOE4_FMT_NF4;
+  constexpr bool NF4 = FMT != MOE4_FMT_MXFP4;   // NF4 levels (plain or double-quantised)
+  constexpr bool DQ = FMT == MOE4_FMT_NF4_DQ;
   constexpr int KB = F::kBlock;
   __shared__ __attribute__((aligned(16))) float2 lutf[256];
+  __shared__ float dqbook[DQ ? 256 : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t gmem[];
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   if (tid < 256) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
+  if (DQ && tid < 256) dqbook[tid] = a.dqbook[tid];
   int e, ut, cg;
   locate_tile_eq<kGM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
   e = __builtin_amdgcn_readfirstlane(e);
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
 
   const rsrc_t ra = make_rsrc(a.A + (int64_t)row0 * Kw, (uint32_t)nrows * Kw * 2);
   const rsrc_t rq = make_rsrc(a.wq + (int64_t)e * Kw * (Nw / 2), (uint32_t)Kw * (Nw / 2));
-  constexpr int sbytes = NF4 ? 4 : 1;
+  constexpr int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
   const rsrc_t rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Kw * (Nw / KB) * sbytes,
                               (uint32_t)Kw * (Nw / KB) * sbytes);
   auto stage = [&](int st) { return gmem + st * kGStage; };
@@ -126,13 +134,17 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
   // weights (waves 0..3): thread t fills bytes 16 t of the packed tile = row
   //    t / 8, physical chunk t % 8 = logical chunk ^ ((row >> 3) & 3)
   // scales (waves 4..7): thread 256 + i fills slot i = 32 b + r (NF4: slots
-  //    past 127 read zeros)
+  //    past 127 read zeros; double-quantised NF4: slots past 127 hold the
+  //    absmax2 of slot i - 128)
   const int bq_row = (tid & 255) >> 3;
   const int bq_byte = 16 * ((tid & 7) ^ ((bq_row >> 3) & 3));
   const bool bq_on = nb / 2 + bq_byte < Nw / 2;
   const int si = tid & 255;
-  const int s_row = si & 31, s_blk = si >> 5;
-  const bool s_on = (NF4 ? si < 128 : true) && (nb / KB + s_blk) < Nw / KB;
+  const int sj = DQ ? si & 127 : si;
+  const int s_row = sj & 31, s_blk = sj >> 5;
+  const bool s_on = (FMT == MOE4_FMT_NF4 ? si < 128 : true) && (nb / KB + s_blk) < Nw / KB;
+  const rsrc_t rs2 = DQ ? make_rsrc(a.ws2, (uint32_t)(((int64_t)a.E * Kw * (Nw / KB) + 255) / 256) * 4)
+                        : rs;
   auto issue_w = [&](int kt, int st) {   // weights / scales of k-tile kt
     uint8_t* base = stage(st);
     const int kb = kt * kGK;
@@ -144,12 +156,25 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
     } else {
       const int soff =
           (s_on && kb + s_row < Kw) ? ((kb + s_row) * (Nw / KB) + nb / KB + s_blk) * sbytes : kOob;
-      if constexpr (NF4)
+      if constexpr (FMT == MOE4_FMT_NF4) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, MOE4_LDS(base + kGStageA + kGStageB + (w - 4) * 256), 4, soff, 0, 0, 0);
-      else
+      } else if constexpr (DQ) {
+        if (w < 6) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, MOE4_LDS(base + kGStageA + kGStageB + (w - 4) * 256), 1, soff, 0, 0, 0);
+        } else {
+          // absmax2 of the slot's flat absmax index (in the whole stack)
+          const int64_t flat =
+              ((int64_t)e * Kw + kb + s_row) * (Nw / KB) + nb / KB + s_blk;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs2, MOE4_LDS(base + kGStageA + kGStageB + (w - 4) * 256), 4,
+              (s_on && kb + s_row < Kw) ? (int)(flat >> 8) * 4 : kOob, 0, 0, 0);
+        }
+      } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, MOE4_LDS(base + kGStageA + kGStageB + (w - 4) * 256), 1, soff, 0, 0, 0);
+      }
     }
   };
   // batch kt: the A tile of k-tile kt (stage kt % 4) and the weights of
@@ -176,6 +201,12 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
     const uint8_t* qb = base + kGStageA;
     const u32x4* sv = reinterpret_cast<const u32x4*>(base + kGStageA + kGStageB) + 8 * dq_blk + 2 * dq_c;
     const u32x4 s0 = sv[0], s1 = sv[1];   // scale slots of rows 8 dq_c .. +7
+    u32x4 g0 = {0u, 0u, 0u, 0u}, g1 = {0u, 0u, 0u, 0u};
+    if constexpr (DQ) {
+      g0 = sv[32];   // their absmax2 (slots + 128)
+      g1 = sv[33];
+    }
+    const float dqo = DQ ? a.dqoff[0] : 0.0f;
     float v0[8], v1[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -187,7 +218,11 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
       const uint32_t byte = (wd >> (8 * (dq_in & 3))) & 255u;
       const uint32_t sraw = i < 4 ? s0[i] : s1[i - 4];
       if constexpr (NF4) {
-        const float sc = __uint_as_float(sraw);
+        // absmax (double-quantised: fp32(fp32(book[code] * absmax2) + offset);
+        // a one-byte load fills the low byte of its slot)
+        const float sc =
+            DQ ? mul_then_add(dqbook[sraw & 255u], __uint_as_float(i < 4 ? g0[i] : g1[i - 4]), dqo)
+               : __uint_as_float(sraw);
         const f32x2 lv = reinterpret_cast<const f32x2*>(lutf)[byte];
         v0[i] = lv.x * sc;
         v1[i] = lv.y * sc;
@@ -373,6 +408,9 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   // dH = dy W_d[e]: W_d is [H (reduction), I]
   d.wq = static_cast<const uint8_t*>(ex.dn_q);
   d.ws = ex.dn_s;
+  d.ws2 = ex.dn_s2;
+  d.dqoff = ex.dn_soff;
+  d.dqbook = ex.dq_book;
   d.Kw = H;
   d.Nw = I;
   d.A = dy_perm;
@@ -399,6 +437,8 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   DgradArgs g = d;
   g.wq = static_cast<const uint8_t*>(ex.gu_q);
   g.ws = ex.gu_s;
+  g.ws2 = ex.gu_s2;
+  g.dqoff = ex.gu_soff;
   g.Kw = 2 * I;
   g.Nw = H;
   g.A = dgu;
@@ -431,7 +471,7 @@ size_t backward_ws_bytes(const moe4_experts& ex, int rows) {
     b += align_up((size_t)rows * ex.lora_r * sizeof(float), 256);
     b += align_up((size_t)ex.E * ex.lora_r * 2 * ex.I * sizeof(uint16_t), 256);   // B^T
   }
-  return b + dq_expand_bytes(ex);
+  return b;
 }
 
 hipError_t launch_expert_backward(const moe4_experts& ex, const uint16_t* x_perm,
@@ -448,14 +488,10 @@ hipError_t launch_expert_backward(const moe4_experts& ex, const uint16_t* x_perm
   uint16_t* bt_ws = ex.lora_A ? reinterpret_cast<uint16_t*>(p) : nullptr;
   if (ex.lora_A) p += align_up((size_t)ex.E * ex.lora_r * 2 * ex.I * sizeof(uint16_t), 256);
   if (rows == 0 && !ex.lora_A) return hipSuccess;
-  if (ex.format == MOE4_FMT_NF4_DQ) {
-    // expand the double-quantised absmax, then the plain NF4 dgrad
-    moe4_experts plain;
-    hipError_t err = dq_expand_experts(ex, p, &plain, s);
-    if (err != hipSuccess) return err;
-    return backward_fmt<MOE4_FMT_NF4>(plain, x_perm, offsets, rows, save_gu, save_xa, dy_perm,
-                                      dx_perm, dA, dB, dgu, tbuf, bt_ws, le, s);
-  }
+  if (ex.format == MOE4_FMT_NF4_DQ)
+    // both absmax levels decoded per k-tile inside the dgrad kernels
+    return backward_fmt<MOE4_FMT_NF4_DQ>(ex, x_perm, offsets, rows, save_gu, save_xa, dy_perm,
+                                         dx_perm, dA, dB, dgu, tbuf, bt_ws, le, s);
   if (ex.format == MOE4_FMT_NF4)
     return backward_fmt<MOE4_FMT_NF4>(ex, x_perm, offsets, rows, save_gu, save_xa, dy_perm,
                                       dx_perm, dA, dB, dgu, tbuf, bt_ws, le, s);

@@ -335,8 +335,8 @@ void k_skinny(const GemmArgs a) {
   constexpr int KB = F::kBlock;
   // NF4 byte -> two fp32 levels; the absmax code book of a double-quantised stack
   __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
-  __shared__ float dqbook[DQ ? 256 : 1];
-  __shared__ float a2tab[DQ ? 32 * kSkNc : 1];
+  __shared__ __attribute__((aligned(16))) float dqbook[DQ ? 256 : 1];
+  __shared__ __attribute__((aligned(16))) float a2tab[DQ ? 32 * kSkNc : 1];
   constexpr int NROW = 16 * kSkNc;   // weight rows of the workgroup
   // [NROW rows][pitch] staged scales (rounded up to 256 bytes), then
   // [S][MAXR][kSkNc][256] partial sums
@@ -394,16 +394,27 @@ void k_skinny(const GemmArgs a) {
             0);
     }
   };
-  if constexpr (DQ) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) dqbook[i] = a.dqbook[i];
-    for (int t = threadIdx.x; t < NROW; t += blockDim.x) {
-      // group scales of the workgroup's weight rows (row (c, n) = t = 16 c + n)
-      const int64_t ng = ((int64_t)a.E * Nw * (K / KB) + 255) / 256;
-      const int64_t g0 = (((int64_t)e * Nw + wrow(t)) * (K / KB)) >> 8;
-      a2tab[2 * t] = g0 < ng ? a.ws2[g0] : 0.0f;   // rows past Nw: unused
-      a2tab[2 * t + 1] = g0 + 1 < ng ? a.ws2[g0 + 1] : 0.0f;
+  // double-quantised NF4: the code book (1 KiB) and the group scales of the
+  // workgroup's weight rows, a2tab[2 t + h] = group h of row t = 16 c + n (zero
+  // past the last group), by direct loads into LDS as well
+  auto dq_issue = [&]() {
+    if constexpr (DQ) {
+      const rsrc_t rb = make_rsrc(a.dqbook, 256 * sizeof(float));
+      for (int q = w; q < 4; q += S)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, MOE4_LDS(reinterpret_cast<uint8_t*>(dqbook) + 256 * q), 4, 256 * q + 4 * l, 0, 0,
+            0);
+      static_assert(2 * NROW == 64, "one 64-lane load covers a2tab");
+      if (w == S - 1) {
+        const int64_t ng = ((int64_t)a.E * Nw * (K / KB) + 255) / 256;
+        const int64_t g =
+            ((((int64_t)e * Nw + wrow(l >> 1)) * (K / KB)) >> 8) + (l & 1);
+        const rsrc_t r2 = make_rsrc(a.ws2, (uint32_t)(ng * 4));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r2, MOE4_LDS(a2tab), 4,
+                                                 g < ng ? (int)g * 4 : kOob, 0, 0, 0);
+      }
     }
-  }
+  };
   SkinnyDq dq{dqbook, a2tab, DQ ? a.dqoff[0] : 0.0f};
   const int nl = l & 15, g = l >> 4;
   SkinnyLane sl;
@@ -451,6 +462,7 @@ void k_skinny(const GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         stage_issue(0);
         lut_issue();
+        dq_issue();
         wait_vmcnt<0>();
         lds_barrier();
       }
@@ -530,7 +542,8 @@ constexpr int kMaxRowTiles = kBM / 32;
 // One LDS stage holds a k-tile of 64: the A tile [kBM rows][128 B] with the
 // 16-byte chunks of row r stored at chunk ^ ((r >> 1) & 7), each wave's packed
 // nibbles [32 rows][32 B], and each wave's
-// scales in 4-byte slots (NF4: slot n = row n's fp32 absmax; MXFP4: slot
+// scales in 4-byte slots (NF4: slot n = row n's fp32 absmax; double-quantised
+// NF4: slot n = row n's absmax code byte; MXFP4: slot
 // 32 h + n = the e8m0 byte of half h of row n; sub-dword loads to LDS advance
 // 4 bytes a lane).
 // The LDS has 64 four-byte banks: a 16-byte operand read serves 16 lanes
@@ -547,13 +560,17 @@ static_assert(kTiledLds + 256 * 8 <= 160 * 1024, "tiled kernel LDS");
 template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   using F = Format<FMT>;
-  constexpr bool NF4 = FMT == MOE4_FMT_NF4;
+  constexpr bool NF4 = FMT != MOE4_FMT_MXFP4;   // NF4 levels (plain or double-quantised)
+  constexpr bool DQ = FMT == MOE4_FMT_NF4_DQ;
   constexpr int KB = F::kBlock;
   constexpr int kLoadsPerTile = kBM / 64 + 1 + 1;
   __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
+  // double-quantised NF4: the absmax code book
+  __shared__ float dqbook[DQ ? 256 : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t stage_mem[];
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   if (NF4 && tid < 256) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
+  if (DQ && tid < 256) dqbook[tid] = a.dqbook[tid];
   int e, ut, cg;
   locate_tile_sorted<kBM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
   // wave-uniform by construction; make it visible to the compiler so that the
@@ -590,7 +607,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
 
   const rsrc_t ra = make_rsrc(a.A + (int64_t)row0 * K, (uint32_t)nrows * K * 2);
   const rsrc_t rq = make_rsrc(a.wq + (int64_t)e * Nw * (K / 2), (uint32_t)Nw * (K / 2));
-  constexpr int sbytes = NF4 ? 4 : 1;
+  constexpr int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
   const rsrc_t rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Nw * (K / KB) * sbytes,
                               (uint32_t)Nw * (K / KB) * sbytes);
 
@@ -609,6 +626,22 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   bool s_on;
   const int s_row = wrow_of(n32, s_on);
   const int s_off = s_row * (K / KB) * sbytes;
+  // double-quantised NF4: absmax = fp32(fp32(book[code] * absmax2) + offset),
+  // absmax2 one per 256 absmax of the stack; a row of at most 256 blocks lies
+  // in at most two such groups, the second from k-tile a2bnd on (k-tiles are
+  // blocks)
+  float a2lo = 0.0f, a2hi = 0.0f, dqoff = 0.0f;
+  int a2bnd = 0;
+  if constexpr (DQ) {
+    const int64_t nb = K / KB;
+    const int64_t f0 = ((int64_t)e * Nw + s_row) * nb;
+    const int64_t ng = ((int64_t)a.E * Nw * nb + 255) / 256;
+    const int64_t g0 = f0 >> 8;
+    a2bnd = 256 - (int)(f0 & 255);
+    a2lo = g0 < ng ? a.ws2[g0] : 0.0f;
+    a2hi = g0 + 1 < ng ? a.ws2[g0 + 1] : 0.0f;
+    dqoff = a.dqoff[0];
+  }
 
   auto stage = [&](int st) { return stage_mem + st * kStageBytes; };
   // Batch j holds the A tile of k-tile j and the wave's weights of k-tile
@@ -622,10 +655,13 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
         rq, MOE4_LDS(base + kStageA + w * 1024), 16,
         (b_on && kb + 32 * (l & 1) < K) ? b_off + kb / 2 : kOob, 0, 0, 0);
     uint8_t* sbase = base + kStageA + kStageB + w * 256;
-    if (NF4) {
+    if (FMT == MOE4_FMT_NF4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, MOE4_LDS(sbase), 4, (s_on && h == 0 && kb < K) ? s_off + (kb / 64) * 4 : kOob, 0,
           0, 0);
+    } else if (DQ) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, MOE4_LDS(sbase), 1, (s_on && h == 0 && kb < K) ? s_off + kb / 64 : kOob, 0, 0, 0);
     } else {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, MOE4_LDS(sbase), 1, (s_on && kb + 32 * h < K) ? s_off + kb / 32 + h : kOob, 0, 0,
@@ -649,15 +685,23 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
     for (int j = 0; j < kParts; ++j) issue_part(kt, j);
   };
   // this lane's raw nibbles (k 32h .. 32h+31 of row n32) and scale of the
-  // weights in stage st (LDS reads through vector types: see dequant8)
-  auto read_b = [&](int st, u32x4& braw, float& sc) {
+  // weights of k-tile kt in stage st (LDS reads through vector types: see
+  // dequant8)
+  auto read_b = [&](int st, int kt, u32x4& braw, float& sc) {
     const uint8_t* base = stage(st);
     braw = *reinterpret_cast<const u32x4*>(base + kStageA + w * 1024 + n32 * 32 + 16 * h);
     const f32x2* Sw = reinterpret_cast<const f32x2*>(base + kStageA + kStageB + w * 256);
     const int slot = NF4 ? n32 : h * 32 + n32;
     const f32x2 pr = Sw[slot >> 1];
     const float raw = (slot & 1) ? pr.y : pr.x;
-    sc = NF4 ? raw : __uint_as_float((__float_as_uint(raw) & 255u) << 23);
+    if constexpr (FMT == MOE4_FMT_NF4) {
+      sc = raw;
+    } else if constexpr (DQ) {
+      // a one-byte load fills the low byte of its 4-byte slot
+      sc = mul_then_add(dqbook[__float_as_uint(raw) & 255u], kt < a2bnd ? a2lo : a2hi, dqoff);
+    } else {
+      sc = __uint_as_float((__float_as_uint(raw) & 255u) << 23);
+    }
   };
 
   const int nk = (K + kBK - 1) / kBK;
@@ -733,7 +777,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
     }
     if (nk > 1) wait_vmcnt<2 * kLoadsPerTile>();
     else wait_vmcnt<kLoadsPerTile>();
-    read_b(0, braw, sc);   // the wave's own loads: no barrier needed
+    read_b(0, 0, braw, sc);   // the wave's own loads: no barrier needed
 #pragma unroll
     for (int p = 0; p < 3; ++p) bq[p] = dequant8<FMT>(braw[p], sc, lutf);
     fetch8<FMT>(braw[3], lutf, lv);
@@ -750,7 +794,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
       const uint16_t* As = reinterpret_cast<const uint16_t*>(stage(kt % kStages));
       // after the last k-tile the B area holds zeros or stale nibbles:
       // decoded and never used
-      read_b((kt + 1) % kStages, braw_n, sc_n);
+      read_b((kt + 1) % kStages, kt + 1, braw_n, sc_n);
       bf16x8 ring[kPre];
 #pragma unroll
       for (int f = 0; f < kPre; ++f)
@@ -982,30 +1026,32 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
     le.after(1, s);
     return err;
   }
-  if constexpr (FMT == MOE4_FMT_NF4_DQ) {
-    return hipErrorInvalidValue;   // the tiled kernels take the expanded (plain NF4) view
-  } else {
-    // row tiles: at most rows / kBM + (one per touched expert)
-    const int ntiles = rows / kBM + touched;
-    g.ncg = (I + 127) / 128;
-    d.ncg = (H + kBN - 1) / kBN;
-    le.before(0, s);
-    err = run_tiled<FMT, true>(g, ntiles, s);
-    le.after(0, s);
-    if (err != hipSuccess) return err;
-    le.before(1, s);
-    err = run_tiled<FMT, false>(d, ntiles, s);
-    le.after(1, s);
-    return err;
-  }
+  // row tiles: at most rows / kBM + (one per touched expert)
+  const int ntiles = rows / kBM + touched;
+  g.ncg = (I + 127) / 128;
+  d.ncg = (H + kBN - 1) / kBN;
+  le.before(0, s);
+  err = run_tiled<FMT, true>(g, ntiles, s);
+  le.after(0, s);
+  if (err != hipSuccess) return err;
+  le.before(1, s);
+  err = run_tiled<FMT, false>(d, ntiles, s);
+  le.after(1, s);
+  return err;
 }
 
 }  // namespace
 
+// double-quantised absmax decoded inside the kernels: every weight row spans at
+// most 256 absmax (two groups of the second level); else expanded first
+static bool dq_in_kernel(const moe4_experts& ex) {
+  return ex.format == MOE4_FMT_NF4_DQ && ex.H / 64 <= 256 && ex.I / 64 <= 256;
+}
+
 size_t forward_ws_bytes(const moe4_experts& ex, int rows) {
   size_t b = align_up((size_t)rows * ex.I * sizeof(uint16_t), 256);
   if (ex.lora_A) b += align_up((size_t)rows * ex.lora_r * sizeof(float), 256);
-  return b + dq_expand_bytes(ex);
+  return b + (dq_in_kernel(ex) ? 0 : dq_expand_bytes(ex));
 }
 
 int choose_variant(const moe4_experts& ex, int rows) {
@@ -1033,10 +1079,10 @@ hipError_t launch_expert_forward(const moe4_experts& ex, const uint16_t* x_perm,
     if (err != hipSuccess) return err;
   }
   if (ex.format == MOE4_FMT_NF4_DQ) {
-    // decode-sized (rows of at most 256 absmax, i.e. K <= 16384): both absmax
-    // levels decoded inside the kernel; otherwise expand the absmax once into
-    // the workspace, then the plain NF4 kernels
-    if (*variant == MOE4_VARIANT_SKINNY && ex.H / 64 <= 256 && ex.I / 64 <= 256)
+    // rows of at most 256 absmax (K <= 16384): both absmax levels decoded
+    // inside the kernels; otherwise expand the absmax once into the workspace,
+    // then the plain NF4 kernels
+    if (dq_in_kernel(ex))
       return forward_fmt<MOE4_FMT_NF4_DQ>(ex, x_perm, offsets, rows, y_perm, save_gu, xa, hbuf,
                                           *variant, le, s);
     moe4_experts plain;

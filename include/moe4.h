@@ -88,10 +88,10 @@ enum { MOE4_VARIANT_AUTO = 0, MOE4_VARIANT_SKINNY = 1, MOE4_VARIANT_TILED = 2 };
  *   codes; gu_s2 / dn_s2 f32 [ceil(n/256)] absmax2 and gu_soff / dn_soff f32
  *   [1] offset of each stack (n = its number of absmax); dq_book f32 [256].
  *   absmax = fp32(fp32(dq_book[code] * absmax2[i / 256]) + offset), i the
- *   flat absmax index in the stack. The decode-sized kernel decodes both
- *   levels in place; the prefill-sized kernel and the backward expand the
- *   absmax into the workspace first (the workspace grows by the two fp32
- *   absmax arrays).
+ *   flat absmax index in the stack. The kernels decode both levels in
+ *   place; only a forward whose weight rows hold more than 256 absmax (H or
+ *   I above 16384) expands the absmax into the workspace first (its
+ *   workspace then grows by the two fp32 absmax arrays).
  * MXFP4 (OCP MX: e2m1 nibbles, 32 per block, one e8m0 scale per block; even
  * element in the low nibble; w = e2m1(n) * 2^(scale - 127)):
  *   gu_q u8 [E, 2I, H/32, 16]   gu_s u8 [E, 2I, H/32]
