@@ -262,8 +262,15 @@ def test_layer_forward_double_quant(spec, T, kind, variant):
     assert_close(res["out32"].cpu().numpy(), ref["out"], "out")
 
 
-def test_layer_backward_double_quant():
-    spec, T = LORA_SMALL, 150
+# rows of 5 and 3 absmax: the 256-absmax groups of the second level begin
+# inside weight rows and inside dgrad k-tiles
+DQ_LORA_ODD = inp.QWEN3_30B_NF4_LORA.scaled(name="lora_dq_odd_rows", seed_id=142, E=8, k=2, H=320,
+                                            I=192, tokens=(90,))
+
+
+@pytest.mark.parametrize("spec,T", [(LORA_SMALL, 150), (DQ_LORA_ODD, 90)],
+                         ids=["lora_small-T150", "lora_dq_odd_rows-T90"])
+def test_layer_backward_double_quant(spec, T):
     say(f"backward, double-quantised absmax: {spec.name} T={T}")
     D = DQLayer(spec)
     ex = D.device()

@@ -74,9 +74,9 @@ def test_noalloc_forward_matches_workspace_forward(spec):
             assert_close(na_out[0].cpu().numpy(), ref["y"], "y_perm (no allocation)")
 
 
-def test_noalloc_forward_double_quant_expands_into_scratch():
-    """The prefill-sized path of a double-quantised stack expands both absmax
-    arrays into the scratch before the GEMMs."""
+def test_noalloc_forward_double_quant_tiled():
+    """A double-quantised stack on the prefill-sized kernel (both absmax levels
+    decoded per k-tile) gives the workspace entry point's results bit for bit."""
     from tests.test_gpu_parity import DQLayer, QWEN_SMALL
     D = DQLayer(QWEN_SMALL)
     for T in (100, 5):
