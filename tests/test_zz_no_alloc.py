@@ -2,9 +2,9 @@
 C ABI: the same outputs bit for bit (both run the same kernels; the scratch
 only replaces the caller's workspace), on two calls in a row, the second with
 a smaller input, on every kernel path that uses scratch (bf16 h for both
-families, the adapter projection, the expanded absmax of a double-quantised
-stack); and the calls that need more scratch than the library holds are
-refused before anything runs."""
+families, the adapter projection, a double-quantised stack); and the calls
+that need more scratch than the library holds are refused before anything
+runs."""
 import numpy as np
 import pytest
 import torch
