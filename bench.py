@@ -156,7 +156,7 @@ def expert_bytes(spec):
 
 
 class Step:
-    """Buffers for one (workload, T) and the four calls of one step."""
+    """Buffers for one (workload, T) and the calls of one step."""
 
     def __init__(self, moe4, torch, spec, T, ex, backward=False):
         self.moe4, self.torch, self.spec, self.T = moe4, torch, spec, T
@@ -189,9 +189,9 @@ class Step:
 
     def forward(self, ex, x, logits):
         m = self.moe4
-        m.moe4_route(logits, self.spec.k, self.idx, self.w)
-        m.moe4_permute(self.idx, self.spec.E, self.offsets, self.sor, self.ros, x=x,
-                       x_perm=self.x_perm, ws=self.ws)
+        # route + permute + gather (one launch for a decode-sized batch)
+        m.moe4_route_permute(logits, self.spec.k, self.idx, self.w, self.offsets, self.sor,
+                             self.ros, x=x, x_perm=self.x_perm, ws=self.ws)
         if self.backward:
             m.moe4_expert_forward(ex, self.x_perm, self.offsets, self.y_perm, save_gu=self.save_gu,
                                   save_xa=self.save_xa, ws=self.ws)

@@ -61,6 +61,11 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
                           int32_t* slot_of_row, int32_t* row_of_slot, const uint16_t* x,
                           const float* row_scale, int H, uint16_t* x_perm, void* ws,
                           hipStream_t s);
+// route + permute (+ gather): one launch for small batches, else the two above
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int renorm,
+                                int32_t* idx, float* w, int32_t* offsets, int32_t* slot_of_row,
+                                int32_t* row_of_slot, const uint16_t* x, int H,
+                                uint16_t* x_perm, void* ws, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_combine(const float* y, const int32_t* row_of_slot, const float* w, int T,
                           int k, int H, void* out, bool out_f32, hipStream_t s);

@@ -385,6 +385,43 @@ int moe4_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32
                   "moe4_permute");
 }
 
+int moe4_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
+                       int32_t renormalize, int32_t* topk_idx, float* topk_w, int32_t* offsets,
+                       int32_t* slot_of_row, int32_t* row_of_slot, const uint16_t* x, int32_t H,
+                       uint16_t* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (E < 1 || E > 1024) return fail(MOE4_ESHAPE, "E = %d outside [1, 1024]", E);
+  if (k < 1 || k > E) return fail(MOE4_ESHAPE, "k = %d outside [1, E = %d]", k, E);
+  if (T < 0 || (int64_t)T * k >= ((int64_t)1 << 31))
+    return fail(MOE4_ESHAPE, "T = %d: need T >= 0 and T*k < 2^31", T);
+  REQUIRE_PTR(offsets, "offsets");
+  if (T > 0) {
+    REQUIRE_PTR(logits, "logits");
+    REQUIRE_PTR(topk_idx, "topk_idx");
+    REQUIRE_PTR(topk_w, "topk_w");
+    REQUIRE_PTR(slot_of_row, "slot_of_row");
+    REQUIRE_PTR(row_of_slot, "row_of_slot");
+    REQUIRE_ALIGN(logits, 4, "logits");
+    REQUIRE_ALIGN(topk_idx, 4, "topk_idx");
+    REQUIRE_ALIGN(topk_w, 4, "topk_w");
+  }
+  if (x != nullptr) {
+    if (H <= 0 || H % 8) return fail(MOE4_ESHAPE, "H = %d must be a positive multiple of 8", H);
+    if (T > 0) REQUIRE_PTR(x_perm, "x_perm");
+    REQUIRE_ALIGN(x, 16, "x");
+    REQUIRE_ALIGN(x_perm, 16, "x_perm");
+  }
+  const size_t need = moe4::permute_ws_bytes(T, k, E);
+  int rc = check_ws(ws, ws_bytes, need, "moe4_route_permute");
+  if (rc) return rc;
+  if (T == 0)
+    return launched(moe4::launch_zero_i32(offsets, E + 1, (hipStream_t)stream),
+                    "moe4_route_permute");
+  return launched(moe4::launch_route_permute(logits, T, E, k, renormalize != 0, topk_idx, topk_w,
+                                             offsets, slot_of_row, row_of_slot, x, H, x_perm, ws,
+                                             (hipStream_t)stream),
+                  "moe4_route_permute");
+}
+
 }  // extern "C"
 
 namespace {

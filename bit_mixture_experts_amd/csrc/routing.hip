@@ -19,15 +19,13 @@ __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// One wave per token; lane l holds experts l, l+64, ... (NPL per lane).
+// Routing of one token by one wave; lane l holds experts l, l+64, ... (NPL
+// per lane). The k chosen experts and their weights go to idx[0..k) and
+// w[0..k) (device or LDS memory).
 template <int NPL>
-__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E,
-                                               int k, int renorm, int32_t* __restrict__ idx,
-                                               float* __restrict__ wout) {
-  const int t = (int)((blockIdx.x * (unsigned)blockDim.x + threadIdx.x) >> 6);
-  if (t >= T) return;
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k,
+                                            int renorm, int32_t* idx, float* wout) {
   const int l = lane_id();
-  const float* row = logits + (int64_t)t * E;
   float v[NPL];
   float selv[NPL];
   uint32_t taken = 0, valid = 0;
@@ -70,7 +68,7 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 #pragma unroll
       for (int i = 0; i < NPL; ++i)
         if (i == j / kWave) selv[i] = bv;
-      idx[(int64_t)t * k + j] = be;
+      idx[j] = be;
     }
   }
   // weights: exp(v - top) normalised over the selection or over all experts
@@ -88,8 +86,19 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int j = l + kWave * i;
-    if (j < k) wout[(int64_t)t * k + j] = expf(selv[i] - top) / denom;
+    if (j < k) wout[j] = expf(selv[i] - top) / denom;
   }
+}
+
+// One wave per token.
+template <int NPL>
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E,
+                                               int k, int renorm, int32_t* __restrict__ idx,
+                                               float* __restrict__ wout) {
+  const int t = (int)((blockIdx.x * (unsigned)blockDim.x + threadIdx.x) >> 6);
+  if (t >= T) return;
+  route_token<NPL>(logits + (int64_t)t * E, E, k, renorm, idx + (int64_t)t * k,
+                   wout + (int64_t)t * k);
 }
 
 // --------------------------------------------------------------- permutation
@@ -198,13 +207,13 @@ __device__ __forceinline__ void copy_row(const uint16_t* __restrict__ x, int src
 
 // Small problems: every workgroup recomputes the whole permutation in LDS (it
 // is at most kSmallSlots slots), workgroup 0 writes the index arrays, and each
-// workgroup gathers its share of rows. One launch.
-__global__ __launch_bounds__(kChunk) void k_permute_small(
-    const int32_t* __restrict__ idx, int S, int k, int E, int32_t* __restrict__ offsets,
+// workgroup gathers its share of rows. One launch. `idx` is device or LDS
+// memory; `lds` holds (6 E + 1 + kSmallSlots + 256) ints.
+__device__ __forceinline__ void permute_small(
+    const int32_t* idx, int S, int k, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ slot_of_row, int32_t* __restrict__ row_of_slot,
     const uint16_t* __restrict__ x, const float* __restrict__ row_scale, int H,
-    uint16_t* __restrict__ x_perm, int rows_per_wg) {
-  extern __shared__ int lds[];
+    uint16_t* __restrict__ x_perm, int rows_per_wg, int* lds) {
   int* cnt = lds;                 // [E]
   int* run = cnt + E;             // [E+1]
   int* wcnt = run + E + 1;        // [4][E]
@@ -251,6 +260,46 @@ __global__ __launch_bounds__(kChunk) void k_permute_small(
     const int s = sor[r];
     copy_row(x, s / k, H, row_scale, s, x_perm + (int64_t)r * H);
   }
+}
+
+__global__ __launch_bounds__(kChunk) void k_permute_small(
+    const int32_t* __restrict__ idx, int S, int k, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot_of_row, int32_t* __restrict__ row_of_slot,
+    const uint16_t* __restrict__ x, const float* __restrict__ row_scale, int H,
+    uint16_t* __restrict__ x_perm, int rows_per_wg) {
+  extern __shared__ int lds[];
+  permute_small(idx, S, k, E, offsets, slot_of_row, row_of_slot, x, row_scale, H, x_perm,
+                rows_per_wg, lds);
+}
+
+// Routing and permutation of a small batch in one launch: every workgroup
+// routes all T tokens into LDS (its waves take the tokens in turn), workgroup
+// 0 writes the routing arrays, then the permutation and gather proceed as in
+// k_permute_small from the LDS copy of the chosen experts.
+// tokens up to which routing is fused: one per wave (with more, each wave
+// routes several tokens in turn, and a batch of 16 measured slower fused)
+constexpr int kFusedTokens = kChunk / kWave;
+template <int NPL>
+__global__ __launch_bounds__(kChunk) void k_route_permute_small(
+    const float* __restrict__ logits, int T, int E, int k, int renorm,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot_of_row, int32_t* __restrict__ row_of_slot,
+    const uint16_t* __restrict__ x, int H, uint16_t* __restrict__ x_perm, int rows_per_wg) {
+  extern __shared__ int lds[];
+  int32_t* sidx = lds;                                        // [kSmallSlots]
+  float* sw = reinterpret_cast<float*>(lds + kSmallSlots);    // [kSmallSlots]
+  const int S = T * k;
+  for (int t = wave_id(); t < T; t += kChunk / kWave)
+    route_token<NPL>(logits + (int64_t)t * E, E, k, renorm, sidx + t * k, sw + t * k);
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int s = threadIdx.x; s < S; s += kChunk) {
+      idx_out[s] = sidx[s];
+      w_out[s] = sw[s];
+    }
+  }
+  permute_small(sidx, S, k, E, offsets, slot_of_row, row_of_slot, x, nullptr, H, x_perm,
+                rows_per_wg, lds + 2 * kSmallSlots);
 }
 
 // Large problems, pass 1: per-chunk expert counts, counts[c * E + e], one
@@ -465,6 +514,40 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
     hipLaunchKernelGGL(k_gather, dim3((S + 3) / 4), dim3(256), 0, s, x, S, k, H, slot_of_row,
                        row_scale, x_perm);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int renorm,
+                                int32_t* idx, float* w, int32_t* offsets, int32_t* slot_of_row,
+                                int32_t* row_of_slot, const uint16_t* x, int H,
+                                uint16_t* x_perm, void* ws, hipStream_t s) {
+  const int S = T * k;
+  if (S > kSmallSlots || T > kFusedTokens) {
+    hipError_t err = launch_route(logits, T, E, k, renorm, idx, w, s);
+    if (err != hipSuccess) return err;
+    return launch_permute(idx, T, k, E, offsets, slot_of_row, row_of_slot, x, nullptr, H, x_perm,
+                          ws, s);
+  }
+  const int rows_per_wg = x ? max(4, (S + 255) / 256) : max(S, 1);
+  const int grid = x ? max(1, (S + rows_per_wg - 1) / rows_per_wg) : 1;
+  const size_t lds =
+      (size_t)(2 * kSmallSlots + E + (E + 1) + 4 * E + kSmallSlots + 256) * sizeof(int);
+  const dim3 g(grid), b(kChunk);
+  if (E <= 64)
+    hipLaunchKernelGGL(k_route_permute_small<1>, g, b, lds, s, logits, T, E, k, renorm, idx, w,
+                       offsets, slot_of_row, row_of_slot, x, H, x_perm, rows_per_wg);
+  else if (E <= 128)
+    hipLaunchKernelGGL(k_route_permute_small<2>, g, b, lds, s, logits, T, E, k, renorm, idx, w,
+                       offsets, slot_of_row, row_of_slot, x, H, x_perm, rows_per_wg);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_route_permute_small<4>, g, b, lds, s, logits, T, E, k, renorm, idx, w,
+                       offsets, slot_of_row, row_of_slot, x, H, x_perm, rows_per_wg);
+  else if (E <= 512)
+    hipLaunchKernelGGL(k_route_permute_small<8>, g, b, lds, s, logits, T, E, k, renorm, idx, w,
+                       offsets, slot_of_row, row_of_slot, x, H, x_perm, rows_per_wg);
+  else
+    hipLaunchKernelGGL(k_route_permute_small<16>, g, b, lds, s, logits, T, E, k, renorm, idx, w,
+                       offsets, slot_of_row, row_of_slot, x, H, x_perm, rows_per_wg);
   return hipGetLastError();
 }
 

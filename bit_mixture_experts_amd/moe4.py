@@ -36,7 +36,7 @@ MOE4_NOALLOC_SCRATCH_BYTES = 16 << 20
 EXPORTS = ("moe4_quantize_nf4", "moe4_compress_absmax", "moe4_expand_absmax",
            "moe4_decode_mxfp4", "moe4_convert_mxfp4_nf4",
            "moe4_router_logits", "moe4_route", "moe4_route_backward", "moe4_permute",
-           "moe4_expert_forward", "moe4_expert_forward_noalloc", "moe4_combine",
+           "moe4_route_permute", "moe4_expert_forward", "moe4_expert_forward_noalloc", "moe4_combine",
            "moe4_expert_backward",
            "moe4_workspace_size", "moe4_set_timing_events", "moe4_last_error",
            "moe4_last_variant")
@@ -74,6 +74,8 @@ _SIGS = {
                              _vp, _vp], ctypes.c_int),
     "moe4_permute": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
                      ctypes.c_int),
+    "moe4_route_permute": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                            _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe4_expert_forward": ([_P, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe4_expert_forward_noalloc": ([_P, _vp, _vp, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe4_combine": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp], ctypes.c_int),
@@ -263,6 +265,21 @@ def moe4_permute(topk_idx, E, offsets, slot_of_row, row_of_slot, x=None, row_sca
                              _ptr(x_perm, _BF16, "x_perm"), _ptr(ws, None, "ws"),
                              0 if ws is None else ws.numel() * ws.element_size(),
                              _stream(stream)))
+
+
+def moe4_route_permute(logits, k, topk_idx, topk_w, offsets, slot_of_row, row_of_slot, x=None,
+                       x_perm=None, ws=None, renormalize=True, stream=None):
+    """moe4_route then moe4_permute (no row_scale), one launch for small batches."""
+    T, E = logits.shape
+    H = 0 if x is None else x.shape[1]
+    _check(_lib.moe4_route_permute(_ptr(logits, _F32, "logits"), T, E, k, int(bool(renormalize)),
+                                   _ptr(topk_idx, _I32, "topk_idx"), _ptr(topk_w, _F32, "topk_w"),
+                                   _ptr(offsets, _I32, "offsets"),
+                                   _ptr(slot_of_row, _I32, "slot_of_row"),
+                                   _ptr(row_of_slot, _I32, "row_of_slot"), _ptr(x, _BF16, "x"), H,
+                                   _ptr(x_perm, _BF16, "x_perm"), _ptr(ws, None, "ws"),
+                                   0 if ws is None else ws.numel() * ws.element_size(),
+                                   _stream(stream)))
 
 
 def moe4_expert_forward(ex, x_perm, offsets, y_perm, save_gu=None, save_xa=None, ws=None,

@@ -286,6 +286,18 @@ int moe4_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe4_route followed by moe4_permute (without row_scale), in one launch when
+ * the batch is small (a decode step of at most 4 tokens),
+ * otherwise as the two calls [the passages of both]. Every output is bit for
+ * bit the two calls' output (same selection order, weights and stable
+ * permutation). Arguments as moe4_route and moe4_permute; ws as moe4_permute.
+ */
+int moe4_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
+                       int32_t renormalize, int32_t* topk_idx, float* topk_w, int32_t* offsets,
+                       int32_t* slot_of_row, int32_t* row_of_slot, const uint16_t* x, int32_t H,
+                       uint16_t* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Grouped expert forward over permuted rows [Solutions index, grouped-nf4-gemm
  * entries; QLoRA entry for the adapter]:
  *   gu = x_perm W_gu[e]^T + b_gu[e] + lora_scale * (x_perm A_e^T) B_e^T
@@ -308,8 +320,9 @@ int moe4_expert_forward(const moe4_experts* ex, const uint16_t* x_perm, const in
  * moe4_expert_forward without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid allocation): the same computation and kernels, with the scratch
- * memory (the bf16 activations h, the adapter projection xa, the expanded
- * absmax of a double-quantised stack) in a buffer of
+ * memory (the bf16 activations h, the adapter projection xa, and for weight
+ * rows of more than 256 absmax the expanded absmax of a double-quantised
+ * stack) in a buffer of
  * MOE4_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
  * until the process ends. Allocates nothing.
  *   A call that needs more scratch than that (moe4_workspace_size's forward

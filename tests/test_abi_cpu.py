@@ -121,6 +121,31 @@ def test_permute_refusals():
                             None) == moe4.MOE4_ESHAPE
 
 
+def test_route_permute_refusals():
+    rp = lib.moe4_route_permute
+    # E, k and T bounds; missing arrays; misaligned x; H not a multiple of 8;
+    # undersized workspace for a large batch; T = 0 needs only offsets
+    assert rp(FAKE, 4, 0, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, None, 0,
+              None) == moe4.MOE4_ESHAPE
+    assert rp(FAKE, 4, 8, 9, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, None, 0,
+              None) == moe4.MOE4_ESHAPE
+    assert rp(FAKE, -1, 8, 2, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, None, 0,
+              None) == moe4.MOE4_ESHAPE
+    assert rp(None, 4, 8, 2, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, None, 0,
+              None) == moe4.MOE4_EINVAL
+    assert "logits is NULL" in moe4.moe4_last_error()
+    assert rp(FAKE, 4, 8, 2, 1, FAKE, FAKE, None, FAKE, FAKE, None, 0, None, None, 0,
+              None) == moe4.MOE4_EINVAL
+    assert rp(FAKE, 4, 8, 2, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_MIS, 16, FAKE, None, 0,
+              None) == moe4.MOE4_EALIGN
+    assert rp(FAKE, 4, 8, 2, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 12, FAKE, None, 0,
+              None) == moe4.MOE4_ESHAPE
+    assert rp(FAKE, 4096, 128, 8, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2048, FAKE, FAKE, 16,
+              None) == moe4.MOE4_EWORKSPACE
+    assert rp(None, 0, 8, 2, 1, None, None, None, None, None, None, 0, None, None, 0,
+              None) == moe4.MOE4_EINVAL   # offsets are still written
+
+
 @pytest.mark.parametrize("field,value,code,msg", [
     ("format", 0, moe4.MOE4_EINVAL, "format unset"),
     ("format", 7, moe4.MOE4_EINVAL, "format unknown"),

@@ -459,6 +459,53 @@ def test_permute_bit_exact(T, E, k):
         assert np.array_equal(bits(xp), oracle.gather_rows(x, rs, k, row_scale=sc))
 
 
+# fused routing + permutation: batches of up to 4 tokens in one launch, the rest
+# through the two separate calls; ties, one expert, E up to 1024
+ROUTE_PERMUTE_CASES = [(1, 128, 8, "normal"), (4, 1024, 16, "ties"), (3, 1, 1, "normal"),
+                       (2, 300, 3, "zipf"), (4, 32, 32, "normal"), (5, 128, 8, "normal"),
+                       (16, 128, 8, "normal"), (64, 32, 4, "zipf"), (200, 64, 6, "ties")]
+
+
+@pytest.mark.parametrize("T,E,k,kind", ROUTE_PERMUTE_CASES)
+def test_route_permute_bit_exact(T, E, k, kind):
+    """moe4_route_permute gives every output of moe4_route + moe4_permute bit
+    for bit, and the oracle's indices, permutation and gathered rows."""
+    say(f"route + permute T={T} E={E} k={k} {kind}")
+    rng = np.random.default_rng(7000 + T * 31 + E + k)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if kind == "ties":
+        lg = rng.integers(-3, 3, (T, E)).astype(np.float32)
+    if kind == "zipf":
+        lg += -1.1 * np.log(1 + rng.permutation(E)).astype(np.float32)
+    H = 72
+    x = inp.to_bf16_bits(rng.standard_normal((T, H)))
+    S = T * k
+    for renorm in (True, False):
+        gi, gw = _route(lg, k, renorm)
+        off, sor, ros, xp = _permute(gi, E, x)
+        fi = torch.empty((T, k), dtype=torch.int32, device=DEV)
+        fw = torch.empty((T, k), dtype=torch.float32, device=DEV)
+        foff = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+        fsor = torch.empty(S, dtype=torch.int32, device=DEV)
+        fros = torch.empty(S, dtype=torch.int32, device=DEV)
+        fxp = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
+        ws = torch.empty(max(256, 4 * ((S + 2047) // 2048) * E + 256), dtype=torch.uint8,
+                         device=DEV)
+        moe4.moe4_route_permute(to_dev(lg), k, fi, fw, foff, fsor, fros, x=to_dev(x), x_perm=fxp,
+                                ws=ws, renormalize=renorm)
+        torch.cuda.synchronize()
+        assert np.array_equal(fi.cpu().numpy(), gi)
+        assert np.array_equal(fw.cpu().numpy().view(np.uint32), gw.view(np.uint32))
+        for a_, b_ in ((foff, off), (fsor, sor), (fros, ros)):
+            assert torch.equal(a_, b_)
+        assert np.array_equal(bits(fxp), bits(xp))
+        ri, _ = oracle.route(lg, k, renormalize=renorm)
+        ro, rs, _ = oracle.permute(ri, E)
+        assert np.array_equal(fi.cpu().numpy(), ri)
+        assert np.array_equal(foff.cpu().numpy(), ro) and np.array_equal(fsor.cpu().numpy(), rs)
+        assert np.array_equal(bits(fxp), oracle.gather_rows(x, rs, k))
+
+
 def test_permute_skewed_one_expert():
     say("permute: every slot on one expert")
     T, E, k = 2500, 64, 1
