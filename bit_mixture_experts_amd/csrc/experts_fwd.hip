@@ -404,14 +404,14 @@ void k_skinny(const GemmArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rb, MOE4_LDS(reinterpret_cast<uint8_t*>(dqbook) + 256 * q), 4, 256 * q + 4 * l, 0, 0,
             0);
-      static_assert(2 * NROW == 64, "one 64-lane load covers a2tab");
-      if (w == S - 1) {
-        const int64_t ng = ((int64_t)a.E * Nw * (K / KB) + 255) / 256;
-        const int64_t g =
-            ((((int64_t)e * Nw + wrow(l >> 1)) * (K / KB)) >> 8) + (l & 1);
-        const rsrc_t r2 = make_rsrc(a.ws2, (uint32_t)(ng * 4));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r2, MOE4_LDS(a2tab), 4,
-                                                 g < ng ? (int)g * 4 : kOob, 0, 0, 0);
+      static_assert((2 * NROW) % 64 == 0, "whole 64-lane loads cover a2tab");
+      const int64_t ng = ((int64_t)a.E * Nw * (K / KB) + 255) / 256;
+      const rsrc_t r2 = make_rsrc(a.ws2, (uint32_t)(ng * 4));
+      for (int q = S - 1 - w; q < 2 * NROW / 64; q += S) {
+        const int j = 64 * q + l;   // a2tab entry: group j % 2 of row j / 2
+        const int64_t g = ((((int64_t)e * Nw + wrow(j >> 1)) * (K / KB)) >> 8) + (j & 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r2, MOE4_LDS(reinterpret_cast<uint8_t*>(a2tab) + 256 * q),
+                                                 4, g < ng ? (int)g * 4 : kOob, 0, 0, 0);
       }
     }
   };
