@@ -378,7 +378,7 @@ def bench_stack(torch, hip, moe4, inputs, spec, T, exs, steps, warmup, seed):
     ms, pass_ms, _ = time_steps(torch, hip, moe4, steps, warmup, run)
     # the same pass captured once in a HIP graph and replayed: the library
     # launches on the current stream and allocates or synchronises nothing, so
-    # the 36 x 4 calls capture as they are and the host launch gaps disappear
+    # the calls of every layer capture as they are and the host launch gaps disappear
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
@@ -551,6 +551,10 @@ def device_state(torch=None, busy=None):
     ones."""
     import subprocess
     import threading
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        # under rocprofv3 its preloaded library would initialise the GPU in the
+        # rocm-smi child before that child starts its interpreter
+        return {"sampled": "not sampled (run under the profiler)"}
     got = {}
 
     def sample():
