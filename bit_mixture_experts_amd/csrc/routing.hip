@@ -400,22 +400,23 @@ __global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ x, 
 // ------------------------------------------------------------------ combine
 
 // out[t] = sum_j w[t,j] * y[row_of_slot[t*k+j]] over fp32 rows, accumulated
-// in fp32 in ascending j; stored as fp32 or rounded once to bf16. One wave per
-// (token, 256-column piece): lane l takes 4 consecutive columns, so every load
-// instruction reads 1 KiB of one y row contiguously, and a token's row is
-// spread over H / 256 waves (a decode-sized batch has few tokens: one wave per
-// token would walk its whole row in dependent round trips). The first kU rows
-// of the token have their loads in flight together; any further rows (k > kU)
-// follow one at a time.
+// in fp32 in ascending j; stored as fp32 or rounded once to bf16. wpt waves per
+// token; wave q of a token takes the 4-float chunks q * 64 + l, stepping by
+// wpt * 64 (lane l), so that every load instruction reads 1 KiB of one y row
+// contiguously. A large batch runs one wave per token (each wave walks its
+// row); a decode-sized batch spreads a token's row over up to H / 256 waves
+// (one wave per token would walk its row in dependent round trips). The first
+// kU rows of the token have their loads in flight together; any further rows
+// (k > kU) follow one at a time.
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const int32_t* __restrict__ row_of_slot,
                                                  const float* __restrict__ w, int T, int k,
-                                                 int H, int npiece, void* __restrict__ out) {
+                                                 int H, int wpt, void* __restrict__ out) {
   const int gw = (int)((blockIdx.x * (unsigned)blockDim.x + threadIdx.x) >> 6);
-  const int t = gw / npiece;
+  const int t = gw / wpt;
   if (t >= T) return;
-  const int c = (gw - t * npiece) * kWave + lane_id();   // 4-float chunk of the row
+  const int q = gw - t * wpt;
   const int nv = H / 4;
   constexpr int kU = 8;
   const int ku = min(k, kU);
@@ -429,26 +430,27 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
       wts[j] = w ? w[s] : 1.0f;
     }
   }
-  if (c >= nv) return;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  f32x4 v[kU];
+  for (int c = q * kWave + lane_id(); c < nv; c += wpt * kWave) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 v[kU];
 #pragma unroll
-  for (int j = 0; j < kU; ++j)
-    if (j < ku)
-      v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (int64_t)rows[j] * H) + c);
+    for (int j = 0; j < kU; ++j)
+      if (j < ku)
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (int64_t)rows[j] * H) + c);
 #pragma unroll
-  for (int j = 0; j < kU; ++j)
-    if (j < ku) acc += wts[j] * v[j];
-  for (int j = kU; j < k; ++j) {
-    const int64_t s = (int64_t)t * k + j;
-    const float wj = w ? w[s] : 1.0f;
-    acc += wj * reinterpret_cast<const f32x4*>(y + (int64_t)row_of_slot[s] * H)[c];
-  }
-  if (OUT_F32) {
-    reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)t * H)[c] = acc;
-  } else {
-    const uint2 o = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
-    reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (int64_t)t * H)[c] = o;
+    for (int j = 0; j < kU; ++j)
+      if (j < ku) acc += wts[j] * v[j];
+    for (int j = kU; j < k; ++j) {
+      const int64_t s = (int64_t)t * k + j;
+      const float wj = w ? w[s] : 1.0f;
+      acc += wj * reinterpret_cast<const f32x4*>(y + (int64_t)row_of_slot[s] * H)[c];
+    }
+    if (OUT_F32) {
+      reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)t * H)[c] = acc;
+    } else {
+      const uint2 o = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (int64_t)t * H)[c] = o;
+    }
   }
 }
 
@@ -554,15 +556,18 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int re
 hipError_t launch_combine(const float* y, const int32_t* row_of_slot, const float* w, int T,
                           int k, int H, void* out, bool out_f32, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int npiece = (H / 4 + kWave - 1) / kWave;   // waves per token
-  const int64_t waves = (int64_t)T * npiece;
+  // waves per token: enough waves for about 4096 in all, at most one per 256
+  // columns (a batch of 4096 tokens runs one wave per token)
+  const int npiece = (H / 4 + kWave - 1) / kWave;
+  const int wpt = max(1, min(npiece, 4096 / T));
+  const int64_t waves = (int64_t)T * wpt;
   const dim3 grid((unsigned)((waves + 3) / 4));
   if (out_f32)
-    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, y, row_of_slot, w, T, k, H,
-                       npiece, out);
+    hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, y, row_of_slot, w, T, k, H, wpt,
+                       out);
   else
-    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, s, y, row_of_slot, w, T, k, H,
-                       npiece, out);
+    hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, s, y, row_of_slot, w, T, k, H, wpt,
+                       out);
   return hipGetLastError();
 }
 
