@@ -291,6 +291,8 @@ def bench_layer(torch, hip, moe4, inputs, spec, T, exs, steps, warmup, seed):
         "workload": spec.name, "T": T, "steps": steps, "replicas": nrep,
         "ms_per_step": round(ms, 5), "step_ms": spread(step_ms, 5),
         "routed_tokens_per_s": round(T / (ms / 1e3), 1),
+        # the median step (robust to a host stall inside the timed region)
+        "routed_tokens_per_s_median": round(T / (pct(step_ms, 0.5) / 1e3), 1),
         "kernel": moe4.moe4_last_variant() == moe4.MOE4_VARIANT_SKINNY and "skinny" or "tiled",
         "gate_up_us": spread([v * 1e3 for v in k_gu], 2),
         "down_us": spread([v * 1e3 for v in k_dn], 2),
