@@ -189,8 +189,18 @@ class Step:
 
     def forward(self, ex, x, logits):
         m = self.moe4
+        k = self.spec.k
+        if not self.backward and self.T * k > 1024:
+            # a prefill-sized batch: the gate_up GEMM gathers its rows from x
+            # itself (no x_perm round trip through HBM, no gather launch)
+            m.moe4_route_permute(logits, k, self.idx, self.w, self.offsets, self.sor, self.ros,
+                                 ws=self.ws)
+            m.moe4_expert_forward_gather(ex, x, k, self.sor, self.offsets, self.y_perm,
+                                         ws=self.ws)
+            m.moe4_combine(self.y_perm, self.ros, self.w, self.out, k)
+            return
         # route + permute + gather (one launch for a decode-sized batch)
-        m.moe4_route_permute(logits, self.spec.k, self.idx, self.w, self.offsets, self.sor,
+        m.moe4_route_permute(logits, k, self.idx, self.w, self.offsets, self.sor,
                              self.ros, x=x, x_perm=self.x_perm, ws=self.ws)
         if self.backward:
             m.moe4_expert_forward(ex, self.x_perm, self.offsets, self.y_perm, save_gu=self.save_gu,

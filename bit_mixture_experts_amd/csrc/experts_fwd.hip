@@ -149,7 +149,7 @@ struct SkinnyBatch {
 struct SkinnyLane {
   rsrc_t rq, ra;        // this expert's nibbles; this row chunk's activations
   int qoff[kSkNc];      // byte offset of the lane's 16-byte column in weight row c, k = 0
-  int aoff;             // byte offset of the lane's activation operand in its row, k = 0
+  int aoff;             // byte offset of the lane's activation operand (its row, k = 8 g)
   int sb[kSkNc];        // LDS byte address of the first staged scale of weight row c
   int a2bnd[kSkNc];     // double-quantised NF4: the first block of weight row c that
                         // lies in the row's second absmax group
@@ -190,11 +190,11 @@ __device__ __forceinline__ void skinny_load(SkinnyBatch<NRT>& bt, const SkinnyLa
 #pragma unroll
       for (int st = 0; st < 4; ++st) bt.av[rt][st] = buf_load_b128(sl.ra, base + 64 * st);
     } else {
-      const int m = rt * 16 + nl;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int k = kb + 32 * st + 8 * g;
-        bt.av[rt][st] = buf_load_b128(sl.ra, (live && k < K) ? (m * K + k) * 2 : kOob);
+        bt.av[rt][st] =
+            buf_load_b128(sl.ra, (live && k < K) ? sl.aoff + (rt * 16 * K + kb + 32 * st) * 2 : kOob);
       }
     }
   }
@@ -324,7 +324,9 @@ __device__ __forceinline__ void skinny_body(SkinnyBatch<NRT> (&b)[kSkNb], const 
 // accumulator tile would cost the third wave).
 constexpr int kSkWavesPerEu = 3;
 constexpr int kSkMaxRowTiles = 1;
-template <int FMT, bool GATEUP>
+// GATHER (gate_up only): the activation rows are gathered from a.A through
+// a.arows (see GemmArgs) instead of read as consecutive rows.
+template <int FMT, bool GATEUP, bool GATHER = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kSkWavesPerEu)))
 void k_skinny(const GemmArgs a) {
   using F = Format<FMT>;
@@ -443,8 +445,15 @@ void k_skinny(const GemmArgs a) {
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int c = 0; c < kSkNc; ++c) acc[rt][c] = zero4;
-    sl.ra = make_rsrc(a.A + (int64_t)(rbeg + rc) * K, (uint32_t)max(nrows, 0) * K * 2);
-    sl.aoff = (nl * K + 8 * g) * 2;
+    if constexpr (GATHER) {
+      // the lane's row: row arows[.] / gk of A; rows past the chunk read past
+      // the resource (A has fewer than 2^29 / K rows, checked by the caller)
+      sl.ra = make_rsrc(a.A, (uint32_t)a.a_rows * K * 2);
+      sl.aoff = nl < nrows ? ((a.arows[rbeg + rc + nl] / a.gk) * K + 8 * g) * 2 : (1 << 30);
+    } else {
+      sl.ra = make_rsrc(a.A + (int64_t)(rbeg + rc) * K, (uint32_t)max(nrows, 0) * K * 2);
+      sl.aoff = (nl * K + 8 * g) * 2;
+    }
     SkinnyBatch<NRT> b[kSkNb];
     // chunk ch of K: its scales in the stage, then the wave's iterations
     auto chunk = [&](int ch, bool setup) {
@@ -557,7 +566,7 @@ constexpr int kStageBytes = kStageA + kStageB + kStageS;
 constexpr int kTiledLds = kStages * kStageBytes;
 static_assert(kTiledLds + 256 * 8 <= 160 * 1024, "tiled kernel LDS");
 
-template <int FMT, bool GATEUP>
+template <int FMT, bool GATEUP, bool GATHER>
 __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   using F = Format<FMT>;
   constexpr bool NF4 = FMT != MOE4_FMT_MXFP4;   // NF4 levels (plain or double-quantised)
@@ -605,7 +614,10 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
     return on ? c : 0;
   };
 
-  const rsrc_t ra = make_rsrc(a.A + (int64_t)row0 * K, (uint32_t)nrows * K * 2);
+  // (the conditional operator does not take buffer-resource operands)
+  rsrc_t ra;
+  if constexpr (GATHER) ra = make_rsrc(a.A, (uint32_t)a.a_rows * K * 2);
+  else ra = make_rsrc(a.A + (int64_t)row0 * K, (uint32_t)nrows * K * 2);
   const rsrc_t rq = make_rsrc(a.wq + (int64_t)e * Nw * (K / 2), (uint32_t)Nw * (K / 2));
   constexpr int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
   const rsrc_t rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Nw * (K / KB) * sbytes,
@@ -618,6 +630,18 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   //    rows, an offset passed in a scalar register)
   const int a_col = 8 * ((l & 7) ^ (((8 * w + (l >> 3)) >> 1) & 7));
   const int a_off = ((8 * w + (l >> 3)) * K + a_col) * 2;
+  // gathered activations: the byte offset of load p's row (row 64 p + 8 w + l / 8
+  // of the tile = row arows[.] / gk of A), or -1 past the tile's rows
+  // (a fixed size: an array of template-dependent size captured by the loader
+  // lambdas made the host-side instantiation fail silently)
+  int a_offg[kBM / 64];
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int p = 0; p < kBM / 64; ++p) {
+      const int r = 64 * p + 8 * w + (l >> 3);
+      a_offg[p] = r < nrows ? ((a.arows[row0 + r] / a.gk) * K + a_col) * 2 : -1;
+    }
+  }
   // B: lane l fills [l/2][16 (l%2)] of this wave's nibble block (row n = l/2,
   //    bytes 16 (l%2) of the k-tile's 32)
   bool b_on;
@@ -673,9 +697,15 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   auto issue_part = [&](int kt, int j) {
     if (j < kBM / 64) {
       const int kb = kt * kBK;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, MOE4_LDS(stage(kt % kStages) + j * 8192 + w * 1024), 16,
-          kb + a_col < K ? a_off + 2 * kb : kOob, j * 64 * K * 2, 0, 0);
+      if constexpr (GATHER) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, MOE4_LDS(stage(kt % kStages) + j * 8192 + w * 1024), 16,
+            (kb + a_col < K && a_offg[j] >= 0) ? a_offg[j] + 2 * kb : kOob, 0, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, MOE4_LDS(stage(kt % kStages) + j * 8192 + w * 1024), 16,
+            kb + a_col < K ? a_off + 2 * kb : kOob, j * 64 * K * 2, 0, 0);
+      }
     } else {
       issue_b(kt + 1, (kt + 1) % kStages);
     }
@@ -917,7 +947,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
 
 // nitems: touched experts (sets the K split); nchunks: a bound on the 16-row
 // chunks of all experts (sets the grid; the workgroups past the last chunk exit)
-template <int FMT, bool GATEUP>
+template <int FMT, bool GATEUP, bool GATHER = false>
 hipError_t run_skinny(const GemmArgs& a, int nitems, int nchunks, hipStream_t s) {
   const int nwg = nitems * a.ncg;
   if (nwg == 0) return hipSuccess;
@@ -935,33 +965,35 @@ hipError_t run_skinny(const GemmArgs& a, int nitems, int nchunks, hipStream_t s)
   const size_t lds =
       SS::lds_bytes(a.K, 16 * kSkNc) + (size_t)S * MAXR * kSkNc * 256 * sizeof(float);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_skinny<FMT, GATEUP>),
+      reinterpret_cast<const void*>(&k_skinny<FMT, GATEUP, GATHER>),
       hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)(SS::lds_bytes(SS::kKc, 16 * kSkNc) + 8 * MAXR * kSkNc * 256 * sizeof(float)));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_skinny<FMT, GATEUP>), dim3(nchunks * a.ncg), dim3(64 * S), lds, s, a);
+  hipLaunchKernelGGL((k_skinny<FMT, GATEUP, GATHER>), dim3(nchunks * a.ncg), dim3(64 * S), lds, s,
+                     a);
   return hipGetLastError();
 }
 
-template <int FMT, bool GATEUP>
+template <int FMT, bool GATEUP, bool GATHER = false>
 hipError_t run_tiled(const GemmArgs& a, int ntiles, hipStream_t s) {
   if (ntiles == 0) return hipSuccess;
   // ntiles bounds the row tiles; tile j of the largest-first order runs on
   // XCD j % 8, so every XCD needs ceil(tiles / 8) * ncg ids
   const int nwg = (ntiles + 7) * a.ncg;
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tiled<FMT, GATEUP>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tiled<FMT, GATEUP, GATHER>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kTiledLds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_tiled<FMT, GATEUP>), dim3(nwg), dim3(64 * kTiledWaves), kTiledLds, s,
-                     a);
+  hipLaunchKernelGGL((k_tiled<FMT, GATEUP, GATHER>), dim3(nwg), dim3(64 * kTiledWaves), kTiledLds,
+                     s, a);
   return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int32_t* offsets,
                        int rows, float* y_perm, float* save_gu, const float* xa,
-                       uint16_t* hbuf, int variant, const LaunchEvents& le, hipStream_t s) {
+                       uint16_t* hbuf, int variant, const GatherRows* ga,
+                       const LaunchEvents& le, hipStream_t s) {
   const int E = ex.E, H = ex.H, I = ex.I;
   GemmArgs g{};
   g.offsets = offsets;
@@ -978,6 +1010,13 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
   g.K = H;
   g.N_out = I;
   g.A = x_perm;
+  if (ga) {
+    // gate_up reads row slot_of_row[r] / k of x for its row r
+    g.A = ga->x;
+    g.arows = ga->slot_of_row;
+    g.gk = ga->k;
+    g.a_rows = ga->T;
+  }
   g.bias = ex.gu_bias;
   g.xa = xa;
   g.loraB = ex.lora_B;
@@ -993,6 +1032,7 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
   d.K = I;
   d.N_out = H;
   d.A = hbuf;
+  d.arows = nullptr;
   d.bias = ex.dn_bias;
   d.xa = nullptr;
   d.loraB = nullptr;
@@ -1018,7 +1058,8 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
     // touched expert
     const int nchunks = min(rows, rows / (16 * kSkMaxRowTiles) + touched);
     le.before(0, s);
-    err = run_skinny<FMT, true>(g, touched, nchunks, s);
+    err = ga ? run_skinny<FMT, true, true>(g, touched, nchunks, s)
+             : run_skinny<FMT, true>(g, touched, nchunks, s);
     le.after(0, s);
     if (err != hipSuccess) return err;
     le.before(1, s);
@@ -1031,7 +1072,7 @@ hipError_t forward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const int
   g.ncg = (I + 127) / 128;
   d.ncg = (H + kBN - 1) / kBN;
   le.before(0, s);
-  err = run_tiled<FMT, true>(g, ntiles, s);
+  err = ga ? run_tiled<FMT, true, true>(g, ntiles, s) : run_tiled<FMT, true>(g, ntiles, s);
   le.after(0, s);
   if (err != hipSuccess) return err;
   le.before(1, s);
@@ -1064,7 +1105,7 @@ int choose_variant(const moe4_experts& ex, int rows) {
 hipError_t launch_expert_forward(const moe4_experts& ex, const uint16_t* x_perm,
                                  const int32_t* offsets, int rows, float* y_perm,
                                  float* save_gu, float* save_xa, void* ws, int* variant,
-                                 const LaunchEvents& le, hipStream_t s) {
+                                 const LaunchEvents& le, hipStream_t s, const GatherRows* ga) {
   *variant = choose_variant(ex, rows);
   if (rows == 0) return hipSuccess;
   char* p = static_cast<char*>(ws);
@@ -1084,18 +1125,18 @@ hipError_t launch_expert_forward(const moe4_experts& ex, const uint16_t* x_perm,
     // then the plain NF4 kernels
     if (dq_in_kernel(ex))
       return forward_fmt<MOE4_FMT_NF4_DQ>(ex, x_perm, offsets, rows, y_perm, save_gu, xa, hbuf,
-                                          *variant, le, s);
+                                          *variant, ga, le, s);
     moe4_experts plain;
     hipError_t err = dq_expand_experts(ex, abs_ws, &plain, s);
     if (err != hipSuccess) return err;
     return forward_fmt<MOE4_FMT_NF4>(plain, x_perm, offsets, rows, y_perm, save_gu, xa, hbuf,
-                                     *variant, le, s);
+                                     *variant, ga, le, s);
   }
   if (ex.format == MOE4_FMT_NF4)
     return forward_fmt<MOE4_FMT_NF4>(ex, x_perm, offsets, rows, y_perm, save_gu, xa, hbuf,
-                                     *variant, le, s);
+                                     *variant, ga, le, s);
   return forward_fmt<MOE4_FMT_MXFP4>(ex, x_perm, offsets, rows, y_perm, save_gu, xa, hbuf,
-                                     *variant, le, s);
+                                     *variant, ga, le, s);
 }
 
 }  // namespace moe4

@@ -21,6 +21,10 @@ struct GemmArgs {
   int layout, act;
   float alpha, limit;
   const uint16_t* A;
+  // gathered activations (gate_up of moe4_expert_forward_gather): row r of the
+  // grouped GEMM is row arows[r] / gk of A, which has a_rows rows; null: row r
+  const int32_t* arows;
+  int gk, a_rows;
   const int32_t* offsets;
   int E, rows;
   const uint16_t* bias; // bf16 [E, Nw] or null

@@ -85,11 +85,21 @@ struct LaunchEvents {
   }
 };
 
-// returns the kernel family used through *variant
+// Activation rows gathered by the gate_up GEMM itself: row r of the grouped
+// GEMM is row slot_of_row[r] / k of x [T, H].
+struct GatherRows {
+  const uint16_t* x;
+  const int32_t* slot_of_row;
+  int k, T;
+};
+
+// returns the kernel family used through *variant; ga (or null) replaces x_perm
+// by rows gathered from x (no adapter then)
 hipError_t launch_expert_forward(const moe4_experts& ex, const uint16_t* x_perm,
                                  const int32_t* offsets, int rows, float* y_perm,
                                  float* save_gu, float* save_xa, void* ws, int* variant,
-                                 const LaunchEvents& le, hipStream_t s);
+                                 const LaunchEvents& le, hipStream_t s,
+                                 const GatherRows* ga = nullptr);
 hipError_t launch_expert_backward(const moe4_experts& ex, const uint16_t* x_perm,
                                   const int32_t* offsets, int rows, const float* save_gu,
                                   const float* save_xa, const uint16_t* dy_perm,

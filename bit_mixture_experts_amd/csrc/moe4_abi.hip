@@ -491,6 +491,45 @@ int moe4_expert_forward(const moe4_experts* ex, const uint16_t* x_perm, const in
   return rc;
 }
 
+int moe4_expert_forward_gather(const moe4_experts* ex, const uint16_t* x, int32_t T, int32_t k,
+                               const int32_t* slot_of_row, const int32_t* offsets, int32_t rows,
+                               float* y_perm, float* save_gu, void* ws, size_t ws_bytes,
+                               void* stream) {
+  g_variant = 0;
+  int rc = check_experts(ex);
+  if (rc) return rc;
+  if (ex->lora_A)
+    return fail(MOE4_EUNSUPPORTED,
+                "moe4_expert_forward_gather: the adapter path takes x_perm (moe4_expert_forward)");
+  if (k < 1) return fail(MOE4_ESHAPE, "k = %d must be >= 1", k);
+  if (T < 0 || (int64_t)T * k >= ((int64_t)1 << 31))
+    return fail(MOE4_ESHAPE, "T = %d: need T >= 0 and T*k < 2^31", T);
+  if (rows != T * k) return fail(MOE4_ESHAPE, "rows = %d must be T*k = %d", rows, T * k);
+  if (ex->H % 8) return fail(MOE4_ESHAPE, "H = %d must be a multiple of 8", ex->H);
+  if ((int64_t)T * ex->H * 2 >= ((int64_t)1 << 29))
+    return fail(MOE4_ESHAPE, "x of T = %d rows of H = %d exceeds 2^29 bytes (gathered rows are "
+                "addressed with 32-bit offsets); use moe4_permute + moe4_expert_forward", T, ex->H);
+  REQUIRE_PTR(offsets, "offsets");
+  if (rows > 0) {
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(slot_of_row, "slot_of_row");
+    REQUIRE_PTR(y_perm, "y_perm");
+  }
+  REQUIRE_ALIGN(x, 16, "x");
+  REQUIRE_ALIGN(y_perm, 16, "y_perm");
+  REQUIRE_ALIGN(save_gu, 4, "save_gu");
+  rc = check_ws(ws, ws_bytes, moe4::forward_ws_bytes(*ex, rows), "moe4_expert_forward_gather");
+  if (rc) return rc;
+  int variant = 0;
+  const moe4::GatherRows ga{x, slot_of_row, k, T};
+  hipError_t e = moe4::launch_expert_forward(*ex, nullptr, offsets, rows, y_perm, save_gu,
+                                             nullptr, ws, &variant, moe4::LaunchEvents{g_events},
+                                             (hipStream_t)stream, &ga);
+  rc = launched(e, "moe4_expert_forward_gather");
+  if (rc == MOE4_OK) g_variant = variant;
+  return rc;
+}
+
 int moe4_combine(const float* y_perm, const int32_t* row_of_slot, const float* topk_w,
                  int32_t T, int32_t k, int32_t H, void* out, int32_t out_dtype, void* stream) {
   if (out_dtype != MOE4_DTYPE_BF16 && out_dtype != MOE4_DTYPE_F32)

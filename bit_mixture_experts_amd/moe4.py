@@ -36,7 +36,7 @@ MOE4_NOALLOC_SCRATCH_BYTES = 16 << 20
 EXPORTS = ("moe4_quantize_nf4", "moe4_compress_absmax", "moe4_expand_absmax",
            "moe4_decode_mxfp4", "moe4_convert_mxfp4_nf4",
            "moe4_router_logits", "moe4_route", "moe4_route_backward", "moe4_permute",
-           "moe4_route_permute", "moe4_expert_forward", "moe4_expert_forward_noalloc", "moe4_combine",
+           "moe4_route_permute", "moe4_expert_forward", "moe4_expert_forward_gather", "moe4_expert_forward_noalloc", "moe4_combine",
            "moe4_expert_backward",
            "moe4_workspace_size", "moe4_set_timing_events", "moe4_last_error",
            "moe4_last_variant")
@@ -78,6 +78,8 @@ _SIGS = {
                             _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe4_expert_forward": ([_P, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe4_expert_forward_noalloc": ([_P, _vp, _vp, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "moe4_expert_forward_gather": ([_P, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
+                                   ctypes.c_int),
     "moe4_combine": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp], ctypes.c_int),
     "moe4_expert_backward": ([_P, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                              ctypes.c_int),
@@ -280,6 +282,19 @@ def moe4_route_permute(logits, k, topk_idx, topk_w, offsets, slot_of_row, row_of
                                    _ptr(x_perm, _BF16, "x_perm"), _ptr(ws, None, "ws"),
                                    0 if ws is None else ws.numel() * ws.element_size(),
                                    _stream(stream)))
+
+
+def moe4_expert_forward_gather(ex, x, k, slot_of_row, offsets, y_perm, save_gu=None, ws=None,
+                               stream=None):
+    """moe4_expert_forward on rows gathered from x [T, H] by the GEMM itself."""
+    T = x.shape[0]
+    _check(_lib.moe4_expert_forward_gather(ctypes.byref(ex.desc), _ptr(x, _BF16, "x"), T, k,
+                                           _ptr(slot_of_row, _I32, "slot_of_row"),
+                                           _ptr(offsets, _I32, "offsets"), T * k,
+                                           _ptr(y_perm, _F32, "y_perm"),
+                                           _ptr(save_gu, _F32, "save_gu"), _ptr(ws, None, "ws"),
+                                           0 if ws is None else ws.numel() * ws.element_size(),
+                                           _stream(stream)))
 
 
 def moe4_expert_forward(ex, x_perm, offsets, y_perm, save_gu=None, save_xa=None, ws=None,

@@ -317,6 +317,23 @@ int moe4_expert_forward(const moe4_experts* ex, const uint16_t* x_perm, const in
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe4_expert_forward with the row gather fused into the gate_up GEMM's loads
+ * [same passages; the gather of moe4_permute's definition]: row r of the
+ * grouped GEMM reads row slot_of_row[r] / k of x itself, so x_perm is never
+ * written. The results are bit for bit those of moe4_permute (with x) followed by
+ * moe4_expert_forward: the same operand values reach the same MFMAs. For a
+ * forward without adapters (the adapter path and its backward take x_perm).
+ *   x bf16 [T, H] (16-byte aligned), T * H * 2 < 2^29 bytes; k >= 1
+ *   slot_of_row i32 [T*k] and offsets i32 [E+1] from moe4_permute (or
+ *   moe4_route_permute) called without x; rows == T*k
+ *   y_perm, save_gu, ws as moe4_expert_forward; MOE4_EUNSUPPORTED with adapters
+ */
+int moe4_expert_forward_gather(const moe4_experts* ex, const uint16_t* x, int32_t T, int32_t k,
+                               const int32_t* slot_of_row, const int32_t* offsets, int32_t rows,
+                               float* y_perm, float* save_gu, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
  * moe4_expert_forward without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid allocation): the same computation and kernels, with the scratch

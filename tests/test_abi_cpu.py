@@ -121,6 +121,30 @@ def test_permute_refusals():
                             None) == moe4.MOE4_ESHAPE
 
 
+def test_forward_gather_refusals():
+    fg = lib.moe4_expert_forward_gather
+    d = _desc()
+    ws = 1 << 30
+    # adapters take x_perm; rows must be T*k; x within 2^29 bytes; alignment; nulls
+    dl = _desc(lora_A=FAKE, lora_B=FAKE, lora_r=8, lora_scale=2.0)
+    assert fg(ctypes.byref(dl), FAKE, 4, 2, FAKE, FAKE, 8, FAKE, None, FAKE, ws,
+              None) == moe4.MOE4_EUNSUPPORTED
+    assert fg(ctypes.byref(d), FAKE, 4, 2, FAKE, FAKE, 9, FAKE, None, FAKE, ws,
+              None) == moe4.MOE4_ESHAPE
+    assert fg(ctypes.byref(d), FAKE, 4, 0, FAKE, FAKE, 0, FAKE, None, FAKE, ws,
+              None) == moe4.MOE4_ESHAPE
+    assert fg(ctypes.byref(d), FAKE, 1 << 20, 1, FAKE, FAKE, 1 << 20, FAKE, None, FAKE, ws,
+              None) == moe4.MOE4_ESHAPE
+    assert "2^29" in moe4.moe4_last_error()
+    assert fg(ctypes.byref(d), FAKE_MIS, 4, 2, FAKE, FAKE, 8, FAKE, None, FAKE, ws,
+              None) == moe4.MOE4_EALIGN
+    assert fg(ctypes.byref(d), FAKE, 4, 2, None, FAKE, 8, FAKE, None, FAKE, ws,
+              None) == moe4.MOE4_EINVAL
+    assert "slot_of_row is NULL" in moe4.moe4_last_error()
+    assert fg(ctypes.byref(d), FAKE, 4, 2, FAKE, FAKE, 8, FAKE, None, FAKE, 16,
+              None) == moe4.MOE4_EWORKSPACE
+
+
 def test_route_permute_refusals():
     rp = lib.moe4_route_permute
     # E, k and T bounds; missing arrays; misaligned x; H not a multiple of 8;

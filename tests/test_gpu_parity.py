@@ -18,6 +18,9 @@ pytestmark = pytest.mark.gpu
 
 moe4 = pytest.importorskip("bit_mixture_experts_amd.moe4")
 
+# both kernel families of the expert forward
+VARIANTS = [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED]
+
 # scaled-down shapes of the workloads (same formats, layouts, epilogues)
 QWEN_SMALL = inp.QWEN3_30B_NF4.scaled(name="qwen3_shaped_small", seed_id=102, E=16, H=512,
                                       I=192, tokens=(5, 100))
@@ -603,6 +606,72 @@ def test_layer_forward_lora_ranks(spec, T, variant):
     rel = np.linalg.norm(got - want) / np.linalg.norm(want)
     say(f"  lora delta relative L2 error {rel:.2e}")
     assert rel < 0.05
+
+
+# the row gather fused into gate_up: shapes that reach both kernel families,
+# ragged tiles, E = 1, one row per expert, double-quantised stacks, skewed rows
+GATHER_CASES = [(QWEN_SMALL, 5), (QWEN_SMALL, 100), (GPTOSS_SMALL, 3), (GPTOSS_SMALL, 200),
+                (DENSE_NF4, 40), (ALLEXP_NF4, 33), (WIDE_NF4, 40), (TOPK16_NF4, 30),
+                (LONGK_MXFP4, 5)]
+
+
+def _gather_forward(ex, x_dev, res, k, save):
+    S, H = res["x_perm"].shape
+    y = torch.full((S, H), float("nan"), dtype=torch.float32, device=DEV)
+    gu = torch.full((S, 2 * ex.I), float("nan"), dtype=torch.float32, device=DEV) if save else None
+    moe4.moe4_expert_forward_gather(ex, x_dev, k, res["slot_of_row"], res["offsets"], y,
+                                    save_gu=gu, ws=res["ws"])
+    torch.cuda.synchronize()
+    return y, gu, moe4.moe4_last_variant()
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("spec,T", GATHER_CASES, ids=[f"{s.name}-T{t}" for s, t in GATHER_CASES])
+def test_forward_gather_matches_x_perm_forward(spec, T, variant):
+    """Gathering the rows inside the gate_up GEMM gives the x_perm forward's
+    y_perm and gu bit for bit (the same operands reach the same MFMAs), and
+    the oracle's layer."""
+    say(f"forward with the gather fused: {spec.name} T={T} variant={variant}")
+    L = layer_of(spec)
+    ex = L.device(variant)
+    x, lg = inp.host_tokens(spec, T)
+    xd = to_dev(x)
+    res = run_layer(ex, xd, to_dev(lg), spec.k, save=True)
+    y, gu, v = _gather_forward(ex, xd, res, spec.k, True)
+    assert v == variant
+    assert torch.equal(y, res["y_perm"]) and torch.equal(gu, res["save_gu"])
+    ri, rw = oracle.route(lg, spec.k)
+    ref = oracle.layer_forward(x, ri, rw, L.W)
+    assert_close(y.cpu().numpy(), ref["y"], "y_perm (gathered)")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_forward_gather_double_quant(variant):
+    spec, T = QWEN_SMALL, 100
+    say(f"forward with the gather fused, double-quantised: T={T} variant={variant}")
+    D = DQLayer(spec)
+    ex = D.device(variant)
+    x, lg = inp.host_tokens(spec, T)
+    xd = to_dev(x)
+    res = run_layer(ex, xd, to_dev(lg), spec.k, save=True)
+    y, gu, _ = _gather_forward(ex, xd, res, spec.k, True)
+    assert torch.equal(y, res["y_perm"]) and torch.equal(gu, res["save_gu"])
+
+
+def test_forward_gather_skewed_rows():
+    """Two hot experts with hundreds of rows: several skinny chunks and several
+    equal tiles per expert, each gathering its own rows."""
+    spec, T = inp.TINY_NF4, 700
+    L = layer_of(spec)
+    x, _ = inp.host_tokens(spec, T)
+    lg = np.full((T, spec.E), -5.0, np.float32)
+    lg[:, 3] = 5.0
+    lg[:, 6] = 4.0
+    xd = to_dev(x)
+    for variant in VARIANTS:
+        res = run_layer(L.device(variant), xd, to_dev(lg), spec.k)
+        y, _, _ = _gather_forward(L.device(variant), xd, res, spec.k, False)
+        assert torch.equal(y, res["y_perm"]), f"variant {variant}"
 
 
 def _without_lora(L):
