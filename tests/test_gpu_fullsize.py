@@ -209,6 +209,17 @@ def check_layer(spec, W, ex, T, layer=0, seed=0):
     assert np.array_equal(res["slot_of_row"].cpu().numpy(), rs)
     assert np.array_equal(res["row_of_slot"].cpu().numpy(), rr)
     assert np.array_equal(bits(res["x_perm"]), oracle.gather_rows(x, rs, spec.k))
+    if not ex.lora_r:
+        # the forward with the gather fused into gate_up (the bench's prefill
+        # path) gives the same y_perm and gu bit for bit
+        S = T * spec.k
+        yg = torch.empty((S, spec.H), dtype=torch.float32, device=DEV)
+        gg = torch.empty((S, 2 * spec.I), dtype=torch.float32, device=DEV)
+        moe4.moe4_expert_forward_gather(ex, to_dev(x), spec.k, res["slot_of_row"],
+                                        res["offsets"], yg, save_gu=gg, ws=res["ws"])
+        torch.cuda.synchronize()
+        assert torch.equal(yg, res["y_perm"]) and torch.equal(gg, res["save_gu"]), \
+            "the gathered forward differs from the x_perm forward"
     t0 = time.time()
     ref = oracle.layer_forward(x, ri, rw, W, keep=True)
     say(f"  oracle over the whole batch ({T * spec.k} rows): {time.time() - t0:.1f} s")
