@@ -190,16 +190,17 @@ class Step:
     def forward(self, ex, x, logits):
         m = self.moe4
         k = self.spec.k
-        if not self.backward and self.T * k > 1024:
-            # a prefill-sized batch: the gate_up GEMM gathers its rows from x
-            # itself (no x_perm round trip through HBM, no gather launch)
+        if not self.backward:
+            # the gate_up GEMM gathers its rows from x itself: no x_perm round
+            # trip through HBM and no gather work (1-2 us a decode step, 34 us
+            # at 4096 Qwen3 tokens)
             m.moe4_route_permute(logits, k, self.idx, self.w, self.offsets, self.sor, self.ros,
                                  ws=self.ws)
             m.moe4_expert_forward_gather(ex, x, k, self.sor, self.offsets, self.y_perm,
                                          ws=self.ws)
             m.moe4_combine(self.y_perm, self.ros, self.w, self.out, k)
             return
-        # route + permute + gather (one launch for a decode-sized batch)
+        # the backward reads x_perm again: route + permute + gather once
         m.moe4_route_permute(logits, k, self.idx, self.w, self.offsets, self.sor,
                              self.ros, x=x, x_perm=self.x_perm, ws=self.ws)
         if self.backward:

@@ -14,61 +14,134 @@ namespace {
 
 // ------------------------------------------------------------------ routing
 
-// (value, index) order used for selection: larger value first, then lower index.
-__device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+// Selection order: larger logit first, then lower expert index; +0 == -0.
+// Each candidate becomes one 64-bit key that is unique and ordered the same
+// way: the logit's bits mapped to an unsigned order (negative values have all
+// bits flipped, the others get the sign bit set; -0 is taken as +0), then the
+// inverted expert index. NaN maps to the lowest value (order 0), so the k
+// chosen experts are always distinct and in range. Key 0 marks a lane slot
+// with no candidate (past E, or already chosen).
+__device__ __forceinline__ uint64_t select_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  if (v != v) o = 0u;
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+}
+// The logit a key was made from (-0 comes back as +0, NaN as a NaN).
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// Routing of one token by one wave; lane l holds experts l, l+64, ... (NPL
-// per lane). The k chosen experts and their weights go to idx[0..k) and
-// w[0..k) (device or LDS memory).
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// DPP move of a 64-bit value inside each row of 16 lanes (CTRL as in
+// v_mov_b32_dpp: quad_perm, row_half_mirror, row_mirror).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)x, (int)(uint32_t)x, CTRL, 0xF, 0xF,
+                                             false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(x >> 32), (int)(uint32_t)(x >> 32),
+                                             CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Maximum over the wave, returned in every lane (the whole wave active):
+// lanes xor 1 and 2 by quad permutes, xor 4 and 8 by the half-row and row
+// mirrors, then rows pairwise by v_permlane16_swap and halves by
+// v_permlane32_swap; no LDS round trip.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  x = max_u64(x, dpp_u64<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = max_u64(x, dpp_u64<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = max_u64(x, dpp_u64<0x141>(x));  // row_half_mirror
+  x = max_u64(x, dpp_u64<0x140>(x));  // row_mirror
+  {
+    const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    x = max_u64(((uint64_t)b[0] << 32) | a[0], ((uint64_t)b[1] << 32) | a[1]);
+  }
+  {
+    const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    x = max_u64(((uint64_t)b[0] << 32) | a[0], ((uint64_t)b[1] << 32) | a[1]);
+  }
+  return x;
+}
+
+// Sum over the wave, in every lane, by the exchange pattern of wave_max_u64
+// (every lane adds the same pairs in the same tree, so all lanes agree bit
+// for bit).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x141>(x);
+  x += dpp_f32<0x140>(x);
+  {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  }
+  {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  }
+  return x;
+}
+
+// Routing of one token by one wave (all 64 lanes active); lane l holds
+// experts l, l+64, ... (NPL per lane). The k chosen experts and their weights
+// go to idx[0..k) and w[0..k) (device or LDS memory). Each of the k picks is
+// one wave-wide maximum of the remaining keys; the owner lane then clears the
+// chosen key.
 template <int NPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k,
                                             int renorm, int32_t* idx, float* wout) {
   const int l = lane_id();
   float v[NPL];
   float selv[NPL];
-  uint32_t taken = 0, valid = 0;
+  uint64_t key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = l + kWave * i;
     v[i] = 0.0f;
     selv[i] = 0.0f;
+    key[i] = 0;
     if (e < E) {
       v[i] = row[e];
-      valid |= 1u << i;
+      key[i] = select_key(v[i], e);
     }
   }
   float top = 0.0f;
   for (int j = 0; j < k; ++j) {
-    float bv = -__builtin_inff();
-    int be = 0x7FFFFFFF;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = l + kWave * i;
-      if (((valid & ~taken) >> i) & 1u) {
-        if (beats(v[i], e, bv, be)) {
-          bv = v[i];
-          be = e;
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, kWave);
-      const int oe = __shfl_xor(be, m, kWave);
-      if (beats(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    for (int i = 1; i < NPL; ++i) best = max_u64(best, key[i]);
+    best = wave_max_u64(best);
+    // the same in every lane: take it into scalar registers
+    const uint32_t be = ~(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)best);
+    const float bv = key_value(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(
+                                    (int)(uint32_t)(best >> 32)))
+                               << 32);
     if (j == 0) top = bv;
-    if ((be & (kWave - 1)) == l) taken |= 1u << (be / kWave);
+    if ((int)(be & (kWave - 1)) == l) {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i)
+        if (i == (int)(be / kWave)) key[i] = 0;
+    }
     if ((j & (kWave - 1)) == l) {
 #pragma unroll
       for (int i = 0; i < NPL; ++i)
         if (i == j / kWave) selv[i] = bv;
-      idx[j] = be;
+      idx[j] = (int32_t)be;
     }
   }
   // weights: exp(v - top) normalised over the selection or over all experts
@@ -78,11 +151,11 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     if (renorm) {
       const int j = l + kWave * i;
       if (j < k) part += expf(selv[i] - top);
-    } else if ((valid >> i) & 1u) {
+    } else if (l + kWave * i < E) {
       part += expf(v[i] - top);
     }
   }
-  const float denom = wave_sum(part);
+  const float denom = wave_sum_dpp(part);
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int j = l + kWave * i;
@@ -397,6 +470,43 @@ __global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ x, 
   copy_row(x, s / k, H, row_scale, s, x_perm + (int64_t)r * H);
 }
 
+// Routing and permutation of at most 64 slots (a decode step of a few tokens)
+// without the row gather, by one workgroup and a single barrier: wave t routes
+// token t into LDS; then every slot's row is counted directly (slots of a
+// smaller expert, plus earlier slots of the same expert) and so is every
+// expert's offset (slots of a smaller expert), each thread reading the
+// expert list from LDS. No scan, atomics or cleared counters.
+constexpr int kTinySlots = 64;
+template <int NPL>
+__global__ __launch_bounds__(kChunk) void k_route_permute_tiny(
+    const float* __restrict__ logits, int T, int E, int k, int renorm,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot_of_row, int32_t* __restrict__ row_of_slot) {
+  __shared__ int32_t sidx[kTinySlots];
+  __shared__ float sw[kTinySlots];
+  const int w = wave_id(), tid = threadIdx.x;
+  if (w < T) route_token<NPL>(logits + (int64_t)w * E, E, k, renorm, sidx + w * k, sw + w * k);
+  __syncthreads();
+  const int S = T * k;
+  if (tid < S) {
+    const int e = sidx[tid];
+    int row = 0;
+    for (int s = 0; s < S; ++s) {
+      const int o = sidx[s];
+      row += (o < e) | ((o == e) & (s < tid));
+    }
+    idx_out[tid] = e;
+    w_out[tid] = sw[tid];
+    slot_of_row[row] = tid;
+    row_of_slot[tid] = row;
+  }
+  for (int e = tid; e <= E; e += kChunk) {
+    int n = 0;
+    for (int s = 0; s < S; ++s) n += sidx[s] < e;
+    offsets[e] = n;
+  }
+}
+
 // ------------------------------------------------------------------ combine
 
 // out[t] = sum_j w[t,j] * y[row_of_slot[t*k+j]] over fp32 rows, accumulated
@@ -524,6 +634,25 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int re
                                 int32_t* row_of_slot, const uint16_t* x, int H,
                                 uint16_t* x_perm, void* ws, hipStream_t s) {
   const int S = T * k;
+  if (x == nullptr && S <= kTinySlots && T <= kFusedTokens) {
+    const dim3 g(1), b(kChunk);
+    if (E <= 64)
+      hipLaunchKernelGGL(k_route_permute_tiny<1>, g, b, 0, s, logits, T, E, k, renorm, idx, w,
+                         offsets, slot_of_row, row_of_slot);
+    else if (E <= 128)
+      hipLaunchKernelGGL(k_route_permute_tiny<2>, g, b, 0, s, logits, T, E, k, renorm, idx, w,
+                         offsets, slot_of_row, row_of_slot);
+    else if (E <= 256)
+      hipLaunchKernelGGL(k_route_permute_tiny<4>, g, b, 0, s, logits, T, E, k, renorm, idx, w,
+                         offsets, slot_of_row, row_of_slot);
+    else if (E <= 512)
+      hipLaunchKernelGGL(k_route_permute_tiny<8>, g, b, 0, s, logits, T, E, k, renorm, idx, w,
+                         offsets, slot_of_row, row_of_slot);
+    else
+      hipLaunchKernelGGL(k_route_permute_tiny<16>, g, b, 0, s, logits, T, E, k, renorm, idx, w,
+                         offsets, slot_of_row, row_of_slot);
+    return hipGetLastError();
+  }
   if (S > kSmallSlots || T > kFusedTokens) {
     hipError_t err = launch_route(logits, T, E, k, renorm, idx, w, s);
     if (err != hipSuccess) return err;

@@ -409,8 +409,13 @@ def _route(lg, k, renorm=True):
 @pytest.mark.parametrize("T,E,k,kind", [(64, 8, 2, "normal"), (300, 128, 8, "normal"),
                                         (77, 32, 4, "normal"), (50, 128, 4, "zipf"),
                                         (40, 1024, 16, "normal"), (33, 16, 16, "normal"),
-                                        (129, 64, 6, "ties"), (17, 1, 1, "normal")])
+                                        (129, 64, 6, "ties"), (17, 1, 1, "normal"),
+                                        (65, 256, 64, "special"), (9, 1000, 100, "normal"),
+                                        (31, 96, 20, "special")])
 def test_route_bit_exact(T, E, k, kind):
+    """Top-k indices equal to the oracle's; weights within 1e-5 relative.
+    'special' rows mix -inf, +-0, subnormals and values near the fp32 limits
+    into the logits (each row keeps a finite maximum)."""
     say(f"route T={T} E={E} k={k} {kind}")
     rng = np.random.default_rng(T * 1000 + E)
     lg = rng.standard_normal((T, E)).astype(np.float32)
@@ -419,6 +424,12 @@ def test_route_bit_exact(T, E, k, kind):
         lg[lg == 0] = np.where(rng.random((lg == 0).sum()) < 0.5, 0.0, -0.0)
     if kind == "zipf":
         lg += -1.1 * np.log(1 + rng.permutation(E)).astype(np.float32)
+    if kind == "special":
+        pool = np.array([-np.inf, 0.0, -0.0, 1e-45, -1e-45, 1e-40, -3.0e38, 3.0e38, -1.0],
+                        dtype=np.float32)
+        hit = rng.random((T, E)) < 0.4
+        lg[hit] = pool[rng.integers(0, len(pool), hit.sum())]
+        lg[:, 0] = np.maximum(lg[:, 0], 0.0)   # a finite maximum in every row
     for renorm in (True, False):
         gi, gw = _route(lg, k, renorm)
         ri, rw = oracle.route(lg, k, renormalize=renorm)
@@ -466,13 +477,16 @@ def test_permute_bit_exact(T, E, k):
 # through the two separate calls; ties, one expert, E up to 1024
 ROUTE_PERMUTE_CASES = [(1, 128, 8, "normal"), (4, 1024, 16, "ties"), (3, 1, 1, "normal"),
                        (2, 300, 3, "zipf"), (4, 32, 32, "normal"), (5, 128, 8, "normal"),
-                       (16, 128, 8, "normal"), (64, 32, 4, "zipf"), (200, 64, 6, "ties")]
+                       (16, 128, 8, "normal"), (64, 32, 4, "zipf"), (200, 64, 6, "ties"),
+                       (1, 256, 64, "ties"), (4, 64, 16, "zipf"), (2, 1000, 2, "normal")]
 
 
 @pytest.mark.parametrize("T,E,k,kind", ROUTE_PERMUTE_CASES)
 def test_route_permute_bit_exact(T, E, k, kind):
     """moe4_route_permute gives every output of moe4_route + moe4_permute bit
-    for bit, and the oracle's indices, permutation and gathered rows."""
+    for bit, and the oracle's indices, permutation and gathered rows; also
+    without the row gather (x = None), which for up to 64 slots of up to 4
+    tokens runs in a kernel of its own."""
     say(f"route + permute T={T} E={E} k={k} {kind}")
     rng = np.random.default_rng(7000 + T * 31 + E + k)
     lg = rng.standard_normal((T, E)).astype(np.float32)
@@ -483,7 +497,7 @@ def test_route_permute_bit_exact(T, E, k, kind):
     H = 72
     x = inp.to_bf16_bits(rng.standard_normal((T, H)))
     S = T * k
-    for renorm in (True, False):
+    for renorm, gather in ((True, True), (False, True), (True, False), (False, False)):
         gi, gw = _route(lg, k, renorm)
         off, sor, ros, xp = _permute(gi, E, x)
         fi = torch.empty((T, k), dtype=torch.int32, device=DEV)
@@ -494,19 +508,29 @@ def test_route_permute_bit_exact(T, E, k, kind):
         fxp = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
         ws = torch.empty(max(256, 4 * ((S + 2047) // 2048) * E + 256), dtype=torch.uint8,
                          device=DEV)
-        moe4.moe4_route_permute(to_dev(lg), k, fi, fw, foff, fsor, fros, x=to_dev(x), x_perm=fxp,
-                                ws=ws, renormalize=renorm)
+        if gather:
+            moe4.moe4_route_permute(to_dev(lg), k, fi, fw, foff, fsor, fros, x=to_dev(x),
+                                    x_perm=fxp, ws=ws, renormalize=renorm)
+        else:
+            # stale contents must not leak into the outputs
+            for t_ in (fi, foff, fsor, fros):
+                t_.fill_(-7)
+            fw.fill_(float("nan"))
+            moe4.moe4_route_permute(to_dev(lg), k, fi, fw, foff, fsor, fros, ws=ws,
+                                    renormalize=renorm)
         torch.cuda.synchronize()
         assert np.array_equal(fi.cpu().numpy(), gi)
         assert np.array_equal(fw.cpu().numpy().view(np.uint32), gw.view(np.uint32))
         for a_, b_ in ((foff, off), (fsor, sor), (fros, ros)):
             assert torch.equal(a_, b_)
-        assert np.array_equal(bits(fxp), bits(xp))
+        if gather:
+            assert np.array_equal(bits(fxp), bits(xp))
         ri, _ = oracle.route(lg, k, renormalize=renorm)
         ro, rs, _ = oracle.permute(ri, E)
         assert np.array_equal(fi.cpu().numpy(), ri)
         assert np.array_equal(foff.cpu().numpy(), ro) and np.array_equal(fsor.cpu().numpy(), rs)
-        assert np.array_equal(bits(fxp), oracle.gather_rows(x, rs, k))
+        if gather:
+            assert np.array_equal(bits(fxp), oracle.gather_rows(x, rs, k))
 
 
 def test_permute_skewed_one_expert():
