@@ -566,6 +566,25 @@ constexpr int kStageBytes = kStageA + kStageB + kStageS;
 constexpr int kTiledLds = kStages * kStageBytes;
 static_assert(kTiledLds + 256 * 8 <= 160 * 1024, "tiled kernel LDS");
 
+// An empty asm that takes v in registers at this point: whatever computes v
+// stays before it.
+__device__ __forceinline__ void pin_regs(const u32x4& v) { asm volatile("" ::"v"(v)); }
+
+// Element column (within the k-tile) of lane l's 16-byte A load in wave w: the
+// chunk l % 8 of row 8 w + l / 8, swizzled by (row >> 1) & 7.
+__device__ __forceinline__ int a_col_of(int l, int w) {
+  return 8 * ((l & 7) ^ (((8 * w + (l >> 3)) >> 1) & 7));
+}
+// The lane index, recomputed where it is used: the empty asm hides it from the
+// compiler, which then cannot keep values derived from it live across the
+// k-loop (the loop's registers are full; such values were spilled and every
+// reload waited for all loads in flight).
+__device__ __forceinline__ int opaque_lane() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t & (kWave - 1);
+}
+
 template <int FMT, bool GATEUP, bool GATHER>
 __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   using F = Format<FMT>;
@@ -628,7 +647,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   //    tile = row 64p + 8w + l/8, physical chunk l%8 = logical chunk ^ ((row >> 1) & 7)
   //    ((row >> 1) & 7 does not depend on p: load p is load 0 moved down 64
   //    rows, an offset passed in a scalar register)
-  const int a_col = 8 * ((l & 7) ^ (((8 * w + (l >> 3)) >> 1) & 7));
+  const int a_col = a_col_of(l, w);
   const int a_off = ((8 * w + (l >> 3)) * K + a_col) * 2;
   // gathered activations: the byte offset of load p's row (row 64 p + 8 w + l / 8
   // of the tile = row arows[.] / gk of A), or -1 past the tile's rows
@@ -675,9 +694,11 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   auto issue_b = [&](int kt, int st) {
     uint8_t* base = stage(st);
     const int kb = kt * kBK;
+    // a whole k-tile (wave-uniform) needs no per-lane k check
+    const bool kin = kb + kBK <= K || kb + 32 * (opaque_lane() & 1) < K;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rq, MOE4_LDS(base + kStageA + w * 1024), 16,
-        (b_on && kb + 32 * (l & 1) < K) ? b_off + kb / 2 : kOob, 0, 0, 0);
+        rq, MOE4_LDS(base + kStageA + w * 1024), 16, (b_on && kin) ? b_off + kb / 2 : kOob, 0, 0,
+        0);
     uint8_t* sbase = base + kStageA + kStageB + w * 256;
     if (FMT == MOE4_FMT_NF4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -697,14 +718,15 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   auto issue_part = [&](int kt, int j) {
     if (j < kBM / 64) {
       const int kb = kt * kBK;
+      const bool kin = kb + kBK <= K || kb + a_col_of(opaque_lane(), w) < K;
       if constexpr (GATHER) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, MOE4_LDS(stage(kt % kStages) + j * 8192 + w * 1024), 16,
-            (kb + a_col < K && a_offg[j] >= 0) ? a_offg[j] + 2 * kb : kOob, 0, 0, 0);
+            (kin && a_offg[j] >= 0) ? a_offg[j] + 2 * kb : kOob, 0, 0, 0);
       } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, MOE4_LDS(stage(kt % kStages) + j * 8192 + w * 1024), 16,
-            kb + a_col < K ? a_off + 2 * kb : kOob, j * 64 * K * 2, 0, 0);
+            kin ? a_off + 2 * kb : kOob, j * 64 * K * 2, 0, 0);
       }
     } else {
       issue_b(kt + 1, (kt + 1) % kStages);
@@ -745,7 +767,8 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[rt][i] = 0.0f;
     // A operand f = NRT s + rt of a k-tile: chunk 4h + s of row 32 rt + n32
-    constexpr int kN = 4 * NRT, kPre = 4;
+    // (ten row tiles: a shorter ring keeps the loop within 256 VGPRs)
+    constexpr int kN = 4 * NRT, kPre = NRT >= 10 ? 2 : 4;
     auto rd = [&](const uint16_t* As, int f) {
       const int s = f / NRT, rt = f % NRT, row = rt * 32 + n32;
       return *reinterpret_cast<const bf16x8*>(As + row * kBK + (((4 * h + s) ^ ((row >> 1) & 7)) * 8));
@@ -840,6 +863,12 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
           // finish the pending piece: s = 0 -> piece 3 of k-tile kt, else
           // piece s - 1 of k-tile kt + 1
           bq[(s + 3) & 3] = apply8<FMT>(wpend, lv, scpend);
+          // NF4: pieces of k-tile kt + 1 are read only in the next iteration;
+          // the compiler would otherwise sink their arithmetic to the end of
+          // this one (a burst of VALU work with no MFMAs beside it, and three
+          // pieces' table values live at once). MXFP4's piece is one
+          // conversion per pair and measured no better pinned.
+          if constexpr (NF4) pin_regs(bq[(s + 3) & 3]);
         }
         if (rt == NRT / 2) {
           // table reads of piece s of k-tile kt + 1
