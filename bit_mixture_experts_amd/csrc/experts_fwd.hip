@@ -592,11 +592,15 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   constexpr bool DQ = FMT == MOE4_FMT_NF4_DQ;
   constexpr int KB = F::kBlock;
   constexpr int kLoadsPerTile = kBM / 64 + 1 + 1;
+  // NF4 stacks have K (H or I) a multiple of their 64-element block, so every
+  // 64-wide k-tile is whole; MXFP4 (32-element blocks) may end in a half tile
+  constexpr bool kWholeTiles = NF4 && F::kBlock % kBK == 0;
   __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
   // double-quantised NF4: the absmax code book
   __shared__ float dqbook[DQ ? 256 : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t stage_mem[];
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  // w in a scalar register: every LDS destination derived from it is scalar
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
   if (NF4 && tid < 256) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
   if (DQ && tid < 256) dqbook[tid] = a.dqbook[tid];
   int e, ut, cg;
@@ -694,8 +698,9 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   auto issue_b = [&](int kt, int st) {
     uint8_t* base = stage(st);
     const int kb = kt * kBK;
-    // a whole k-tile (wave-uniform) needs no per-lane k check
-    const bool kin = kb + kBK <= K || kb + 32 * (opaque_lane() & 1) < K;
+    // a whole k-tile (wave-uniform; every NF4 k-tile, as K is a multiple of
+    // the 64-element block) needs no per-lane k check
+    const bool kin = kWholeTiles || kb + kBK <= K || kb + 32 * (opaque_lane() & 1) < K;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rq, MOE4_LDS(base + kStageA + w * 1024), 16, (b_on && kin) ? b_off + kb / 2 : kOob, 0, 0,
         0);
@@ -718,7 +723,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   auto issue_part = [&](int kt, int j) {
     if (j < kBM / 64) {
       const int kb = kt * kBK;
-      const bool kin = kb + kBK <= K || kb + a_col_of(opaque_lane(), w) < K;
+      const bool kin = kWholeTiles || kb + kBK <= K || kb + a_col_of(opaque_lane(), w) < K;
       if constexpr (GATHER) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, MOE4_LDS(stage(kt % kStages) + j * 8192 + w * 1024), 16,
