@@ -71,6 +71,37 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// Integer sum over the wave, in every lane (the whole wave active): lanes
+// xor 1 and 2 by quad permutes, xor 4 and 8 by the half-row and row mirrors
+// (DPP), then rows pairwise by v_permlane16_swap and halves by
+// v_permlane32_swap; no LDS round trip.
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = (int)(a[0] + a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (int)(b[0] + b[1]);
+}
+
+// Inclusive prefix sum over the wave (the whole wave active): Hillis-Steele
+// steps inside each 16-lane row by DPP row shifts (lanes shifted in from
+// outside the row add zero), then the totals of the rows below, read from
+// lanes 15, 31 and 47. The same result as wave_inclusive_scan without its
+// six LDS permutes.
+__device__ __forceinline__ int wave_scan_dpp(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int l = lane_id();
+  return x + (l >= 16 ? r0 : 0) + (l >= 32 ? r1 : 0) + (l >= 48 ? r2 : 0);
+}
+
 // fp32(fp32(a * b) + c): one rounded product, one rounded sum; the pragma
 // keeps the compiler from contracting the pair into a fused multiply-add
 __device__ __forceinline__ float mul_then_add(float a, float b, float c) {
@@ -104,7 +135,7 @@ __device__ __forceinline__ void locate_item(const int32_t* __restrict__ offsets,
       prev = nx;
     }
   }
-  int incl = wave_inclusive_scan(cnt);
+  int incl = wave_scan_dpp(cnt);
   int excl = incl - cnt;
   bool own = (q >= excl) && (q < incl);
   unsigned long long b = __ballot(own);
@@ -133,10 +164,10 @@ __device__ __forceinline__ void locate_item(const int32_t* __restrict__ offsets,
       prev = nx;
     }
   }
-  e_out = __shfl(ef, owner, kWave);
-  u_out = __shfl(uf, owner, kWave);
-  beg_out = __shfl(bf, owner, kWave);
-  end_out = __shfl(nf, owner, kWave);
+  e_out = __builtin_amdgcn_readlane(ef, owner);
+  u_out = __builtin_amdgcn_readlane(uf, owner);
+  beg_out = __builtin_amdgcn_readlane(bf, owner);
+  end_out = __builtin_amdgcn_readlane(nf, owner);
 }
 // locate_item for E <= 64 * PER: each lane reads its PER + 1 offsets as one
 // batch of loads (no dependent round trips), keeps them in registers for the
@@ -155,7 +186,7 @@ __device__ __forceinline__ void locate_item_batched(const int32_t* __restrict__ 
 #pragma unroll
   for (int i = 0; i < PER; ++i)
     if (e0 + i < E) cnt += units(o[i + 1] - o[i]);
-  const int incl = wave_inclusive_scan(cnt);
+  const int incl = wave_scan_dpp(cnt);
   const int excl = incl - cnt;
   const bool own = (q >= excl) && (q < incl);
   const unsigned long long b = __ballot(own);
@@ -183,10 +214,10 @@ __device__ __forceinline__ void locate_item_batched(const int32_t* __restrict__ 
       }
     }
   }
-  e_out = __shfl(ef, owner, kWave);
-  u_out = __shfl(uf, owner, kWave);
-  beg_out = __shfl(bf, owner, kWave);
-  end_out = __shfl(nf, owner, kWave);
+  e_out = __builtin_amdgcn_readlane(ef, owner);
+  u_out = __builtin_amdgcn_readlane(uf, owner);
+  beg_out = __builtin_amdgcn_readlane(bf, owner);
+  end_out = __builtin_amdgcn_readlane(nf, owner);
 }
 template <typename Units>
 __device__ __forceinline__ void locate_item(const int32_t* __restrict__ offsets, int E, int q,
@@ -222,8 +253,8 @@ __device__ __forceinline__ void locate_tile_xcd(const int32_t* __restrict__ offs
       prev = nx;
     }
   }
-  const int NF = __shfl(wave_inclusive_scan(nf), kWave - 1, kWave) * ncg;
-  const int NR = __shfl(wave_inclusive_scan(nr), kWave - 1, kWave) * ncg;
+  const int NF = wave_sum_i32(nf) * ncg;
+  const int NR = wave_sum_i32(nr) * ncg;
   const int x = b % kXcd, i = b / kXcd;
   const int f0 = (int)((int64_t)NF * x / kXcd), f1 = (int)((int64_t)NF * (x + 1) / kXcd);
   const int r0 = (int)((int64_t)NR * x / kXcd), r1 = (int)((int64_t)NR * (x + 1) / kXcd);
@@ -313,7 +344,7 @@ __device__ __forceinline__ void locate_tile_eq(const int32_t* __restrict__ offse
       prev = nx;
     }
   }
-  const int N = __shfl(wave_inclusive_scan(nt), kWave - 1, kWave) * ncg;
+  const int N = wave_sum_i32(nt) * ncg;
   const int x = b % kXcd, i = b / kXcd;
   const int f0 = (int)((int64_t)N * x / kXcd), f1 = (int)((int64_t)N * (x + 1) / kXcd);
   int e = -1, u = 0, item = 0;
@@ -372,7 +403,7 @@ __device__ __forceinline__ void locate_tile_sorted(const int32_t* __restrict__ o
   int before = 0;
 #pragma unroll
   for (int c = kC - 1; c >= 0; --c) {
-    const int tot = __shfl(wave_inclusive_scan(cnt[c]), kWave - 1, kWave);
+    const int tot = wave_sum_i32(cnt[c]);
     if (j >= before && j < before + tot) {
       const int k = j - before;   // k-th tile of count c + 1, experts in order
       const int C = c + 1;
