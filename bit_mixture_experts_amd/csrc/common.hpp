@@ -20,6 +20,8 @@ constexpr int kWave = 64;
 // size returns zeros, which takes the place of per-lane bounds branches.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kOob = 0x7FFFFFF0;   // offset past the end of any resource used here
+// cache-policy operand of the raw buffer builtins: the non-temporal bit
+constexpr int kCpolNt = 2;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // word 3 = 0x00020000: 32-bit data format, no swizzle (gfx9 family)

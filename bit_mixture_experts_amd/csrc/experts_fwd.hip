@@ -912,7 +912,18 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
       const float al = clamped ? a.alpha : 1.0f;
       const float lim = clamped ? a.limit : __int_as_float(0x7F800000);
       const float c1 = clamped ? 1.0f : 0.0f;
-      const bool extra = a.save_gu != nullptr;   // saved pre-activations
+      // the pre-activations g and u saved for the backward pass go through a
+      // resource over the tile's rows, so that stores past its last row (or
+      // of a pair past I, sent out of range without wrapping: the host keeps
+      // a 320-row fp32 tile of 2I values under 2 GiB) are dropped; the test
+      // on save_gu is uniform, a scalar branch
+      const bool extra = a.save_gu != nullptr;
+      const rsrc_t rg = make_rsrc(extra ? a.save_gu + (int64_t)row0 * 2 * a.I : a.save_gu,
+                                  (uint32_t)nrows * 2 * a.I * 4);
+      const uint32_t gpitch = (uint32_t)a.I * 8;
+      uint32_t cg_off = jon ? (uint32_t)ng * 4 : (uint32_t)kOob;
+      uint32_t cu_off = jon ? (uint32_t)nu * 4 : (uint32_t)kOob;
+      asm volatile("" : "+v"(cg_off), "+v"(cu_off));
       __syncthreads();
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
@@ -927,19 +938,20 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
           // (a gate lane keeps its own entries i < 8, an up lane its i >= 8)
           const auto gu = __builtin_amdgcn_permlane16_swap(
               __float_as_uint(acc[rt][q]), __float_as_uint(acc[rt][q + 8]), false, false);
-          float g = __uint_as_float(gu[0]) + bg;
-          float u = __uint_as_float(gu[1]) + bu;
+          const float g = __uint_as_float(gu[0]) + bg;
+          const float u = __uint_as_float(gu[1]) + bu;
           const int rt_row = rt * 32 + 8 * (q >> 2) + (gate_lane ? 0 : 16) + 4 * h + (q & 3);
-          if (rt_row < nrows && jon) {
-            if (extra) {
-              float* sg = a.save_gu + (int64_t)(row0 + rt_row) * 2 * a.I;
-              sg[ng] = g;
-              sg[nu] = u;
-            }
-            const float gc = fminf(g, lim);
-            const float uc = fminf(fmaxf(u, -lim), lim);
-            hs[rt_row * 128 + w * 16 + jl] = f32_to_bf16(gc * sigmoidf_(al * gc) * (uc + c1));
+          if (extra) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rg,
+                                                  (int)(rt_row * gpitch + cg_off), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), rg,
+                                                  (int)(rt_row * gpitch + cu_off), 0, 0);
           }
+          // every entry goes to the staging tile (rt_row < kBM): rows past the
+          // tile and pairs past I are never copied out
+          const float gc = fminf(g, lim);
+          const float uc = fminf(fmaxf(u, -lim), lim);
+          hs[rt_row * 128 + w * 16 + jl] = f32_to_bf16(gc * sigmoidf_(al * gc) * (uc + c1));
         }
       }
       __syncthreads();
@@ -953,14 +965,24 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
       }
     } else {
       const float bd = (a.bias && col_on) ? bf16_to_f32(a.bias[(int64_t)e * a.N_out + col_row]) : 0.0f;
+      // the tile's rows of y as one buffer resource: a store past its last
+      // row (or of a column past N_out, sent out of range) is dropped by the
+      // hardware, so no store needs a branch; y rows are read once, by the
+      // combine, long after: non-temporal
+      const rsrc_t ry = make_rsrc(a.yout + (int64_t)row0 * a.N_out, (uint32_t)nrows * a.N_out * 4);
+      const uint32_t pitch = (uint32_t)a.N_out * 4;
+      // a lane with no column adds kOob to every offset, which puts them all
+      // past the resource without wrapping (the host keeps a 320-row fp32
+      // tile under 2 GiB); opaque, so that the choice stays one select
+      uint32_t cb = col_on ? (uint32_t)col_row * 4 : (uint32_t)kOob;
+      asm volatile("" : "+v"(cb));
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int rt_row = rt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (col_on && rt_row < nrows)
-            __builtin_nontemporal_store(acc[rt][i] + bd,
-                                        a.yout + (int64_t)(row0 + rt_row) * a.N_out + col_row);
+          const uint32_t rt_row = rt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[rt][i] + bd), ry,
+                                                (int)(rt_row * pitch + cb), 0, kCpolNt);
         }
       }
     }

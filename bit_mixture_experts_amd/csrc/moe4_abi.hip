@@ -91,11 +91,12 @@ int check_experts(const moe4_experts* ex) {
     return fail(MOE4_ESHAPE, "moe4_experts: I*H = %lld; one expert's packed matrix must stay "
                 "under 2 GiB", (long long)ex->I * ex->H);
   // the GEMM kernels address an activation tile (up to 320 rows of K = H or
-  // 2I bf16 values) with 32-bit byte offsets
+  // 2I bf16 values) and an output tile (up to 320 rows of H fp32 values) with
+  // 32-bit byte offsets
   {
     const int64_t kmax = ex->H > 2 * (int64_t)ex->I ? ex->H : 2 * (int64_t)ex->I;
-    if (320 * 2 * kmax >= ((int64_t)1 << 31))
-      return fail(MOE4_ESHAPE, "moe4_experts: max(H, 2I) = %lld; a 320-row activation tile "
+    if (320 * 4 * kmax >= ((int64_t)1 << 31) - ((int64_t)1 << 24))
+      return fail(MOE4_ESHAPE, "moe4_experts: max(H, 2I) = %lld; a 320-row fp32 tile "
                   "must stay under 2 GiB", (long long)kmax);
   }
   REQUIRE_PTR(ex->gu_q, "moe4_experts.gu_q");

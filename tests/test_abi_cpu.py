@@ -192,16 +192,17 @@ def test_descriptor_refusals(field, value, code, msg):
     assert moe4.moe4_last_variant() == 0
 
 
-def test_activation_tile_offsets_refused():
-    # one expert's packed matrix fits (I * H < 2^31) but a 320-row activation
-    # tile of K = H bf16 values does not fit 32-bit byte offsets
-    d = _desc(H=1 << 22, I=64)
+def test_tile_offsets_refused():
+    # one expert's packed matrix fits (I * H < 2^31) but a 320-row tile of
+    # H fp32 values (the down GEMM's output rows) does not fit 32-bit byte
+    # offsets with room for the out-of-range offset above it
+    d = _desc(H=1 << 21, I=64)
     assert _fwd(d) == moe4.MOE4_ESHAPE
-    assert "320-row activation tile" in moe4.moe4_last_error()
-    d = _desc(H=64, I=1 << 21)   # K = 2I of the gate_up dgrad
+    assert "320-row fp32 tile" in moe4.moe4_last_error()
+    d = _desc(H=64, I=1 << 20)   # K = 2I of the gate_up dgrad
     assert _fwd(d) == moe4.MOE4_ESHAPE
-    d = _desc(H=3 << 20, I=64)   # the largest H below the limit passes validation
-    assert 640 * d.H < 1 << 31
+    d = _desc(H=1600 * 1024, I=64)   # near the limit passes validation
+    assert 1280 * d.H < (1 << 31) - (1 << 24)
     assert lib.moe4_workspace_size(ctypes.byref(d), 4, 2) > 0
 
 
