@@ -374,28 +374,33 @@ __device__ __forceinline__ int eq_tile_nrt(int n, int u) {
 // so every XCD starts its largest tiles first and fills in with the small ones
 // (longest-first list scheduling). The grid needs (tiles + 7) * ncg
 // workgroups; the rest get e = -1.
-template <int BM>
-__device__ __forceinline__ void locate_tile_sorted(const int32_t* __restrict__ offsets, int E,
-                                                   int ncg, int b, int& e_out, int& u_out,
-                                                   int& cg_out) {
+template <int BM, int PER>
+__device__ __forceinline__ void locate_tile_sorted_p(const int32_t* __restrict__ offsets, int E,
+                                                     int ncg, int b, int& e_out, int& u_out,
+                                                     int& cg_out) {
   constexpr int kXcd = 8, kC = BM / 32;
   const int l = lane_id();
-  const int per = (E + kWave - 1) / kWave;
-  const int e0 = l * per;
+  const int e0 = l * PER;
+  // lane l owns experts [e0, e0 + PER): its PER + 1 offsets go out as one
+  // batch of loads (a single round trip) and both passes below run on them
+  const rsrc_t ro = make_rsrc(offsets, (uint32_t)(E + 1) * 4);
+  int o[PER + 1];
+#pragma unroll
+  for (int i = 0; i <= PER; ++i) o[i] = (int)buf_load_b32(ro, e0 + i <= E ? 4 * (e0 + i) : kOob);
+  // per expert: tile count, and the classes (row-tile counts) of its first
+  // and last tile; an expert's tiles are all of the first class but the last
+  int nt[PER], cf[PER], cl[PER];
   int cnt[kC];
 #pragma unroll
   for (int c = 0; c < kC; ++c) cnt[c] = 0;
-  if (e0 < E) {
-    int prev = offsets[e0];
-    for (int i = 0; i < per && e0 + i < E; ++i) {
-      const int nx = offsets[e0 + i + 1], n = nx - prev;
-      prev = nx;
-      const int nt = eq_tiles<BM>(n);
-      if (nt == 0) continue;
-      const int cf = eq_tile_nrt<BM>(n, 0), cl = eq_tile_nrt<BM>(n, nt - 1);
 #pragma unroll
-      for (int c = 0; c < kC; ++c) cnt[c] += (cf == c + 1 ? nt - 1 : 0) + (cl == c + 1 ? 1 : 0);
-    }
+  for (int i = 0; i < PER; ++i) {
+    const int n = e0 + i < E ? o[i + 1] - o[i] : 0;
+    nt[i] = eq_tiles<BM>(n);
+    cf[i] = nt[i] ? eq_tile_nrt<BM>(n, 0) : 0;
+    cl[i] = nt[i] ? eq_tile_nrt<BM>(n, nt[i] - 1) : 0;
+#pragma unroll
+    for (int c = 0; c < kC; ++c) cnt[c] += (cf[i] == c + 1 ? nt[i] - 1 : 0) + (cl[i] == c + 1 ? 1 : 0);
   }
   const int x = b % kXcd, i = b / kXcd;
   const int j = (i / ncg) * kXcd + x;   // position in the largest-first order
@@ -407,24 +412,44 @@ __device__ __forceinline__ void locate_tile_sorted(const int32_t* __restrict__ o
   for (int c = kC - 1; c >= 0; --c) {
     const int tot = wave_sum_i32(cnt[c]);
     if (j >= before && j < before + tot) {
-      const int k = j - before;   // k-th tile of count c + 1, experts in order
-      const int C = c + 1;
-      int e, idx;
-      locate_item(offsets, E, k, [&](int n) {
-        const int nt = eq_tiles<BM>(n);
-        if (nt == 0) return 0;
-        return (eq_tile_nrt<BM>(n, 0) == C ? nt - 1 : 0) + (eq_tile_nrt<BM>(n, nt - 1) == C ? 1 : 0);
-      }, e, idx);
-      if (e >= 0) {
-        const int n = offsets[e + 1] - offsets[e], nt = eq_tiles<BM>(n);
-        const int nfull = eq_tile_nrt<BM>(n, 0) == C ? nt - 1 : 0;
-        e_out = e;
-        u_out = idx < nfull ? idx : nt - 1;
+      // the k-th tile of class C, experts in order: find the lane whose
+      // experts hold it, then the expert within the lane
+      const int k = j - before, C = c + 1;
+      const int mine = cnt[c];
+      const int incl = wave_scan_dpp(mine), excl = incl - mine;
+      const bool own = k >= excl && k < incl;
+      const unsigned long long bl = __ballot(own);
+      const int owner = __ffsll((long long)bl) - 1;   // bl != 0: k < tot
+      int ef = -1, uf = 0, acc = excl;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int nfull = cf[q] == C ? nt[q] - 1 : 0;
+        const int u = nfull + (cl[q] == C ? 1 : 0);
+        if (ef < 0 && k < acc + u) {
+          ef = e0 + q;
+          uf = k - acc < nfull ? k - acc : nt[q] - 1;
+        }
+        acc += u;
       }
+      e_out = __builtin_amdgcn_readlane(ef, owner);
+      u_out = __builtin_amdgcn_readlane(uf, owner);
       return;
     }
     before += tot;
   }
+}
+
+template <int BM>
+__device__ __forceinline__ void locate_tile_sorted(const int32_t* __restrict__ offsets, int E,
+                                                   int ncg, int b, int& e_out, int& u_out,
+                                                   int& cg_out) {
+  // experts per lane, rounded up to a power of two (E <= 1024)
+  const int per = (E + kWave - 1) / kWave;
+  if (per <= 1) locate_tile_sorted_p<BM, 1>(offsets, E, ncg, b, e_out, u_out, cg_out);
+  else if (per <= 2) locate_tile_sorted_p<BM, 2>(offsets, E, ncg, b, e_out, u_out, cg_out);
+  else if (per <= 4) locate_tile_sorted_p<BM, 4>(offsets, E, ncg, b, e_out, u_out, cg_out);
+  else if (per <= 8) locate_tile_sorted_p<BM, 8>(offsets, E, ncg, b, e_out, u_out, cg_out);
+  else locate_tile_sorted_p<BM, 16>(offsets, E, ncg, b, e_out, u_out, cg_out);
 }
 
 }  // namespace moe4

@@ -601,10 +601,16 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t stage_mem[];
   // w in a scalar register: every LDS destination derived from it is scalar
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
-  if (NF4 && tid < 256) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
-  if (DQ && tid < 256) dqbook[tid] = a.dqbook[tid];
+  // the table values are loaded first and stored after the locator, so that
+  // their loads and the locator's are in flight together
+  float2 lv0 = make_float2(0.0f, 0.0f);
+  float dq0 = 0.0f;
+  if (NF4 && tid < 256) lv0 = make_float2(F::level(tid & 15), F::level(tid >> 4));
+  if (DQ && tid < 256) dq0 = a.dqbook[tid];
   int e, ut, cg;
   locate_tile_sorted<kBM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
+  if (NF4 && tid < 256) lutf[tid] = lv0;
+  if (DQ && tid < 256) dqbook[tid] = dq0;
   // wave-uniform by construction; make it visible to the compiler so that the
   // buffer resources below live in scalar registers
   e = __builtin_amdgcn_readfirstlane(e);

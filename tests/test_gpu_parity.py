@@ -52,6 +52,10 @@ WIDE_NF4 = inp.TINY_NF4.scaled(name="wide_nf4_E160_k2", seed_id=115, E=160, k=2,
                                tokens=(40,))
 WIDEST_MXFP4 = inp.GPT_OSS_20B_MXFP4.scaled(name="widest_mxfp4_E1024_k4", seed_id=116, E=1024,
                                             k=4, H=64, I=64, tokens=(20,))
+# 257..512 experts (eight experts per lane in the tile locator), routing
+# skewed so that some experts fill several row tiles
+WIDE8_NF4 = inp.TINY_NF4.scaled(name="wide_nf4_E400_k4_zipf", seed_id=143, E=400, k=4, H=128,
+                                I=64, tokens=(300,), zipf=1.1)
 # top-16 routing: the combine's rows past the eighth and permute's k > 8
 TOPK16_NF4 = inp.TINY_NF4.scaled(name="top16_nf4_E64_k16", seed_id=118, E=64, k=16, H=128,
                                  I=64, tokens=(30,))
@@ -574,7 +578,8 @@ def test_combine_against_oracle(T, k, H):
 FWD_CASES = [(inp.TINY_NF4, 64), (QWEN_SMALL, 5), (QWEN_SMALL, 100), (GPTOSS_SMALL, 3),
              (GPTOSS_SMALL, 200), (LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (LONGK_NF4, 6),
              (LONGK_MXFP4, 5), (DENSE_NF4, 40), (ALLEXP_NF4, 33), (MIN_MXFP4, 9), (QWEN_SMALL, 1),
-             (GPTOSS_SMALL, 1), (WIDE_NF4, 40), (WIDEST_MXFP4, 20), (TOPK16_NF4, 30)]
+             (GPTOSS_SMALL, 1), (WIDE_NF4, 40), (WIDEST_MXFP4, 20), (TOPK16_NF4, 30),
+             (WIDE8_NF4, 300)]
 
 
 @pytest.mark.parametrize("variant", [moe4.MOE4_VARIANT_SKINNY, moe4.MOE4_VARIANT_TILED])
@@ -636,7 +641,7 @@ def test_layer_forward_lora_ranks(spec, T, variant):
 # ragged tiles, E = 1, one row per expert, double-quantised stacks, skewed rows
 GATHER_CASES = [(QWEN_SMALL, 5), (QWEN_SMALL, 100), (GPTOSS_SMALL, 3), (GPTOSS_SMALL, 200),
                 (DENSE_NF4, 40), (ALLEXP_NF4, 33), (WIDE_NF4, 40), (TOPK16_NF4, 30),
-                (LONGK_MXFP4, 5)]
+                (LONGK_MXFP4, 5), (WIDE8_NF4, 300)]
 
 
 def _gather_forward(ex, x_dev, res, k, save):
