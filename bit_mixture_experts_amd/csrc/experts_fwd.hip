@@ -770,13 +770,17 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   const int nk = (K + kBK - 1) / kBK;
   bool col_on;
   const int col_row = wrow_of(n32, col_on);
+  // the bias of the lane's column is where its accumulators start (after the
+  // scaled LoRA sum, when there is one), so the epilogue adds no bias
+  const float binit = (a.bias && col_on) ? bf16_to_f32(a.bias[(int64_t)e * Nw + col_row]) : 0.0f;
   auto kloop = [&](auto nrt_c) {
     constexpr int NRT = decltype(nrt_c)::value;
     f32x16 acc[NRT];
+    const float a0 = (GATEUP && a.r) ? 0.0f : binit;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rt][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) acc[rt][i] = a0;
     // A operand f = NRT s + rt of a k-tile: chunk 4h + s of row 32 rt + n32
     // (ten row tiles: a shorter ring keeps the loop within 256 VGPRs)
     constexpr int kN = 4 * NRT, kPre = NRT >= 10 ? 2 : 4;
@@ -836,7 +840,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[rt][i] *= a.lscale;
+          for (int i = 0; i < 16; ++i) acc[rt][i] = acc[rt][i] * a.lscale + binit;
       }
     }
     if (nk > 1) wait_vmcnt<2 * kLoadsPerTile>();
@@ -894,7 +898,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
       }
     }
     // ---- epilogue. Lane holds column n32 of each 32x32 tile, rows
-    // 8*(i/4) + 4*h + i%4. Per-column constants (bias, LoRA row) are read once.
+    // 8*(i/4) + 4*h + i%4.
     if constexpr (GATEUP) {
       // The gate of pair j0 + n sits in column n, its up in column n + 16 (same
       // rows): a shuffle gives each lane the pair; lanes n32 < 16 finish entries
@@ -904,20 +908,12 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
       const int jl = n32 & 15, j = j0 + jl;
       const bool jon = j < a.I;
       const int ng = gate_row(a.layout, a.I, jon ? j : 0), nu = up_row(a.layout, a.I, jon ? j : 0);
-      float bg = 0.0f, bu = 0.0f;
-      if (a.bias && jon) {
-        bg = bf16_to_f32(a.bias[(int64_t)e * 2 * a.I + ng]);
-        bu = bf16_to_f32(a.bias[(int64_t)e * 2 * a.I + nu]);
-      }
       const bool gate_lane = n32 < 16;
-      uint16_t* hs = reinterpret_cast<uint16_t*>(stage_mem);   // [kBM][128] bf16
-      // both activations in one branch-free form: h = gc sigma(al gc) (uc + c1),
-      // gc = min(g, lim), uc = clamp(u, -lim, lim); SwiGLU is al = 1, lim = inf,
-      // c1 = 0
-      const bool clamped = a.act == MOE4_ACT_SWIGLU_CLAMPED;
-      const float al = clamped ? a.alpha : 1.0f;
-      const float lim = clamped ? a.limit : __int_as_float(0x7F800000);
-      const float c1 = clamped ? 1.0f : 0.0f;
+      // entry (rt, q) of the lane sits in row lrow + rrow(rt, q) of the tile
+      const int lrow = (gate_lane ? 0 : 16) + 4 * h;
+      auto rrow = [](int rt, int q) { return rt * 32 + 8 * (q >> 2) + (q & 3); };
+      // h staged as [kBM][128] bf16; this lane's column of it
+      uint16_t* hl = reinterpret_cast<uint16_t*>(stage_mem) + lrow * 128 + w * 16 + jl;
       // the pre-activations g and u saved for the backward pass go through a
       // resource over the tile's rows, so that stores past its last row (or
       // of a pair past I, sent out of range without wrapping: the host keeps
@@ -927,40 +923,54 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
       const rsrc_t rg = make_rsrc(extra ? a.save_gu + (int64_t)row0 * 2 * a.I : a.save_gu,
                                   (uint32_t)nrows * 2 * a.I * 4);
       const uint32_t gpitch = (uint32_t)a.I * 8;
-      uint32_t cg_off = jon ? (uint32_t)ng * 4 : (uint32_t)kOob;
-      uint32_t cu_off = jon ? (uint32_t)nu * 4 : (uint32_t)kOob;
+      uint32_t cg_off = (jon ? (uint32_t)ng * 4 : (uint32_t)kOob) + lrow * gpitch;
+      uint32_t cu_off = (jon ? (uint32_t)nu * 4 : (uint32_t)kOob) + lrow * gpitch;
       asm volatile("" : "+v"(cg_off), "+v"(cu_off));
-      __syncthreads();
+      // h = g sigma(g) u (SwiGLU) or gc sigma(al gc) (uc + 1) with gc = min(g,
+      // lim), uc = clamp(u, -lim, lim) (clamped GLU); sigma(z) = 1 / (1 +
+      // 2^(-z log2 e)), the exponent's scale folded into one constant
+      auto finish = [&](auto clamped_c) {
+        constexpr bool CL = decltype(clamped_c)::value;
+        const float ns = (CL ? a.alpha : 1.0f) * -1.4426950408889634f;
+        const float lim = a.limit;
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        // entry i' < 8 of a gate lane and entry i' + 8 of an up lane are
-        // finished by that lane; the partner lane (16 apart) holds the other
-        // half of the pair
+        for (int rt = 0; rt < NRT; ++rt) {
+          // entry i' < 8 of a gate lane and entry i' + 8 of an up lane are
+          // finished by that lane; the partner lane (16 apart) holds the other
+          // half of the pair
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          // v_permlane16_swap(lo, hi) swaps rows 1 and 3 of lo with rows 0
-          // and 2 of hi (16-lane rows): every lane then holds the gate value
-          // of its entry in the first result and the up value in the second
-          // (a gate lane keeps its own entries i < 8, an up lane its i >= 8)
-          const auto gu = __builtin_amdgcn_permlane16_swap(
-              __float_as_uint(acc[rt][q]), __float_as_uint(acc[rt][q + 8]), false, false);
-          const float g = __uint_as_float(gu[0]) + bg;
-          const float u = __uint_as_float(gu[1]) + bu;
-          const int rt_row = rt * 32 + 8 * (q >> 2) + (gate_lane ? 0 : 16) + 4 * h + (q & 3);
-          if (extra) {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), rg,
-                                                  (int)(rt_row * gpitch + cg_off), 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(u), rg,
-                                                  (int)(rt_row * gpitch + cu_off), 0, 0);
+          for (int q = 0; q < 8; ++q) {
+            // v_permlane16_swap(lo, hi) swaps rows 1 and 3 of lo with rows 0
+            // and 2 of hi (16-lane rows): every lane then holds the gate value
+            // of its entry in the first result and the up value in the second
+            // (a gate lane keeps its own entries i < 8, an up lane its i >= 8)
+            const auto gu = __builtin_amdgcn_permlane16_swap(
+                __float_as_uint(acc[rt][q]), __float_as_uint(acc[rt][q + 8]), false, false);
+            const float g = __uint_as_float(gu[0]), u = __uint_as_float(gu[1]);
+            const uint32_t roff = (uint32_t)rrow(rt, q) * gpitch;
+            if (extra) {
+              __builtin_amdgcn_raw_buffer_store_b32(gu[0], rg, (int)(roff + cg_off), 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(gu[1], rg, (int)(roff + cu_off), 0, 0);
+            }
+            float hv;
+            if constexpr (CL) {
+              const float gc = fminf(g, lim);
+              const float uc = fminf(fmaxf(u, -lim), lim);
+              hv = gc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gc * ns)) * (uc + 1.0f);
+            } else {
+              hv = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * ns)) * u;
+            }
+            // every entry goes to the staging tile (row < kBM): rows past the
+            // tile and pairs past I are never copied out
+            hl[rrow(rt, q) * 128] = f32_to_bf16(hv);
           }
-          // every entry goes to the staging tile (rt_row < kBM): rows past the
-          // tile and pairs past I are never copied out
-          const float gc = fminf(g, lim);
-          const float uc = fminf(fmaxf(u, -lim), lim);
-          hs[rt_row * 128 + w * 16 + jl] = f32_to_bf16(gc * sigmoidf_(al * gc) * (uc + c1));
         }
-      }
+      };
       __syncthreads();
+      if (a.act == MOE4_ACT_SWIGLU_CLAMPED) finish(std::true_type{});
+      else finish(std::false_type{});
+      __syncthreads();
+      const uint16_t* hs = reinterpret_cast<const uint16_t*>(stage_mem);
       const int pbase = cg * 128;
       for (int idx = tid; idx < nrows * 16; idx += 64 * kTiledWaves) {
         const int r = idx >> 4, c = idx & 15;
@@ -970,7 +980,6 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
               reinterpret_cast<u32x4*>(a.hout + (int64_t)(row0 + r) * a.I + pbase + 8 * c));
       }
     } else {
-      const float bd = (a.bias && col_on) ? bf16_to_f32(a.bias[(int64_t)e * a.N_out + col_row]) : 0.0f;
       // the tile's rows of y as one buffer resource: a store past its last
       // row (or of a column past N_out, sent out of range) is dropped by the
       // hardware, so no store needs a branch; y rows are read once, by the
@@ -987,7 +996,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const uint32_t rt_row = rt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[rt][i] + bd), ry,
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[rt][i]), ry,
                                                 (int)(rt_row * pitch + cb), 0, kCpolNt);
         }
       }
