@@ -377,7 +377,7 @@ __device__ __forceinline__ int eq_tile_nrt(int n, int u) {
 template <int BM, int PER>
 __device__ __forceinline__ void locate_tile_sorted_p(const int32_t* __restrict__ offsets, int E,
                                                      int ncg, int b, int& e_out, int& u_out,
-                                                     int& cg_out) {
+                                                     int& cg_out, int& beg_out, int& end_out) {
   constexpr int kXcd = 8, kC = BM / 32;
   const int l = lane_id();
   const int e0 = l * PER;
@@ -407,6 +407,7 @@ __device__ __forceinline__ void locate_tile_sorted_p(const int32_t* __restrict__
   cg_out = i % ncg;
   e_out = -1;
   u_out = 0;
+  beg_out = end_out = 0;
   int before = 0;
 #pragma unroll
   for (int c = kC - 1; c >= 0; --c) {
@@ -420,7 +421,7 @@ __device__ __forceinline__ void locate_tile_sorted_p(const int32_t* __restrict__
       const bool own = k >= excl && k < incl;
       const unsigned long long bl = __ballot(own);
       const int owner = __ffsll((long long)bl) - 1;   // bl != 0: k < tot
-      int ef = -1, uf = 0, acc = excl;
+      int ef = -1, uf = 0, bf = 0, nf = 0, acc = excl;
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const int nfull = cf[q] == C ? nt[q] - 1 : 0;
@@ -428,28 +429,37 @@ __device__ __forceinline__ void locate_tile_sorted_p(const int32_t* __restrict__
         if (ef < 0 && k < acc + u) {
           ef = e0 + q;
           uf = k - acc < nfull ? k - acc : nt[q] - 1;
+          bf = o[q];
+          nf = o[q + 1];
         }
         acc += u;
       }
       e_out = __builtin_amdgcn_readlane(ef, owner);
       u_out = __builtin_amdgcn_readlane(uf, owner);
+      beg_out = __builtin_amdgcn_readlane(bf, owner);
+      end_out = __builtin_amdgcn_readlane(nf, owner);
       return;
     }
     before += tot;
   }
 }
 
+// beg_out/end_out: offsets[e] and offsets[e + 1] of the expert found (the
+// locator holds them already; zero when there is none)
 template <int BM>
 __device__ __forceinline__ void locate_tile_sorted(const int32_t* __restrict__ offsets, int E,
                                                    int ncg, int b, int& e_out, int& u_out,
-                                                   int& cg_out) {
+                                                   int& cg_out, int& beg_out, int& end_out) {
   // experts per lane, rounded up to a power of two (E <= 1024)
   const int per = (E + kWave - 1) / kWave;
-  if (per <= 1) locate_tile_sorted_p<BM, 1>(offsets, E, ncg, b, e_out, u_out, cg_out);
-  else if (per <= 2) locate_tile_sorted_p<BM, 2>(offsets, E, ncg, b, e_out, u_out, cg_out);
-  else if (per <= 4) locate_tile_sorted_p<BM, 4>(offsets, E, ncg, b, e_out, u_out, cg_out);
-  else if (per <= 8) locate_tile_sorted_p<BM, 8>(offsets, E, ncg, b, e_out, u_out, cg_out);
-  else locate_tile_sorted_p<BM, 16>(offsets, E, ncg, b, e_out, u_out, cg_out);
+#define MOE4_LOCATE(P) \
+  locate_tile_sorted_p<BM, P>(offsets, E, ncg, b, e_out, u_out, cg_out, beg_out, end_out)
+  if (per <= 1) MOE4_LOCATE(1);
+  else if (per <= 2) MOE4_LOCATE(2);
+  else if (per <= 4) MOE4_LOCATE(4);
+  else if (per <= 8) MOE4_LOCATE(8);
+  else MOE4_LOCATE(16);
+#undef MOE4_LOCATE
 }
 
 }  // namespace moe4

@@ -607,8 +607,8 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   float dq0 = 0.0f;
   if (NF4 && tid < 256) lv0 = make_float2(F::level(tid & 15), F::level(tid >> 4));
   if (DQ && tid < 256) dq0 = a.dqbook[tid];
-  int e, ut, cg;
-  locate_tile_sorted<kBM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
+  int e, ut, cg, obeg, oend;
+  locate_tile_sorted<kBM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg, obeg, oend);
   if (NF4 && tid < 256) lutf[tid] = lv0;
   if (DQ && tid < 256) dqbook[tid] = dq0;
   // wave-uniform by construction; make it visible to the compiler so that the
@@ -619,8 +619,8 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   __syncthreads();
   if (e < 0) return;
   const int K = a.K;
-  const int ebeg = min(a.offsets[e], a.rows);
-  const int n_e = min(a.offsets[e + 1], a.rows) - ebeg;
+  const int ebeg = min(obeg, a.rows);
+  const int n_e = min(oend, a.rows) - ebeg;
   const int R = eq_tile_rows<kBM>(n_e);
   const int row0 = ebeg + ut * R;
   const int nrows = min(R, ebeg + n_e - row0);
