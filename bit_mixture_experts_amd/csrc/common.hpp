@@ -28,6 +28,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+// make_rsrc for a base and size that are wave-uniform by construction, said so
+// to the compiler (else it may keep the resource in vector registers and wrap
+// every access in a loop over its distinct values)
+__device__ __forceinline__ rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo),
+                   __builtin_amdgcn_readfirstlane(bytes));
+}
 __device__ __forceinline__ u32x4 buf_load_b128(rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }

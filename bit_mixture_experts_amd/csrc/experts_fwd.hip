@@ -616,6 +616,8 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
   e = __builtin_amdgcn_readfirstlane(e);
   ut = __builtin_amdgcn_readfirstlane(ut);
   cg = __builtin_amdgcn_readfirstlane(cg);
+  obeg = __builtin_amdgcn_readfirstlane(obeg);
+  oend = __builtin_amdgcn_readfirstlane(oend);
   __syncthreads();
   if (e < 0) return;
   const int K = a.K;
@@ -920,8 +922,8 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
       // a 320-row fp32 tile of 2I values under 2 GiB) are dropped; the test
       // on save_gu is uniform, a scalar branch
       const bool extra = a.save_gu != nullptr;
-      const rsrc_t rg = make_rsrc(extra ? a.save_gu + (int64_t)row0 * 2 * a.I : a.save_gu,
-                                  (uint32_t)nrows * 2 * a.I * 4);
+      const rsrc_t rg = make_rsrc_uniform(extra ? a.save_gu + (int64_t)row0 * 2 * a.I : a.save_gu,
+                                          (uint32_t)nrows * 2 * a.I * 4);
       const uint32_t gpitch = (uint32_t)a.I * 8;
       uint32_t cg_off = (jon ? (uint32_t)ng * 4 : (uint32_t)kOob) + lrow * gpitch;
       uint32_t cu_off = (jon ? (uint32_t)nu * 4 : (uint32_t)kOob) + lrow * gpitch;
@@ -984,7 +986,8 @@ __global__ __launch_bounds__(512, 1) void k_tiled(const GemmArgs a) {
       // row (or of a column past N_out, sent out of range) is dropped by the
       // hardware, so no store needs a branch; y rows are read once, by the
       // combine, long after: non-temporal
-      const rsrc_t ry = make_rsrc(a.yout + (int64_t)row0 * a.N_out, (uint32_t)nrows * a.N_out * 4);
+      const rsrc_t ry =
+          make_rsrc_uniform(a.yout + (int64_t)row0 * a.N_out, (uint32_t)nrows * a.N_out * 4);
       const uint32_t pitch = (uint32_t)a.N_out * 4;
       // a lane with no column adds kOob to every offset, which puts them all
       // past the resource without wrapping (the host keeps a 320-row fp32

@@ -81,6 +81,33 @@ def test_no_kernel_uses_scratch(kernels):
         f"{n} {f}" for n, f in spilled.items())
 
 
+WATERFALL = re.compile(r"v_cmp_eq_u64_e(?:32|64) \S+, s\[\d+:\d+\], v\[\d+:\d+\]")
+
+
+def test_no_buffer_resource_in_vector_registers(tmp_path):
+    # A buffer resource the compiler cannot prove wave-uniform lives in vector
+    # registers, and every access through it becomes a loop over its distinct
+    # values (read one lane's resource, compare it with every lane's, run the
+    # access for the matching lanes, repeat): correct, and many times slower.
+    # Its mark is a 64-bit compare of a scalar pair with a vector pair.
+    objdump = f"{LLVM}/llvm-objdump"
+    if shutil.which(objdump) is None:
+        pytest.skip("llvm-objdump not found")
+    _kernels(tmp_path)   # unbundles the code objects into tmp_path
+    hits = {}
+    for co in sorted(tmp_path.glob("c*.elf")):
+        text = subprocess.run([objdump, "-d", "--no-show-raw-insn", str(co)], check=True,
+                              capture_output=True, text=True).stdout
+        name = None
+        for line in text.splitlines():
+            m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
+            if m:
+                name = m.group(1)
+            elif WATERFALL.search(line):
+                hits[name] = hits.get(name, 0) + 1
+    assert not hits, f"per-lane resource loops in: {hits}"
+
+
 def test_tiled_gemms_fit_two_waves_per_simd_and_the_lds(kernels):
     tiled = {n: f for n, f in kernels.items() if "k_tiled" in n}
     assert len(tiled) >= 9   # three formats x (gate_up, gate_up gathered, down)
