@@ -59,35 +59,38 @@ __device__ __forceinline__ void act_backward(int act, float g, float u, float dh
   }
 }
 
-// One workgroup per CU: eight waves, an expert tile of up to kGM rows and kGN
-// output columns, k-tiles of kGK weight rows. A k-tile's packed weights
-// [kGK rows][kGN/2 B] and their scales come to LDS by direct loads one k-tile
-// ahead of its activation tile; while the MFMAs of k-tile kt run, every thread
-// dequantises its share of k-tile kt + 1 (8 weight rows x 2 columns) into a
-// transposed bf16 buffer Bt [kGN columns][kGK], which the next k-tile's MFMAs
-// read as their B operand. Wave w computes columns 32 w .. +31 of the tile
-// against every 32-row tile (the loop is instantiated per count of row tiles,
-// so that short expert tiles keep all eight waves busy).
-constexpr int kGM = 256, kGN = 256, kGK = 32, kGStages = 4;
-// Stage: A [kGM rows][kGK] bf16 (four 16-byte chunks a row, chunk c of row r
-// stored at c ^ ((r >> 2) & 3): 16 consecutive rows of one chunk column fall
-// in 16 different 16-byte bank groups of the 64-bank LDS), the packed weights
-// [kGK rows][kGN / 2 B] (16-byte chunk c of row r stored at c ^ ((r >> 3) & 3),
-// so that the dequantising threads' byte reads spread over the banks), and
-// the scales in 4-byte slots 32 b + r (block b of weight row r: NF4 the fp32
-// absmax, MXFP4 the e8m0 byte; double-quantised NF4 the code byte, and in slot
-// 128 + 32 b + r the group's absmax2).
-constexpr int kGStageA = kGM * kGK * 2;
-constexpr int kGStageB = kGK * kGN / 2;
-constexpr int kGStageS = 1024;
-constexpr int kGStage = kGStageA + kGStageB + kGStageS;
-// Bt [kGN columns][kGK] bf16 at a pitch of 80 bytes: the MFMA operand reads
-// of 16 consecutive columns hit 16 different 16-byte bank groups
-constexpr int kGBtPitch = kGK * 2 + 16;
-constexpr int kGBt = kGN * kGBtPitch;
-constexpr int kGLds = kGStages * kGStage + 2 * kGBt;
-constexpr int kGLoads = 3;   // direct loads per thread and batch
-static_assert(kGLds + 256 * 8 <= 160 * 1024, "dgrad LDS");
+// One workgroup per CU: eight waves, an expert tile of up to kDM rows and kDN
+// output columns, k-tiles of kDK weight rows (the reduction). A k-tile's
+// activation rows, packed weights [kDK rows][kDN / 2 B] and scales come to LDS
+// by direct loads, two k-tiles ahead; one barrier per k-tile.
+//
+// Each wave owns 64 output columns as two interleaved 32-wide MFMA column
+// tiles: MFMA column c of tile m is output column nb + 64 w + 2 c + m, so that
+// one byte of a weight row holds the lane's weight of both tiles (low nibble:
+// tile 0). The MFMA wants each lane's B operand along the reduction (8
+// consecutive weight rows of one column), which is the opposite of the packed
+// order; the lane therefore reads one byte from each of the 8 rows, looks the
+// byte up in the table of fp32 NF4 level pairs (MXFP4: the hardware e2m1
+// conversion), scales and rounds, and packs the two tiles' operands in
+// registers. No transposed copy of the weights is written, and no wave reads
+// another wave's dequantised values: the barrier only guards the ring.
+constexpr int kDM = 160, kDN = 512, kDK = 64, kDStages = 3;
+constexpr int kDMaxRowTiles = kDM / 32;
+// Stage: A [kDM rows][128 B] (16-byte chunk c of row r stored at c ^ ((r >> 1)
+// & 7), the forward's layout: the 16 rows of an operand read fall in 16
+// different bank groups), the packed weights [kDK rows][256 B] (16-byte chunk
+// c of row r stored at (c + 2 ((r >> 3) & 1)) % 16: the two halves of a wave,
+// which read rows 8 apart, hit disjoint banks), and the scales in 4-byte slots
+// 64 b + r (block b of the workgroup's columns, weight row r of the k-tile:
+// NF4 the fp32 absmax, MXFP4 the e8m0 byte in the low byte; double-quantised
+// NF4 the code byte, and in slot 512 + 64 b + r the group's absmax2).
+constexpr int kDStageA = kDM * kDK * 2;
+constexpr int kDStageW = kDK * kDN / 2;
+constexpr int kDStageS = 4096;
+constexpr int kDStage = kDStageA + kDStageW + kDStageS;
+constexpr int kDLds = kDStages * kDStage;
+static_assert(kDLds + 256 * 8 + 256 * 4 <= 160 * 1024, "dgrad LDS");
+static_assert(kDM % 64 == 32, "A loads: two per lane, a third for waves 0..3");
 
 template <int FMT, int MODE>
 __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
@@ -95,270 +98,324 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
   constexpr bool NF4 = FMT != MOE4_FMT_MXFP4;   // NF4 levels (plain or double-quantised)
   constexpr bool DQ = FMT == MOE4_FMT_NF4_DQ;
   constexpr int KB = F::kBlock;
-  __shared__ __attribute__((aligned(16))) float2 lutf[256];
+  // direct loads per lane and batch: A 2 (+1 in waves 0..3), weights 2, scales
+  constexpr int kSLoads = FMT == MOE4_FMT_NF4 ? 1 : 2;
+  constexpr int kLoads = 4 + kSLoads;
+  __shared__ __attribute__((aligned(16))) float2 lutf[NF4 ? 256 : 1];
   __shared__ float dqbook[DQ ? 256 : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t gmem[];
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  if (tid < 256) lutf[tid] = make_float2(F::level(tid & 15), F::level(tid >> 4));
-  if (DQ && tid < 256) dqbook[tid] = a.dqbook[tid];
-  int e, ut, cg;
-  locate_tile_eq<kGM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg);
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
+  float2 lv0 = make_float2(0.0f, 0.0f);
+  float dq0 = 0.0f;
+  if (NF4 && tid < 256) lv0 = make_float2(F::level(tid & 15), F::level(tid >> 4));
+  if (DQ && tid < 256) dq0 = a.dqbook[tid];
+  int e, ut, cg, obeg, oend;
+  locate_tile_sorted<kDM>(a.offsets, a.E, a.ncg, blockIdx.x, e, ut, cg, obeg, oend);
+  if (NF4 && tid < 256) lutf[tid] = lv0;
+  if (DQ && tid < 256) dqbook[tid] = dq0;
   e = __builtin_amdgcn_readfirstlane(e);
   ut = __builtin_amdgcn_readfirstlane(ut);
   cg = __builtin_amdgcn_readfirstlane(cg);
+  obeg = __builtin_amdgcn_readfirstlane(obeg);
+  oend = __builtin_amdgcn_readfirstlane(oend);
   __syncthreads();
   if (e < 0) return;
   const int Kw = a.Kw, Nw = a.Nw;
-  const int ebeg = min(a.offsets[e], a.rows);
-  const int n_e = min(a.offsets[e + 1], a.rows) - ebeg;
-  const int R = eq_tile_rows<kGM>(n_e);
+  const int ebeg = min(obeg, a.rows);
+  const int n_e = min(oend, a.rows) - ebeg;
+  const int R = eq_tile_rows<kDM>(n_e);
   const int row0 = ebeg + ut * R;
   const int nrows = min(R, ebeg + n_e - row0);
-  const int n32 = l & 31, h = l >> 5;
-  const int nb = cg * kGN;
+  const int nrt = (nrows + 31) >> 5;
+  const int c32 = l & 31, hk = l >> 5;
+  const int nb = cg * kDN;
+  // the lane's two output columns (tile 0, tile 1)
+  const int n0 = nb + 64 * w + 2 * c32;
 
   const rsrc_t ra = make_rsrc(a.A + (int64_t)row0 * Kw, (uint32_t)nrows * Kw * 2);
   const rsrc_t rq = make_rsrc(a.wq + (int64_t)e * Kw * (Nw / 2), (uint32_t)Kw * (Nw / 2));
   constexpr int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
   const rsrc_t rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Kw * (Nw / KB) * sbytes,
                               (uint32_t)Kw * (Nw / KB) * sbytes);
-  auto stage = [&](int st) { return gmem + st * kGStage; };
-  uint8_t* bt = gmem + kGStages * kGStage;
-
-  // ---- loader roles (lane-contiguous LDS destinations)
-  // A: load p of thread t fills bytes 8192 p + 16 t of the A tile = row
-  //    128 p + t / 4, physical chunk t % 4
-  const int arow = tid >> 2;
-  const int a_col = 8 * ((tid & 3) ^ ((arow >> 2) & 3));
-  const int a_off = (arow * Kw + a_col) * 2;
-  // weights (waves 0..3): thread t fills bytes 16 t of the packed tile = row
-  //    t / 8, physical chunk t % 8 = logical chunk ^ ((row >> 3) & 3)
-  // scales (waves 4..7): thread 256 + i fills slot i = 32 b + r (NF4: slots
-  //    past 127 read zeros; double-quantised NF4: slots past 127 hold the
-  //    absmax2 of slot i - 128)
-  const int bq_row = (tid & 255) >> 3;
-  const int bq_byte = 16 * ((tid & 7) ^ ((bq_row >> 3) & 3));
-  const bool bq_on = nb / 2 + bq_byte < Nw / 2;
-  const int si = tid & 255;
-  const int sj = DQ ? si & 127 : si;
-  const int s_row = sj & 31, s_blk = sj >> 5;
-  const bool s_on = (FMT == MOE4_FMT_NF4 ? si < 128 : true) && (nb / KB + s_blk) < Nw / KB;
   const rsrc_t rs2 = DQ ? make_rsrc(a.ws2, (uint32_t)(((int64_t)a.E * Kw * (Nw / KB) + 255) / 256) * 4)
                         : rs;
-  auto issue_w = [&](int kt, int st) {   // weights / scales of k-tile kt
-    uint8_t* base = stage(st);
-    const int kb = kt * kGK;
-    if (w < 4) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rq, MOE4_LDS(base + kGStageA + w * 1024), 16,
-          (bq_on && kb + bq_row < Kw) ? (kb + bq_row) * (Nw / 2) + nb / 2 + bq_byte : kOob, 0, 0,
-          0);
-    } else {
-      const int soff =
-          (s_on && kb + s_row < Kw) ? ((kb + s_row) * (Nw / KB) + nb / KB + s_blk) * sbytes : kOob;
-      if constexpr (FMT == MOE4_FMT_NF4) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, MOE4_LDS(base + kGStageA + kGStageB + (w - 4) * 256), 4, soff, 0, 0, 0);
-      } else if constexpr (DQ) {
-        if (w < 6) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs, MOE4_LDS(base + kGStageA + kGStageB + (w - 4) * 256), 1, soff, 0, 0, 0);
-        } else {
-          // absmax2 of the slot's flat absmax index (in the whole stack)
-          const int64_t flat =
-              ((int64_t)e * Kw + kb + s_row) * (Nw / KB) + nb / KB + s_blk;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs2, MOE4_LDS(base + kGStageA + kGStageB + (w - 4) * 256), 4,
-              (s_on && kb + s_row < Kw) ? (int)(flat >> 8) * 4 : kOob, 0, 0, 0);
-        }
-      } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, MOE4_LDS(base + kGStageA + kGStageB + (w - 4) * 256), 1, soff, 0, 0, 0);
-      }
-    }
-  };
-  // batch kt: the A tile of k-tile kt (stage kt % 4) and the weights of
-  // k-tile kt + 1 (stage (kt + 1) % 4)
+  auto stage = [&](int st) { return gmem + st * kDStage; };
+
+  // ---- loader roles (lane-contiguous LDS destinations)
+  // A: load p of lane (w, l) fills bytes 8192 p + 1024 w + 16 l of the tile =
+  //    row 64 p + 8 w + l / 8, physical chunk l % 8 (p = 2: waves 0..3 only)
+  const int a_lc = (l & 7) ^ ((4 * w + (l >> 4)) & 7);
+  int a_off[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const int r = 64 * p + 8 * w + (l >> 3);
+    a_off[p] = r < nrows ? (r * Kw + 8 * a_lc) * 2 : kOob;
+  }
+  // weights: load q fills bytes 8192 q + 1024 w + 16 l = row 32 q + 4 w + l /
+  //    16, physical chunk l % 16
+  int w_row[2], w_off[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int rr = 32 * q + 4 * w + (l >> 4);
+    const int c = ((l & 15) - 2 * ((rr >> 3) & 1)) & 15;
+    w_row[q] = rr;
+    w_off[q] = nb + 32 * c < Nw ? rr * (Nw / 2) + nb / 2 + 16 * c : kOob;
+  }
   auto issue = [&](int kt) {
-    const int kb = kt * kGK;
-    const int aoff = kb + a_col < Kw ? a_off + 2 * kb : kOob;
+    const int kb = kt * kDK;
+    uint8_t* base = stage(kt % kDStages);
+    const bool kin = (NF4 && KB % kDK == 0) || kb + 8 * a_lc < Kw;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < 3; ++p)
+      if (p < 2 || w < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, MOE4_LDS(base + p * 8192 + w * 1024), 16,
+            (kin && a_off[p] != kOob) ? a_off[p] + 2 * kb : kOob, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, MOE4_LDS(stage(kt % kGStages) + p * 8192 + w * 1024), 16,
-          aoff == kOob ? kOob : aoff, p * 128 * Kw * 2, 0, 0);
-    issue_w(kt + 1, (kt + 1) % kGStages);
+          rq, MOE4_LDS(base + kDStageA + q * 8192 + w * 1024), 16,
+          (w_off[q] != kOob && kb + w_row[q] < Kw) ? w_off[q] + kb * (Nw / 2) : kOob, 0, 0, 0);
+    uint8_t* sb = base + kDStageA + kDStageW;
+    const bool rin = kb + l < Kw;
+    if constexpr (FMT == MOE4_FMT_NF4) {
+      // slot 64 w + l: block w of the workgroup's columns, row l
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, MOE4_LDS(sb + w * 256), 4,
+          (rin && nb / 64 + w < Nw / 64) ? ((kb + l) * (Nw / 64) + nb / 64 + w) * 4 : kOob, 0, 0,
+          0);
+    } else if constexpr (DQ) {
+      const bool on = rin && nb / 64 + w < Nw / 64;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, MOE4_LDS(sb + w * 256), 1, on ? (kb + l) * (Nw / 64) + nb / 64 + w : kOob, 0, 0, 0);
+      // absmax2 of the slot's flat absmax index (in the whole stack)
+      const int64_t flat = ((int64_t)e * Kw + kb + l) * (Nw / 64) + nb / 64 + w;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs2, MOE4_LDS(sb + 2048 + w * 256), 4,
+                                               on ? (int)(flat >> 8) * 4 : kOob, 0, 0, 0);
+    } else {
+      // slots 512 q + 64 w + l: block 8 q + w, row l
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, MOE4_LDS(sb + q * 2048 + w * 256), 1,
+            (rin && nb / 32 + 8 * q + w < Nw / 32) ? (kb + l) * (Nw / 32) + nb / 32 + 8 * q + w
+                                                   : kOob,
+            0, 0, 0);
+    }
   };
-  // dequantise the packed weights of stage st into Bt buffer bi: thread t
-  // takes weight rows 8 (t % 4) .. +7 (chunk t % 4 of a Bt column) and byte
-  // t / 4 (columns 2 (t / 4), +1). LDS reads go through vector types (the
-  // compiler then does not wait for the LDS-DMA loads in flight).
-  const int dq_c = tid & 3, dq_j = tid >> 2;
-  const int dq_chunk = dq_j >> 4, dq_in = dq_j & 15;
-  const int dq_blk = NF4 ? dq_j >> 5 : dq_j >> 4;
-  auto dequant_to_bt = [&](int st, int bi) {
-    const uint8_t* base = stage(st);
-    const uint8_t* qb = base + kGStageA;
-    const u32x4* sv = reinterpret_cast<const u32x4*>(base + kGStageA + kGStageB) + 8 * dq_blk + 2 * dq_c;
-    const u32x4 s0 = sv[0], s1 = sv[1];   // scale slots of rows 8 dq_c .. +7
-    u32x4 g0 = {0u, 0u, 0u, 0u}, g1 = {0u, 0u, 0u, 0u};
-    if constexpr (DQ) {
-      g0 = sv[32];   // their absmax2 (slots + 128)
-      g1 = sv[33];
-    }
-    const float dqo = DQ ? a.dqoff[0] : 0.0f;
-    float v0[8], v1[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 8 * dq_c + i;
-      // the 8 bytes holding byte dq_in of the row's chunk dq_chunk
-      const u32x2 pr = *reinterpret_cast<const u32x2*>(
-          qb + row * (kGN / 2) + 16 * (dq_chunk ^ ((row >> 3) & 3)) + 8 * (dq_in >> 3));
-      const uint32_t wd = (dq_in & 4) ? pr.y : pr.x;
-      const uint32_t byte = (wd >> (8 * (dq_in & 3))) & 255u;
-      const uint32_t sraw = i < 4 ? s0[i] : s1[i - 4];
-      if constexpr (NF4) {
-        // absmax (double-quantised: fp32(fp32(book[code] * absmax2) + offset);
-        // a one-byte load fills the low byte of its slot)
-        const float sc =
-            DQ ? mul_then_add(dqbook[sraw & 255u], __uint_as_float(i < 4 ? g0[i] : g1[i - 4]), dqo)
-               : __uint_as_float(sraw);
-        const f32x2 lv = reinterpret_cast<const f32x2*>(lutf)[byte];
-        v0[i] = lv.x * sc;
-        v1[i] = lv.y * sc;
-      } else {
-        const float sc = __uint_as_float((sraw & 255u) << 23);
-        const uint32_t p =
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(byte, sc, 0));
-        v0[i] = bf16lo(p);
-        v1[i] = bf16hi(p);
-      }
-    }
-    uint8_t* bb = bt + bi * kGBt;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const float* v = q ? v1 : v0;
-      const u32x4 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-      *reinterpret_cast<u32x4*>(bb + (2 * dq_j + q) * kGBtPitch + 16 * dq_c) = pk;
+  // wait until batch kt is in (at most the following batch in flight)
+  auto wait_batch = [&](bool more) {
+    if (more) {
+      if (w < 4) wait_vmcnt<kLoads + 1>();
+      else wait_vmcnt<kLoads>();
+    } else {
+      wait_vmcnt<0>();
     }
   };
 
-  const int nk = (Kw + kGK - 1) / kGK;
-  const int nrt = (nrows + 31) >> 5;
-  // column of this wave's MFMA B operand and output (wave w: columns
-  // nb + 32 w .. +31 against every row tile)
-  const int col = 32 * w + n32;
-  const int n = nb + col;
+  // ---- operand addresses within a stage
+  // B bytes: rows 16 s + 8 hk + i, byte 32 w + c32 of the row (its physical
+  // chunk is rotated by 2 for rows with bit 3 set, i.e. hk = 1)
+  const int b_rd = kDStageA + 8 * hk * 256 + 16 * ((2 * w + (c32 >> 4) + 2 * hk) & 15) + (c32 & 15);
+  // scales: NF4 / double-quantised block w, MXFP4 block 2 w + c32 / 16; rows
+  // 16 s + 8 hk .. + 7
+  const int s_rd = kDStageA + kDStageW + 4 * ((NF4 ? w : 2 * w + (c32 >> 4)) * 64 + 8 * hk);
+  // A operand of step s: chunk 2 s + hk of row 32 rt + c32
+  int a_rd[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) a_rd[s] = c32 * 128 + 16 * ((2 * s + hk) ^ ((c32 >> 1) & 7));
+  const float dqo = DQ ? a.dqoff[0] : 0.0f;
+
+  // B operands of step s of the k-tile in stage base (tile 0 and tile 1)
+  auto b_operands = [&](const uint8_t* base, int s, u32x4& b0, u32x4& b1) {
+    uint32_t by[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) by[i] = base[b_rd + (16 * s + i) * 256];
+    const u32x4 s0 = *reinterpret_cast<const u32x4*>(base + s_rd + 64 * s);
+    const u32x4 s1 = *reinterpret_cast<const u32x4*>(base + s_rd + 64 * s + 16);
+    float sc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t raw = i < 4 ? s0[i] : s1[i - 4];
+      if constexpr (FMT == MOE4_FMT_NF4) {
+        sc[i] = __uint_as_float(raw);
+      } else if constexpr (DQ) {
+        const float g2 = *reinterpret_cast<const float*>(base + s_rd + 2048 + 64 * s + 4 * i);
+        sc[i] = mul_then_add(dqbook[raw & 255u], g2, dqo);
+      } else {
+        sc[i] = __uint_as_float((raw & 255u) << 23);
+      }
+    }
+    if constexpr (NF4) {
+      f32x2 lv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lv[i] = reinterpret_cast<const f32x2*>(lutf)[by[i]];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        b0[q] = pack_bf16x2(lv[2 * q].x * sc[2 * q], lv[2 * q + 1].x * sc[2 * q + 1]);
+        b1[q] = pack_bf16x2(lv[2 * q].y * sc[2 * q], lv[2 * q + 1].y * sc[2 * q + 1]);
+      }
+    } else {
+      uint32_t p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        p[i] = __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(by[i], sc[i], 0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        b0[q] = __builtin_amdgcn_perm(p[2 * q + 1], p[2 * q], 0x05040100u);
+        b1[q] = __builtin_amdgcn_perm(p[2 * q + 1], p[2 * q], 0x07060302u);
+      }
+    }
+  };
+
+  const int nk = (Kw + kDK - 1) / kDK;
   auto kloop = [&](auto nrt_c) {
     constexpr int NRT = decltype(nrt_c)::value;
-    f32x16 acc[NRT];
+    f32x16 acc0[NRT], acc1[NRT];
 #pragma unroll
     for (int i = 0; i < NRT; ++i)
 #pragma unroll
-      for (int z = 0; z < 16; ++z) acc[i][z] = 0.0f;
+      for (int z = 0; z < 16; ++z) acc0[i][z] = acc1[i][z] = 0.0f;
 
-    // prologue: weights of k-tile 0, batches 0 .. 2, then k-tile 0 into Bt 0
-    issue_w(0, 0);
-#pragma unroll
-    for (int j = 0; j < kGStages - 1; ++j)
-      if (j < nk) issue(j);
+    issue(0);
+    if (nk > 1) issue(1);
     // LoRA delta of dx (gate_up dgrad) while the first batches land: MFMA steps
     // over the rank, A = bf16(t[row][q]), B = A_e[q][n] (bf16 already). They
     // start from zero accumulators, which then hold the fp32 sum scaled once
     // by lora_scale, as dx = dGU W + lora_scale * (bf16(t) A) defines it; the
     // k-tiles accumulate on top.
     if (MODE == DGRAD_GATEUP && a.r) {
-      const uint16_t* ar = a.loraA + ((int64_t)e * a.r) * Nw + n;
+      // the lane's two columns are adjacent: one dword of a row of A_e
+      const uint32_t* ar = reinterpret_cast<const uint32_t*>(a.loraA + (int64_t)e * a.r * Nw + n0);
       for (int q0 = 0; q0 < a.r; q0 += 16) {
-        u32x4 pb;
+        uint32_t x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int q = q0 + 8 * hk + i;
+          x[i] = (n0 < Nw && q < a.r) ? ar[(int64_t)q * (Nw / 2)] : 0u;
+        }
+        u32x4 pb0, pb1;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int q = q0 + 8 * h + 2 * jj;
-          const uint32_t x0 = (n < Nw && q < a.r) ? ar[(int64_t)q * Nw] : 0u;
-          const uint32_t x1 = (n < Nw && q + 1 < a.r) ? ar[(int64_t)(q + 1) * Nw] : 0u;
-          pb[jj] = x0 | (x1 << 16);
+          pb0[jj] = __builtin_amdgcn_perm(x[2 * jj + 1], x[2 * jj], 0x05040100u);
+          pb1[jj] = __builtin_amdgcn_perm(x[2 * jj + 1], x[2 * jj], 0x07060302u);
         }
 #pragma unroll
         for (int i = 0; i < NRT; ++i) {
-          const int rr = i * 32 + n32;
+          const int rr = i * 32 + c32;
           const float* tr = a.t + (int64_t)(row0 + rr) * a.r;
           u32x4 pk;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const int q = q0 + 8 * h + 2 * jj;
+            const int q = q0 + 8 * hk + 2 * jj;
             const float x0 = (rr < nrows && q < a.r) ? tr[q] : 0.0f;
             const float x1 = (rr < nrows && q + 1 < a.r) ? tr[q + 1] : 0.0f;
             pk[jj] = pack_bf16x2(x0, x1);
           }
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
-                                                           __builtin_bit_cast(bf16x8, pb), acc[i],
-                                                           0, 0, 0);
+          acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
+                                                            __builtin_bit_cast(bf16x8, pb0),
+                                                            acc0[i], 0, 0, 0);
+          acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
+                                                            __builtin_bit_cast(bf16x8, pb1),
+                                                            acc1[i], 0, 0, 0);
         }
       }
 #pragma unroll
       for (int i = 0; i < NRT; ++i)
 #pragma unroll
-        for (int z = 0; z < 16; ++z) acc[i][z] *= a.lscale;
+        for (int z = 0; z < 16; ++z) {
+          acc0[i][z] *= a.lscale;
+          acc1[i][z] *= a.lscale;
+        }
     }
-    if (nk >= 3) wait_vmcnt<3 * kGLoads>();
-    else if (nk == 2) wait_vmcnt<2 * kGLoads>();
-    else wait_vmcnt<kGLoads>();
-    lds_barrier();   // the weights of k-tile 0 come from every wave's loads
-    dequant_to_bt(0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      // batch kt landed (for this wave); then everyone's, and every wave's Bt
-      // writes of the previous step, behind the barrier
-      if (kt + 2 < nk) wait_vmcnt<2 * kGLoads>();
-      else if (kt + 1 < nk) wait_vmcnt<kGLoads>();
-      else wait_vmcnt<0>();
-      wait_lgkm0();
+      wait_batch(kt + 1 < nk);
+      // batch kt is in LDS everywhere; stage (kt + 2) % 3 is free
       lds_barrier();
-      if (kt + kGStages - 1 < nk) issue(kt + kGStages - 1);
-      const uint8_t* As = stage(kt % kGStages);
-      const uint8_t* Bs = bt + (kt & 1) * kGBt;
+      if (kt + 2 < nk) issue(kt + 2);
+      const uint8_t* base = stage(kt % kDStages);
 #pragma unroll
-      for (int s = 0; s < kGK / 16; ++s) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Bs + col * kGBtPitch + 16 * (2 * s + h));
+      for (int s = 0; s < kDK / 16; ++s) {
+        u32x4 b0, b1;
+        b_operands(base, s, b0, b1);
 #pragma unroll
         for (int i = 0; i < NRT; ++i) {
-          const int r = i * 32 + n32;
-          const bf16x8 av =
-              *reinterpret_cast<const bf16x8*>(As + r * 64 + 16 * ((2 * s + h) ^ ((r >> 2) & 3)));
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(base + a_rd[s] + i * 4096);
+          acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, b0),
+                                                            acc0[i], 0, 0, 0);
+          acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, b1),
+                                                            acc1[i], 0, 0, 0);
         }
       }
-      // next k-tile's weights into the other Bt buffer (after the last k-tile
-      // the stage holds zeros or stale bytes: decoded and never read)
-      dequant_to_bt((kt + 1) % kGStages, (kt + 1) & 1);
     }
 
-    // ---- epilogue: lane holds column n of each 32 x 32 row tile, rows
-    // 8 (z / 4) + 4 h + z % 4
-    if (n >= Nw) return;
-    int ng = 0, nu = 0;
+    // ---- epilogue: lane holds columns n0 (acc0) and n0 + 1 (acc1) of each
+    // 32 x 32 row tile, rows 8 (z / 4) + 4 hk + z % 4. Stores go through
+    // resources over the tile's rows; a pair past Nw is sent out of range.
+    const bool con = n0 < Nw;
     if (MODE == DGRAD_DOWN) {
-      ng = gate_row(a.layout, a.I, n);
-      nu = up_row(a.layout, a.I, n);
-    }
+      // n0 indexes the intermediate dimension: dH[row][n0], dH[row][n0 + 1]
+      const int I = a.I;
+      const rsrc_t rg = make_rsrc_uniform(a.save_gu + (int64_t)row0 * 2 * I,
+                                          (uint32_t)nrows * 2 * I * 4);
+      const rsrc_t rd = make_rsrc_uniform(a.dgu + (int64_t)row0 * 2 * I,
+                                          (uint32_t)nrows * 2 * I * 2);
+      const bool halves = a.layout == MOE4_GU_HALVES;
+      // byte offsets within a row: HALVES gate pair at n0, up pair at I + n0;
+      // INTERLEAVED (g, u, g, u) at 2 n0
+      const uint32_t gin = con ? (uint32_t)(halves ? n0 : 2 * n0) * 4 : (uint32_t)kOob;
+      const uint32_t uin = con ? (uint32_t)(I + n0) * 4 : (uint32_t)kOob;
+      const uint32_t gout = con ? (uint32_t)(halves ? n0 : 2 * n0) * 2 : (uint32_t)kOob;
+      const uint32_t uout = con ? (uint32_t)(I + n0) * 2 : (uint32_t)kOob;
 #pragma unroll
-    for (int i = 0; i < NRT; ++i) {
+      for (int i = 0; i < NRT; ++i) {
 #pragma unroll
-      for (int z = 0; z < 16; ++z) {
-        const int rr = i * 32 + 8 * (z >> 2) + 4 * h + (z & 3);
-        if (rr >= nrows) continue;
-        const int row = row0 + rr;
-        const float v = acc[i][z];
-        if (MODE == DGRAD_DOWN) {
-          // n indexes the intermediate dimension: dH[row][n]
-          const float* sg = a.save_gu + (int64_t)row * 2 * a.I;
-          float dg, du;
-          act_backward(a.act, sg[ng], sg[nu], v, a.alpha, a.limit, dg, du);
-          uint16_t* d = a.dgu + (int64_t)row * 2 * a.I;
-          d[ng] = f32_to_bf16(dg);
-          d[nu] = f32_to_bf16(du);
-        } else {
-          a.dx[(int64_t)row * Nw + n] = v;
+        for (int z = 0; z < 16; ++z) {
+          const int rr = i * 32 + 8 * (z >> 2) + 4 * hk + (z & 3);
+          float g0, u0, g1, u1;
+          if (halves) {
+            const u32x2 gg = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, (int)(rr * 8 * I + gin), 0, 0));
+            const u32x2 uu = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, (int)(rr * 8 * I + uin), 0, 0));
+            g0 = __uint_as_float(gg.x);
+            g1 = __uint_as_float(gg.y);
+            u0 = __uint_as_float(uu.x);
+            u1 = __uint_as_float(uu.y);
+          } else {
+            const u32x4 v = buf_load_b128(rg, (int)(rr * 8 * I + gin));
+            g0 = __uint_as_float(v[0]);
+            u0 = __uint_as_float(v[1]);
+            g1 = __uint_as_float(v[2]);
+            u1 = __uint_as_float(v[3]);
+          }
+          float dg0, du0, dg1, du1;
+          act_backward(a.act, g0, u0, acc0[i][z], a.alpha, a.limit, dg0, du0);
+          act_backward(a.act, g1, u1, acc1[i][z], a.alpha, a.limit, dg1, du1);
+          if (halves) {
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(dg0, dg1), rd,
+                                                  (int)(rr * 4 * I + gout), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(du0, du1), rd,
+                                                  (int)(rr * 4 * I + uout), 0, 0);
+          } else {
+            const u32x2 o = {pack_bf16x2(dg0, du0), pack_bf16x2(dg1, du1)};
+            __builtin_amdgcn_raw_buffer_store_b64(o, rd,
+                                                  (int)(rr * 4 * I + gout), 0, 0);
+          }
+        }
+      }
+    } else {
+      const rsrc_t rx = make_rsrc_uniform(a.dx + (int64_t)row0 * Nw, (uint32_t)nrows * Nw * 4);
+      const uint32_t cin = con ? (uint32_t)n0 * 4 : (uint32_t)kOob;
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) {
+#pragma unroll
+        for (int z = 0; z < 16; ++z) {
+          const int rr = i * 32 + 8 * (z >> 2) + 4 * hk + (z & 3);
+          const u32x2 o = {__float_as_uint(acc0[i][z]), __float_as_uint(acc1[i][z])};
+          __builtin_amdgcn_raw_buffer_store_b64(o, rx,
+                                                (int)(rr * 4 * Nw + cin), 0, 0);
         }
       }
     }
@@ -368,20 +425,17 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
     case 2: kloop(std::integral_constant<int, 2>{}); break;
     case 3: kloop(std::integral_constant<int, 3>{}); break;
     case 4: kloop(std::integral_constant<int, 4>{}); break;
-    case 5: kloop(std::integral_constant<int, 5>{}); break;
-    case 6: kloop(std::integral_constant<int, 6>{}); break;
-    case 7: kloop(std::integral_constant<int, 7>{}); break;
-    default: kloop(std::integral_constant<int, kGM / 32>{}); break;
+    default: kloop(std::integral_constant<int, kDMaxRowTiles>{}); break;
   }
 }
 
 template <int FMT>
 hipError_t set_dgrad_lds() {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dgrad<FMT, DGRAD_DOWN>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kDLds);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dgrad<FMT, DGRAD_GATEUP>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kDLds);
 }
 
 template <int FMT>
@@ -393,7 +447,7 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   const int E = ex.E, H = ex.H, I = ex.I;
   const bool lora = ex.lora_A != nullptr;
   const int touched = min(E, rows);
-  const int ntiles = rows / kGM + touched;
+  const int ntiles = rows / kDM + touched;
   static const hipError_t attr = set_dgrad_lds<FMT>();
   if (attr != hipSuccess) return attr;
   DgradArgs d{};
@@ -416,13 +470,13 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   d.A = dy_perm;
   d.save_gu = save_gu;
   d.dgu = dgu;
-  d.ncg = (I + kGN - 1) / kGN;
+  d.ncg = (I + kDN - 1) / kDN;
   le.before(0, s);
   if (ntiles * d.ncg > 0)
-    // ntiles bounds the row tiles; 8 spare ids keep every XCD's share of the
-    // items within the ids it is dealt
-    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_DOWN>), dim3(ntiles * d.ncg + 8), dim3(512), kGLds, s,
-                       d);
+    // ntiles bounds the row tiles; tile j of the largest-first order runs on
+    // XCD j % 8, so every XCD needs ceil(tiles / 8) * ncg ids
+    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_DOWN>), dim3((ntiles + 7) * d.ncg), dim3(512), kDLds,
+                       s, d);
   le.after(0, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -447,11 +501,11 @@ hipError_t backward_fmt(const moe4_experts& ex, const uint16_t* x_perm, const in
   g.r = lora ? ex.lora_r : 0;
   g.lscale = ex.lora_scale;
   g.dx = dx_perm;
-  g.ncg = (H + kGN - 1) / kGN;
+  g.ncg = (H + kDN - 1) / kDN;
   le.before(1, s);
   if (ntiles * g.ncg > 0)
-    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_GATEUP>), dim3(ntiles * g.ncg + 8), dim3(512), kGLds,
-                       s, g);
+    hipLaunchKernelGGL((k_dgrad<FMT, DGRAD_GATEUP>), dim3((ntiles + 7) * g.ncg), dim3(512),
+                       kDLds, s, g);
   le.after(1, s);
   err = hipGetLastError();
   if (err != hipSuccess || !lora) return err;
