@@ -44,9 +44,10 @@ struct DgradArgs {
 };
 
 // d(loss)/d(g), d(loss)/d(u) for h = act(g, u), given dh.
-__device__ __forceinline__ void act_backward(int act, float g, float u, float dh, float alpha,
-                                             float limit, float& dg, float& du) {
-  if (act == MOE4_ACT_SWIGLU) {
+template <int ACT>
+__device__ __forceinline__ void act_backward_t(float g, float u, float dh, float alpha,
+                                               float limit, float& dg, float& du) {
+  if constexpr (ACT == MOE4_ACT_SWIGLU) {
     const float s = sigmoidf_(g);
     du = dh * g * s;
     dg = dh * u * s * (1.0f + g * (1.0f - s));
@@ -132,13 +133,17 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
   // the lane's two output columns (tile 0, tile 1)
   const int n0 = nb + 64 * w + 2 * c32;
 
-  const rsrc_t ra = make_rsrc(a.A + (int64_t)row0 * Kw, (uint32_t)nrows * Kw * 2);
-  const rsrc_t rq = make_rsrc(a.wq + (int64_t)e * Kw * (Nw / 2), (uint32_t)Kw * (Nw / 2));
+  // every resource is wave-uniform by construction, said so to the compiler
+  // (else it may keep one in vector registers and loop over its lanes' values)
+  const rsrc_t ra = make_rsrc_uniform(a.A + (int64_t)row0 * Kw, (uint32_t)nrows * Kw * 2);
+  const rsrc_t rq = make_rsrc_uniform(a.wq + (int64_t)e * Kw * (Nw / 2), (uint32_t)Kw * (Nw / 2));
   constexpr int sbytes = FMT == MOE4_FMT_NF4 ? 4 : 1;
-  const rsrc_t rs = make_rsrc(static_cast<const uint8_t*>(a.ws) + (int64_t)e * Kw * (Nw / KB) * sbytes,
-                              (uint32_t)Kw * (Nw / KB) * sbytes);
-  const rsrc_t rs2 = DQ ? make_rsrc(a.ws2, (uint32_t)(((int64_t)a.E * Kw * (Nw / KB) + 255) / 256) * 4)
-                        : rs;
+  const rsrc_t rs = make_rsrc_uniform(
+      static_cast<const uint8_t*>(a.ws) + (int64_t)e * Kw * (Nw / KB) * sbytes,
+      (uint32_t)Kw * (Nw / KB) * sbytes);
+  const rsrc_t rs2 =
+      DQ ? make_rsrc_uniform(a.ws2, (uint32_t)(((int64_t)a.E * Kw * (Nw / KB) + 255) / 256) * 4)
+         : rs;
   auto stage = [&](int st) { return gmem + st * kDStage; };
 
   // ---- loader roles (lane-contiguous LDS destinations)
@@ -355,55 +360,81 @@ __global__ __launch_bounds__(512, 1) void k_dgrad(const DgradArgs a) {
     // resources over the tile's rows; a pair past Nw is sent out of range.
     const bool con = n0 < Nw;
     if (MODE == DGRAD_DOWN) {
-      // n0 indexes the intermediate dimension: dH[row][n0], dH[row][n0 + 1]
-      const int I = a.I;
-      const rsrc_t rg = make_rsrc_uniform(a.save_gu + (int64_t)row0 * 2 * I,
-                                          (uint32_t)nrows * 2 * I * 4);
-      const rsrc_t rd = make_rsrc_uniform(a.dgu + (int64_t)row0 * 2 * I,
-                                          (uint32_t)nrows * 2 * I * 2);
-      const bool halves = a.layout == MOE4_GU_HALVES;
-      // byte offsets within a row: HALVES gate pair at n0, up pair at I + n0;
-      // INTERLEAVED (g, u, g, u) at 2 n0
-      const uint32_t gin = con ? (uint32_t)(halves ? n0 : 2 * n0) * 4 : (uint32_t)kOob;
-      const uint32_t uin = con ? (uint32_t)(I + n0) * 4 : (uint32_t)kOob;
-      const uint32_t gout = con ? (uint32_t)(halves ? n0 : 2 * n0) * 2 : (uint32_t)kOob;
-      const uint32_t uout = con ? (uint32_t)(I + n0) * 2 : (uint32_t)kOob;
+      // n0 indexes the intermediate dimension: dH[row][n0], dH[row][n0 + 1].
+      // The layout and the activation are uniform: one epilogue per pair.
+      auto down = [&](auto halves_c, auto act_c) {
+        constexpr bool HALVES = decltype(halves_c)::value;
+        constexpr int ACT = decltype(act_c)::value;
+        const int I = a.I;
+        const rsrc_t rg = make_rsrc_uniform(a.save_gu + (int64_t)row0 * 2 * I,
+                                            (uint32_t)nrows * 2 * I * 4);
+        const rsrc_t rd = make_rsrc_uniform(a.dgu + (int64_t)row0 * 2 * I,
+                                            (uint32_t)nrows * 2 * I * 2);
+        // byte offsets within a row: HALVES gate pair at n0, up pair at I + n0;
+        // INTERLEAVED (g, u, g, u) at 2 n0
+        const uint32_t gin = con ? (uint32_t)(HALVES ? n0 : 2 * n0) * 4 : (uint32_t)kOob;
+        const uint32_t uin = con ? (uint32_t)(I + n0) * 4 : (uint32_t)kOob;
+        const uint32_t gout = con ? (uint32_t)(HALVES ? n0 : 2 * n0) * 2 : (uint32_t)kOob;
+        const uint32_t uout = con ? (uint32_t)(I + n0) * 2 : (uint32_t)kOob;
+        // group q = entries 4 (q % 4) .. + 3 of row tile q / 4: the saved
+        // pre-activations of group q + 1 are loaded while group q is finished
+        // (each wait then covers one group's loads, not one element's)
+        constexpr int NG = 4 * NRT;
+        auto row_of = [&](int q, int zz) {
+          const int z = 4 * (q & 3) + zz;
+          return (q >> 2) * 32 + 8 * (z >> 2) + 4 * hk + (z & 3);
+        };
+        auto load_group = [&](int q, u32x4 (&b)[4]) {
 #pragma unroll
-      for (int i = 0; i < NRT; ++i) {
-#pragma unroll
-        for (int z = 0; z < 16; ++z) {
-          const int rr = i * 32 + 8 * (z >> 2) + 4 * hk + (z & 3);
-          float g0, u0, g1, u1;
-          if (halves) {
-            const u32x2 gg = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, (int)(rr * 8 * I + gin), 0, 0));
-            const u32x2 uu = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, (int)(rr * 8 * I + uin), 0, 0));
-            g0 = __uint_as_float(gg.x);
-            g1 = __uint_as_float(gg.y);
-            u0 = __uint_as_float(uu.x);
-            u1 = __uint_as_float(uu.y);
-          } else {
-            const u32x4 v = buf_load_b128(rg, (int)(rr * 8 * I + gin));
-            g0 = __uint_as_float(v[0]);
-            u0 = __uint_as_float(v[1]);
-            g1 = __uint_as_float(v[2]);
-            u1 = __uint_as_float(v[3]);
+          for (int zz = 0; zz < 4; ++zz) {
+            const uint32_t ro = (uint32_t)row_of(q, zz) * 8 * I;
+            if constexpr (HALVES) {
+              const u32x2 gg = __builtin_bit_cast(
+                  u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, (int)(ro + gin), 0, 0));
+              const u32x2 uu = __builtin_bit_cast(
+                  u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, (int)(ro + uin), 0, 0));
+              b[zz] = u32x4{gg.x, uu.x, gg.y, uu.y};
+            } else {
+              b[zz] = buf_load_b128(rg, (int)(ro + gin));
+            }
           }
-          float dg0, du0, dg1, du1;
-          act_backward(a.act, g0, u0, acc0[i][z], a.alpha, a.limit, dg0, du0);
-          act_backward(a.act, g1, u1, acc1[i][z], a.alpha, a.limit, dg1, du1);
-          if (halves) {
-            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(dg0, dg1), rd,
-                                                  (int)(rr * 4 * I + gout), 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(du0, du1), rd,
-                                                  (int)(rr * 4 * I + uout), 0, 0);
-          } else {
-            const u32x2 o = {pack_bf16x2(dg0, du0), pack_bf16x2(dg1, du1)};
-            __builtin_amdgcn_raw_buffer_store_b64(o, rd,
-                                                  (int)(rr * 4 * I + gout), 0, 0);
+        };
+        u32x4 bufs[2][4];
+        load_group(0, bufs[0]);
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          if (q + 1 < NG) load_group(q + 1, bufs[(q + 1) & 1]);
+          const int i = q >> 2;
+#pragma unroll
+          for (int zz = 0; zz < 4; ++zz) {
+            const int z = 4 * (q & 3) + zz;
+            const u32x4 v = bufs[q & 1][zz];   // g0, u0, g1, u1
+            float dg0, du0, dg1, du1;
+            act_backward_t<ACT>(__uint_as_float(v[0]), __uint_as_float(v[1]), acc0[i][z],
+                                a.alpha, a.limit, dg0, du0);
+            act_backward_t<ACT>(__uint_as_float(v[2]), __uint_as_float(v[3]), acc1[i][z],
+                                a.alpha, a.limit, dg1, du1);
+            const uint32_t ro = (uint32_t)row_of(q, zz) * 4 * I;
+            if constexpr (HALVES) {
+              __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(dg0, dg1), rd, (int)(ro + gout),
+                                                    0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(du0, du1), rd, (int)(ro + uout),
+                                                    0, 0);
+            } else {
+              const u32x2 o = {pack_bf16x2(dg0, du0), pack_bf16x2(dg1, du1)};
+              __builtin_amdgcn_raw_buffer_store_b64(o, rd, (int)(ro + gout), 0, 0);
+            }
           }
         }
+      };
+      using Sw = std::integral_constant<int, MOE4_ACT_SWIGLU>;
+      using Cl = std::integral_constant<int, MOE4_ACT_SWIGLU_CLAMPED>;
+      if (a.layout == MOE4_GU_HALVES) {
+        if (a.act == MOE4_ACT_SWIGLU) down(std::true_type{}, Sw{});
+        else down(std::true_type{}, Cl{});
+      } else {
+        if (a.act == MOE4_ACT_SWIGLU) down(std::false_type{}, Sw{});
+        else down(std::false_type{}, Cl{});
       }
     } else {
       const rsrc_t rx = make_rsrc_uniform(a.dx + (int64_t)row0 * Nw, (uint32_t)nrows * Nw * 4);
