@@ -585,7 +585,14 @@ def device_state(torch=None, busy=None):
     import threading
     if "rocprof" in os.environ.get("LD_PRELOAD", ""):
         # under rocprofv3 its preloaded library would initialise the GPU in the
-        # rocm-smi child before that child starts its interpreter
+        # rocm-smi child before that child starts its interpreter: the GPU runs
+        # the work all the same (the traced run times what the plain run times)
+        if busy is not None:
+            t0 = time.time()
+            while time.time() - t0 < 2.5:
+                for _ in range(20):
+                    busy()
+                torch.cuda.synchronize()
         return {"sampled": "not sampled (run under the profiler)"}
     got = {}
 

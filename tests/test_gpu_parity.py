@@ -796,9 +796,9 @@ BWD_CASES = [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (DENSE_LORA, 50), (DENSE
 
 @pytest.mark.parametrize("T", [256, 257, 300])
 def test_layer_backward_skewed(T):
-    """All tokens on two experts (T rows each): the dgrad kernels take 256 rows
-    in one tile and cut 257 or 300 rows into two, and the adapter reductions
-    run over long row ranges."""
+    """All tokens on two experts (T rows each): the dgrad kernels (tiles of at
+    most 160 rows) cut 256 rows into two of 128, 257 into 160 + 97 and 300
+    into 160 + 140, and the adapter reductions run over long row ranges."""
     spec = LORA_SMALL
     say(f"backward skewed {spec.name} T={T}")
     L = layer_of(spec)
