@@ -790,8 +790,21 @@ ALLEXP_LORA = inp.QWEN3_30B_NF4_LORA.scaled(name="all_experts_lora_E2_k2", seed_
                                             lora_alpha=16.0)
 WIDE_LORA = inp.QWEN3_30B_NF4_LORA.scaled(name="wide_lora_E160_k2", seed_id=117, E=160, k=2,
                                           H=128, I=64, tokens=(40,), lora_r=4, lora_alpha=8.0)
+# the dgrad kernels' column groups of 512 and row tiles of 160: a second
+# column group of 64 (NF4) or 32 (MXFP4) columns, where whole waves have no
+# column and one wave (MXFP4) only half its lanes; an output width of 96
+# (MXFP4 gate_up dgrad: one and a half waves); a reduction of 96 (MXFP4 down
+# dgrad: one and a half k-tiles); Zipf-skewed rows, so that hot experts take
+# two row tiles
+COLGROUP_NF4_LORA = inp.QWEN3_30B_NF4_LORA.scaled(name="lora_nf4_H128_I576_zipf", seed_id=150,
+                                                  E=4, k=2, H=128, I=576, tokens=(200,),
+                                                  zipf=1.1)
+COLGROUP_MXFP4_LORA = inp.GPT_OSS_20B_MXFP4.scaled(name="lora_mxfp4_H96_I544_zipf", seed_id=151,
+                                                   E=4, k=2, H=96, I=544, tokens=(200,),
+                                                   lora_r=4, lora_alpha=8.0, zipf=1.1)
 BWD_CASES = [(LORA_SMALL, 150), (MXFP4_LORA_SMALL, 40), (DENSE_LORA, 50), (DENSE_MXFP4_LORA, 30),
-             (ALLEXP_LORA, 45), (WIDE_LORA, 40)]
+             (ALLEXP_LORA, 45), (WIDE_LORA, 40), (COLGROUP_NF4_LORA, 200),
+             (COLGROUP_MXFP4_LORA, 200)]
 
 
 @pytest.mark.parametrize("T", [256, 257, 300])
