@@ -6,9 +6,8 @@
 // fused-experts entry) and get no gradient.
 //
 // The dgrad GEMMs contract over the weight rows, the opposite orientation of
-// the forward: each k-tile of packed weights (rows along the reduction) is
-// dequantised by the whole workgroup into LDS, transposed so that each MFMA
-// lane reads 8 consecutive reduction values with one 128-bit LDS load.
+// the forward: each MFMA lane needs 8 consecutive weight rows of one column,
+// which it assembles in registers from one byte of each row (see k_dgrad).
 #include <type_traits>
 
 #include "common.hpp"
