@@ -183,9 +183,6 @@ class Step:
             self.dx = torch.empty((T, H), dtype=bf, device=dev)
             self.dA = torch.empty((E, r, H), dtype=f32, device=dev) if r else None
             self.dB = torch.empty((E, 2 * spec.I, r), dtype=f32, device=dev) if r else None
-            self.scratch_sor = torch.empty(S, dtype=i32, device=dev)
-            self.scratch_ros = torch.empty(S, dtype=i32, device=dev)
-            self.scratch_o = torch.empty(E + 1, dtype=i32, device=dev)
 
     def forward(self, ex, x, logits):
         m = self.moe4
@@ -212,8 +209,8 @@ class Step:
 
     def backward_pass(self, ex, dout):
         m = self.moe4
-        m.moe4_permute(self.idx, self.spec.E, self.scratch_o, self.scratch_sor, self.scratch_ros,
-                       x=dout, row_scale=self.w.reshape(-1), x_perm=self.dy, ws=self.ws)
+        # dOut gathered by the forward's permutation, scaled by the routing weights
+        m.moe4_gather_rows(dout, self.spec.k, self.sor, self.dy, row_scale=self.w.reshape(-1))
         m.moe4_expert_backward(ex, self.x_perm, self.offsets, self.save_gu, self.save_xa, self.dy,
                                self.dx_perm, self.dA, self.dB, ws=self.ws)
         m.moe4_combine(self.dx_perm, self.ros, None, self.dx, self.spec.k)

@@ -67,6 +67,8 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int re
                                 int32_t* row_of_slot, const uint16_t* x, int H,
                                 uint16_t* x_perm, void* ws, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+hipError_t launch_gather(const uint16_t* x, int T, int k, int H, const int32_t* slot_of_row,
+                         const float* row_scale, uint16_t* x_perm, hipStream_t s);
 hipError_t launch_combine(const float* y, const int32_t* row_of_slot, const float* w, int T,
                           int k, int H, void* out, bool out_f32, hipStream_t s);
 

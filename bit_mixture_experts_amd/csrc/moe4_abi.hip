@@ -386,6 +386,26 @@ int moe4_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32
                   "moe4_permute");
 }
 
+int moe4_gather_rows(const uint16_t* x, int32_t T, int32_t k, int32_t H,
+                     const int32_t* slot_of_row, const float* row_scale, uint16_t* x_perm,
+                     void* stream) {
+  if (k < 1 || k > 1024) return fail(MOE4_ESHAPE, "k = %d outside [1, 1024]", k);
+  if (T < 0 || (int64_t)T * k >= ((int64_t)1 << 31))
+    return fail(MOE4_ESHAPE, "T = %d: need T >= 0 and T*k < 2^31", T);
+  if (H <= 0 || H % 8) return fail(MOE4_ESHAPE, "H = %d must be a positive multiple of 8", H);
+  if (T > 0) {
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(slot_of_row, "slot_of_row");
+    REQUIRE_PTR(x_perm, "x_perm");
+  }
+  REQUIRE_ALIGN(x, 16, "x");
+  REQUIRE_ALIGN(x_perm, 16, "x_perm");
+  REQUIRE_ALIGN(row_scale, 4, "row_scale");
+  return launched(moe4::launch_gather(x, T, k, H, slot_of_row, row_scale, x_perm,
+                                      (hipStream_t)stream),
+                  "moe4_gather_rows");
+}
+
 int moe4_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
                        int32_t renormalize, int32_t* topk_idx, float* topk_w, int32_t* offsets,
                        int32_t* slot_of_row, int32_t* row_of_slot, const uint16_t* x, int32_t H,

@@ -459,7 +459,8 @@ __global__ __launch_bounds__(kChunk) void k_chunk_scatter(const int32_t* __restr
   }
 }
 
-// Pass 4: gather rows (one wave per row).
+// Pass 4: gather rows (one wave per row). A slot outside [0, S) (only from a
+// caller's slot_of_row) gives a zero row.
 __global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ x, int S, int k,
                                                 int H, const int32_t* __restrict__ slot_of_row,
                                                 const float* __restrict__ row_scale,
@@ -467,6 +468,12 @@ __global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ x, 
   const int r = (int)((blockIdx.x * (unsigned)blockDim.x + threadIdx.x) >> 6);
   if (r >= S) return;
   const int s = slot_of_row[r];
+  if ((unsigned)s >= (unsigned)S) {
+    u32x4* d = reinterpret_cast<u32x4*>(x_perm + (int64_t)r * H);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int c = lane_id(); c < H / 8; c += kWave) d[c] = z;
+    return;
+  }
   copy_row(x, s / k, H, row_scale, s, x_perm + (int64_t)r * H);
 }
 
@@ -599,6 +606,15 @@ size_t permute_ws_bytes(int T, int k, int E) {
   if (S <= kSmallSlots) return 0;
   const int64_t nchunks = (S + kBigChunk - 1) / kBigChunk;
   return align_up((size_t)(nchunks * E) * sizeof(int32_t), 256);
+}
+
+hipError_t launch_gather(const uint16_t* x, int T, int k, int H, const int32_t* slot_of_row,
+                         const float* row_scale, uint16_t* x_perm, hipStream_t s) {
+  const int S = T * k;
+  if (S == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather, dim3((S + 3) / 4), dim3(256), 0, s, x, S, k, H, slot_of_row,
+                     row_scale, x_perm);
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,

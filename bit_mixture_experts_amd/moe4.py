@@ -36,7 +36,7 @@ MOE4_NOALLOC_SCRATCH_BYTES = 16 << 20
 EXPORTS = ("moe4_quantize_nf4", "moe4_compress_absmax", "moe4_expand_absmax",
            "moe4_decode_mxfp4", "moe4_convert_mxfp4_nf4",
            "moe4_router_logits", "moe4_route", "moe4_route_backward", "moe4_permute",
-           "moe4_route_permute", "moe4_expert_forward", "moe4_expert_forward_gather", "moe4_expert_forward_noalloc", "moe4_combine",
+           "moe4_gather_rows", "moe4_route_permute", "moe4_expert_forward", "moe4_expert_forward_gather", "moe4_expert_forward_noalloc", "moe4_combine",
            "moe4_expert_backward",
            "moe4_workspace_size", "moe4_set_timing_events", "moe4_last_error",
            "moe4_last_variant")
@@ -74,6 +74,7 @@ _SIGS = {
                              _vp, _vp], ctypes.c_int),
     "moe4_permute": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp],
                      ctypes.c_int),
+    "moe4_gather_rows": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     "moe4_route_permute": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                             _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe4_expert_forward": ([_P, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -267,6 +268,15 @@ def moe4_permute(topk_idx, E, offsets, slot_of_row, row_of_slot, x=None, row_sca
                              _ptr(x_perm, _BF16, "x_perm"), _ptr(ws, None, "ws"),
                              0 if ws is None else ws.numel() * ws.element_size(),
                              _stream(stream)))
+
+
+def moe4_gather_rows(x, k, slot_of_row, x_perm, row_scale=None, stream=None):
+    """The row gather of moe4_permute on an existing permutation (slot_of_row)."""
+    T, H = x.shape
+    _check(_lib.moe4_gather_rows(_ptr(x, _BF16, "x"), T, k, H,
+                                 _ptr(slot_of_row, _I32, "slot_of_row"),
+                                 _ptr(row_scale, _F32, "row_scale"), _ptr(x_perm, _BF16, "x_perm"),
+                                 _stream(stream)))
 
 
 def moe4_route_permute(logits, k, topk_idx, topk_w, offsets, slot_of_row, row_of_slot, x=None,

@@ -287,6 +287,25 @@ int moe4_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The row gather of moe4_permute on a permutation already computed [the same
+ * passages]: x_perm[r] = x[slot_of_row[r] / k], or with row_scale,
+ * bf16(fp32(row_scale[s] * x[s / k])) for s = slot_of_row[r], as moe4_permute
+ * writes them. For the backward of a layer whose forward permuted its tokens:
+ * the upstream gradient gathered with the routing weights, without ranking the
+ * slots again.
+ *   x bf16 [T, H], 16-byte aligned, H % 8 == 0
+ *   slot_of_row i32 [T*k] (a permutation of the slots, as moe4_permute writes
+ *   it; a row whose entry lies outside [0, T*k) is written as zeros)
+ *   row_scale f32 [T*k] or NULL
+ *   x_perm bf16 [T*k, H] out, 16-byte aligned (caller-owned)
+ * Asynchronous on stream; argument errors are returned before anything is
+ * launched.
+ */
+int moe4_gather_rows(const uint16_t* x, int32_t T, int32_t k, int32_t H,
+                     const int32_t* slot_of_row, const float* row_scale, uint16_t* x_perm,
+                     void* stream);
+
+/*
  * moe4_route followed by moe4_permute (without row_scale), in one launch when
  * the batch is small (a decode step of at most 4 tokens),
  * otherwise as the two calls [the passages of both]. Every output is bit for

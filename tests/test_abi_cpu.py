@@ -121,6 +121,19 @@ def test_permute_refusals():
                             None) == moe4.MOE4_ESHAPE
 
 
+def test_gather_rows_refusals():
+    # k outside [1, 1024], H not a multiple of 8, a NULL slot map, misaligned rows;
+    # nothing to gather (T = 0) is accepted with NULL buffers
+    g = lib.moe4_gather_rows
+    assert g(FAKE, 4, 0, 64, FAKE, None, FAKE, None) == moe4.MOE4_ESHAPE
+    assert g(FAKE, 4, 2, 12, FAKE, None, FAKE, None) == moe4.MOE4_ESHAPE
+    assert g(FAKE, -1, 2, 64, FAKE, None, FAKE, None) == moe4.MOE4_ESHAPE
+    assert g(FAKE, 4, 2, 64, None, None, FAKE, None) == moe4.MOE4_EINVAL
+    assert "slot_of_row" in moe4.moe4_last_error()
+    assert g(FAKE_MIS, 4, 2, 64, FAKE, None, FAKE, None) == moe4.MOE4_EALIGN
+    assert g(None, 0, 2, 64, None, None, None, None) == moe4.MOE4_OK
+
+
 def test_forward_gather_refusals():
     fg = lib.moe4_expert_forward_gather
     d = _desc()

@@ -477,6 +477,44 @@ def test_permute_bit_exact(T, E, k):
         assert np.array_equal(bits(xp), oracle.gather_rows(x, rs, k, row_scale=sc))
 
 
+@pytest.mark.parametrize("T,E,k,H", [(100, 40, 2, 264), (300, 128, 8, 2048), (1, 8, 2, 8),
+                                     (0, 8, 2, 64)])
+def test_gather_rows_bit_exact(T, E, k, H):
+    """moe4_gather_rows on moe4_permute's slot_of_row gives moe4_permute's
+    x_perm bit for bit, with and without a row scale, and the oracle's rows;
+    a slot outside [0, T*k) gives a zero row (the other rows unchanged)."""
+    say(f"gather rows T={T} E={E} k={k} H={H}")
+    rng = np.random.default_rng(900 + T + E + k + H)
+    idx = np.array([rng.choice(E, k, replace=False) for _ in range(T)],
+                   dtype=np.int32).reshape(T, k)
+    x = inp.to_bf16_bits(rng.standard_normal((T, H)))
+    scale = rng.random(T * k).astype(np.float32)
+    for sc in (None, scale):
+        _, sor, _, xp = _permute(idx, E, x, sc) if T else (None, None, None, None)
+        S = T * k
+        sor_d = sor if T else torch.empty(0, dtype=torch.int32, device=DEV)
+        out = torch.full((S, H), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        xd = to_dev(x) if T else torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+        moe4.moe4_gather_rows(xd, k, sor_d, out,
+                              row_scale=None if sc is None else to_dev(sc))
+        torch.cuda.synchronize()
+        if T == 0:
+            continue
+        assert np.array_equal(bits(out), bits(xp))
+        _, rs, _ = oracle.permute(idx, E)
+        assert np.array_equal(bits(out), oracle.gather_rows(x, rs, k, row_scale=sc))
+    if T:
+        bad = sor.clone()
+        bad[0] = S
+        bad[-1] = -1
+        out = torch.full((S, H), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        moe4.moe4_gather_rows(to_dev(x), k, bad, out)
+        torch.cuda.synchronize()
+        ob, ref = bits(out), oracle.gather_rows(x, rs, k)
+        assert np.all(ob[0] == 0) and np.all(ob[-1] == 0)
+        assert np.array_equal(ob[1:-1], ref[1:-1])
+
+
 # fused routing + permutation: batches of up to 4 tokens in one launch, the rest
 # through the two separate calls; ties, one expert, E up to 1024
 ROUTE_PERMUTE_CASES = [(1, 128, 8, "normal"), (4, 1024, 16, "ties"), (3, 1, 1, "normal"),
