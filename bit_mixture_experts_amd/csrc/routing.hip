@@ -178,7 +178,11 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 
 constexpr int kChunk = 256;        // slots ranked per pass (one per thread)
 constexpr int kSmallSlots = 1024;  // single-kernel path up to this many slots
-constexpr int kBigChunk = 2048;    // slots per workgroup in the multi-kernel path
+// slots per workgroup in the multi-kernel path: 512 up to 64K slots (64 or
+// more workgroups at the Qwen3 prefill shape; 2048 took 1% longer per layer
+// step there), 2048 beyond (every scatter workgroup sums all chunks' counts,
+// so the work grows with the square of the chunk count)
+__host__ __device__ constexpr int big_chunk(int64_t S) { return S <= 65536 ? 512 : 2048; }
 
 // Lanes of this wave whose expert equals mine (match-any emulated with one
 // ballot per bit of the expert index). Invalid lanes carry e = -1 (all bits
@@ -376,15 +380,16 @@ __global__ __launch_bounds__(kChunk) void k_route_permute_small(
 }
 
 // Large problems, pass 1: per-chunk expert counts, counts[c * E + e], one
-// workgroup per chunk of kBigChunk slots.
+// workgroup per chunk of big_chunk(S) slots.
 __global__ __launch_bounds__(kChunk) void k_chunk_hist(const int32_t* __restrict__ idx, int S,
                                                        int E, int32_t* __restrict__ counts) {
+  const int chunk = big_chunk(S);
   extern __shared__ int cnt[];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kChunk) cnt[e] = 0;
   __syncthreads();
-  const int s0 = blockIdx.x * kBigChunk;
-  const int s1 = min(S, s0 + kBigChunk);
+  const int s0 = blockIdx.x * chunk;
+  const int s1 = min(S, s0 + chunk);
   for (int s = s0 + tid; s < s1; s += kChunk) {
     const int e = idx[s];
     if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
@@ -437,8 +442,8 @@ __global__ __launch_bounds__(kChunk) void k_chunk_scatter(const int32_t* __restr
     for (int e = tid; e <= E; e += kChunk) offsets[e] = run[e];
   for (int e = tid; e < E; e += kChunk) run[e] += before[e];
   const int ebits = bits_for(E);
-  const int s0 = c * kBigChunk;
-  const int s1 = min(S, s0 + kBigChunk);
+  const int s0 = c * big_chunk(S);
+  const int s1 = min(S, s0 + big_chunk(S));
   for (int p0 = s0; p0 < s1; p0 += kChunk) {
     for (int i = tid; i < 4 * E; i += kChunk) wcnt[i] = 0;
     __syncthreads();
@@ -604,7 +609,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, in
 size_t permute_ws_bytes(int T, int k, int E) {
   const int64_t S = (int64_t)T * k;
   if (S <= kSmallSlots) return 0;
-  const int64_t nchunks = (S + kBigChunk - 1) / kBigChunk;
+  const int64_t nchunks = (S + big_chunk(S) - 1) / big_chunk(S);
   return align_up((size_t)(nchunks * E) * sizeof(int32_t), 256);
 }
 
@@ -631,7 +636,7 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
                        slot_of_row, row_of_slot, x, row_scale, H, x_perm, rows_per_wg);
     return hipGetLastError();
   }
-  const int nchunks = (S + kBigChunk - 1) / kBigChunk;
+  const int nchunks = (S + big_chunk(S) - 1) / big_chunk(S);
   int32_t* counts = static_cast<int32_t*>(ws);
   hipLaunchKernelGGL(k_chunk_hist, dim3(nchunks), dim3(kChunk), E * sizeof(int), s, idx, S, E,
                      counts);

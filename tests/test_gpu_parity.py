@@ -441,6 +441,13 @@ def test_route_bit_exact(T, E, k, kind):
         assert np.allclose(gw, rw, rtol=1e-5, atol=0)
 
 
+def _perm_ws_bytes(S, E):
+    """A descriptor-free workspace size for the permutation: per-chunk expert
+    counts, chunks of 512 slots up to 64K slots and of 2048 beyond."""
+    chunk = 512 if S <= 65536 else 2048
+    return max(256, 4 * -(-S // chunk) * E + 256)
+
+
 def _permute(idx, E, x=None, scale=None):
     T, k = idx.shape
     S = T * k
@@ -451,16 +458,19 @@ def _permute(idx, E, x=None, scale=None):
     x_perm = None if x is None else torch.empty((max(S, 1), x.shape[1]), dtype=torch.bfloat16,
                                                 device=DEV)
     # a descriptor-free workspace size: the permutation part only needs E, T, k
-    ws = torch.empty(max(256, 4 * ((S + 2047) // 2048) * E + 256), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(_perm_ws_bytes(S, E), dtype=torch.uint8, device=DEV)
     moe4.moe4_permute(to_dev(idx), E, offsets, sor, ros, x=xd,
                       row_scale=None if scale is None else to_dev(scale), x_perm=x_perm, ws=ws)
     torch.cuda.synchronize()
     return offsets, sor, ros, x_perm
 
 
+# (8192, 128, 8) and (9000, 128, 8): 65536 and 72000 slots, both sides of the
+# switch from 512-slot to 2048-slot chunks
 @pytest.mark.parametrize("T,E,k", [(64, 8, 2), (1, 128, 8), (128, 128, 8), (200, 32, 4),
                                    (3000, 128, 8), (300, 1024, 7), (1500, 4, 4), (100, 64, 16),
-                                   (700, 32, 16), (40, 1024, 32), (50, 64, 16)])
+                                   (700, 32, 16), (40, 1024, 32), (50, 64, 16), (8192, 128, 8),
+                                   (9000, 128, 8)])
 def test_permute_bit_exact(T, E, k):
     say(f"permute T={T} E={E} k={k}")
     rng = np.random.default_rng(T + E + k)
@@ -548,7 +558,7 @@ def test_route_permute_bit_exact(T, E, k, kind):
         fsor = torch.empty(S, dtype=torch.int32, device=DEV)
         fros = torch.empty(S, dtype=torch.int32, device=DEV)
         fxp = torch.empty((S, H), dtype=torch.bfloat16, device=DEV)
-        ws = torch.empty(max(256, 4 * ((S + 2047) // 2048) * E + 256), dtype=torch.uint8,
+        ws = torch.empty(_perm_ws_bytes(S, E), dtype=torch.uint8,
                          device=DEV)
         if gather:
             moe4.moe4_route_permute(to_dev(lg), k, fi, fw, foff, fsor, fros, x=to_dev(x),
